@@ -1,0 +1,15 @@
+"""CPU oracle for the block-scaled fp8 small-M GEMM path: float64, slow, written from the pages.
+
+TEST INFRASTRUCTURE ONLY. It may be imported by tests/, by __graft_entry__.smoke() and by the
+cpu_baseline leg of bench.py, and by nothing else. It shares no code, tables or constants with
+the HIP library under block_scaled_fp8_skinny_amd/, and imports nothing from it.
+
+Parity status: every function here is pinned by CPU tests (tests/test_oracle_*.py) to values
+fixed by the format definitions, closed forms, invariants and exact rational brute force.
+"""
+from . import formats
+from .formats import (bf16_bits_to_f64, decode_e4m3, encode_e4m3, exp_factor, f64_to_bf16_bits,
+                      f64_to_fp32, round_bf16, round_fp32, round_to_binary)
+from .ops import (PAD_EXPONENT, ScaleError, Twin, abs_products_sum, block_exponent, dequant_bf16,
+                  dequant_values, gemm, gemm_exact_f64, make_twin, pad_k_input, pad_k_weight,
+                  scales_from_f32)
