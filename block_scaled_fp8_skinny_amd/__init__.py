@@ -1,0 +1,282 @@
+"""Python binding of libbsfp8 (the block-scaled fp8 small-M GEMM for MI355X).
+
+Argument marshalling only: every function here checks tensor dtypes/devices, takes pointers,
+strides and torch's current HIP stream, and calls the C entry point of the same name. All
+computation runs in the HIP kernels of the library. If libbsfp8.so is missing, every call raises
+(build it with `python -m block_scaled_fp8_skinny_amd.build`); there is no fallback.
+
+Conventions (see include/bsfp8.h): bf16 tensors are torch.bfloat16; e4m3 codes are uint8 tensors
+(torch.float8_e4m3fn tensors are accepted and viewed as uint8); exponent bytes are uint8.
+"""
+import ctypes
+import os
+from collections import namedtuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsfp8.so")
+
+OK, NOT_EXACT = 0, 1
+EINVAL, ESHAPE, ESCALE, ESTRIDE, EWORKSPACE, EHIP = -1, -2, -3, -4, -5, -6
+OUT_BF16, OUT_F32 = 0, 1
+
+# name -> (restype, argtypes)
+_P, _I64, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+_GEMM_ARGS = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _P, _SZ, _P, _I, _P]
+_SIGS = {
+    "bsfp8_strerror": (ctypes.c_char_p, [_I]),
+    "bsfp8_abi_version": (_I, []),
+    "bsfp8_scales_from_f32": (_I, [_P, _I64, _I64, _P, ctypes.POINTER(_I64), _P]),
+    "bsfp8_make_twin": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, ctypes.POINTER(_I64), _P]),
+    "bsfp8_pad_k_weight": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P]),
+    "bsfp8_pad_k_input": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]),
+    "bsfp8_dequant": (_I, [_P, _P, _I64, _I64, _I64, _P, _P]),
+    "bsfp8_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I]),
+    "bsfp8_gemm_small": (_I, _GEMM_ARGS),
+    "bsfp8_gemm_mid": (_I, _GEMM_ARGS),
+    "bsfp8_gemm": (_I, _GEMM_ARGS),
+    "bsfp8_num_configs": (_I, []),
+    "bsfp8_config_info": (_I, [_I, ctypes.POINTER(_I)]),
+    "bsfp8_plan_info": (_I, [_I64, _I64, _I64, _I64, _I, _I, ctypes.POINTER(_I)]),
+    "bsfp8_workspace_bytes_config": (_SZ, [_I64, _I64, _I64, _I64, _I, _I]),
+    "bsfp8_gemm_config": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _I, _P, _SZ, _P, _I, _P]),
+}
+
+_lib = None
+
+
+class BsfpError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def lib():
+    """The loaded libbsfp8.so (raises when it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m block_scaled_fp8_skinny_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype, f.argtypes = res, args
+        _lib = l
+    return _lib
+
+
+def strerror(status):
+    return lib().bsfp8_strerror(int(status)).decode()
+
+
+def _check(status, where):
+    if status < 0:
+        raise BsfpError(status, where)
+    return status
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _codes(q):
+    if q.dtype == torch.float8_e4m3fn:
+        q = q.view(torch.uint8)
+    if q.dtype != torch.uint8:
+        raise TypeError("e4m3 codes must be uint8 or float8_e4m3fn")
+    return q
+
+
+def _need(t, dtype, name, cuda=True):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if cuda and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------------------------------------
+# prepare
+# ------------------------------------------------------------------------------------------------
+def bsfp8_scales_from_f32(scales, exp_out=None):
+    """fp32 block scales [rows, cols] -> uint8 exponent bytes. Raises BsfpError(ESCALE) when any
+    scale is not a positive finite power of two (the error carries .n_bad)."""
+    _need(scales, torch.float32, "scales")
+    rows, cols = scales.shape
+    if exp_out is None:
+        exp_out = torch.empty((rows, cols), dtype=torch.uint8, device=scales.device)
+    _need(exp_out, torch.uint8, "exp_out")
+    bad = _I64(0)
+    st = lib().bsfp8_scales_from_f32(_ptr(scales), rows, cols, _ptr(exp_out), ctypes.byref(bad), _stream(scales))
+    if st < 0:
+        err = BsfpError(st, "bsfp8_scales_from_f32")
+        err.n_bad = bad.value
+        raise err
+    return exp_out
+
+
+Twin = namedtuple("Twin", "accepted q e ok n_bad")
+
+
+def bsfp8_make_twin(w):
+    """bf16 weight [G, R, D] -> Twin(accepted, q [G,R,D] uint8, e [G,R/32,D/32] uint8,
+    ok [G,R/32,D/32] uint8, n_bad)."""
+    _need(w, torch.bfloat16, "w")
+    if w.dim() != 3:
+        raise ValueError("w must be [G, R, D]")
+    G, R, D = w.shape
+    q = torch.empty((G, R, D), dtype=torch.uint8, device=w.device)
+    e = torch.empty((G, R // 32, D // 32), dtype=torch.uint8, device=w.device)
+    ok = torch.empty((G, R // 32, D // 32), dtype=torch.uint8, device=w.device)
+    bad = _I64(0)
+    st = _check(lib().bsfp8_make_twin(_ptr(w), G, R, D, _ptr(q), _ptr(e), _ptr(ok), ctypes.byref(bad),
+                                      _stream(w)), "bsfp8_make_twin")
+    return Twin(st == OK, q, e, ok, bad.value)
+
+
+def make_twin(w):
+    """(q, e) when the twin rebuilds w bit for bit, else None (the page's make_twin contract)."""
+    t = bsfp8_make_twin(w)
+    return (t.q, t.e) if t.accepted else None
+
+
+def bsfp8_pad_k_weight(q, e, K_pad):
+    """Twin codes [G,N,K] and exponents [G,N/32,K/32] -> padded to K_pad (zero codes, byte 127)."""
+    q = _codes(q)
+    _need(q, torch.uint8, "q")
+    _need(e, torch.uint8, "e")
+    G, N, K = q.shape
+    qp = torch.empty((G, N, K_pad), dtype=torch.uint8, device=q.device)
+    ep = torch.empty((G, N // 32, K_pad // 32), dtype=torch.uint8, device=q.device)
+    _check(lib().bsfp8_pad_k_weight(_ptr(q), _ptr(e), G, N, K, K_pad, _ptr(qp), _ptr(ep), _stream(q)),
+           "bsfp8_pad_k_weight")
+    return qp, ep
+
+
+def _x_view(x):
+    """Activation tensor -> (x, M, ldx). Accepts [M, L] with unit column stride or the page's
+    [M, G, K] layout with strides (ldx, K, 1)."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda:
+        raise TypeError("x must be a bf16 GPU tensor")
+    if x.dim() == 3:
+        M, G, K = x.shape
+        if x.stride(2) != 1 or x.stride(1) != K:
+            raise ValueError("x [M, G, K] must have strides (ldx, K, 1)")
+        return x, M, x.stride(0) if M > 1 else G * K
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [M, L] with unit column stride")
+    return x, x.shape[0], x.stride(0) if x.shape[0] > 1 else x.shape[1]
+
+
+def bsfp8_pad_k_input(x, G, K, K_pad, out=None):
+    """x [M, >=G*K] (group g at columns g*K) -> [M, G*K_pad] with zero tails."""
+    x, M, ldx = _x_view(x)
+    if out is None:
+        out = torch.empty((M, G * K_pad), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out")
+    _check(lib().bsfp8_pad_k_input(_ptr(x), ldx, M, G, K, K_pad, _ptr(out), _stream(x)), "bsfp8_pad_k_input")
+    return out
+
+
+def bsfp8_dequant(q, e, out=None):
+    """Twin -> bf16 weight [G, N, K], exact."""
+    q = _codes(q)
+    _need(q, torch.uint8, "q")
+    _need(e, torch.uint8, "e")
+    G, N, K = q.shape
+    if out is None:
+        out = torch.empty((G, N, K), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out")
+    _check(lib().bsfp8_dequant(_ptr(q), _ptr(e), G, N, K, _ptr(out), _stream(q)), "bsfp8_dequant")
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# per call
+# ------------------------------------------------------------------------------------------------
+def bsfp8_workspace_bytes(M, G, N, K, split_k=0):
+    return int(lib().bsfp8_workspace_bytes(M, G, N, K, split_k))
+
+
+def workspace(M, G, N, K, split_k=0, device="cuda"):
+    """A zero-filled workspace tensor for these sizes (or None when none is needed)."""
+    n = bsfp8_workspace_bytes(M, G, N, K, split_k)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _gemm(entry, x, q, e, split_k, ws, out, out_dtype):
+    q = _codes(q)
+    _need(q, torch.uint8, "q")
+    _need(e, torch.uint8, "e")
+    G, N, K = q.shape
+    x, M, ldx = _x_view(x)
+    od = OUT_F32 if out_dtype in ("f32", torch.float32, OUT_F32) else OUT_BF16
+    if out is None:
+        out = torch.empty((M, G, N), dtype=torch.float32 if od == OUT_F32 else torch.bfloat16, device=x.device)
+    _need(out, torch.float32 if od == OUT_F32 else torch.bfloat16, "out")
+    if ws is None:
+        n = bsfp8_workspace_bytes(max(M, 1), G, N, K, split_k)
+        ws = torch.zeros(n, dtype=torch.uint8, device=x.device) if n else None
+    wsb = ws.numel() if ws is not None else 0
+    fn = getattr(lib(), entry)
+    _check(fn(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), split_k, _ptr(ws), wsb, _ptr(out), od, _stream(x)), entry)
+    return out
+
+
+def bsfp8_gemm(x, q, e, split_k=0, ws=None, out=None, out_dtype="bf16"):
+    """Y [M, G, N] = per group X[:, g*K:(g+1)*K] @ W_g^T, W_g rebuilt from the twin (q, e)."""
+    return _gemm("bsfp8_gemm", x, q, e, split_k, ws, out, out_dtype)
+
+
+def bsfp8_gemm_small(x, q, e, split_k=0, ws=None, out=None, out_dtype="bf16"):
+    return _gemm("bsfp8_gemm_small", x, q, e, split_k, ws, out, out_dtype)
+
+
+def bsfp8_gemm_mid(x, q, e, split_k=0, ws=None, out=None, out_dtype="bf16"):
+    return _gemm("bsfp8_gemm_mid", x, q, e, split_k, ws, out, out_dtype)
+
+
+# ------------------------------------------------------------------------------------------------
+# tuning interface (include/bsfp8_tuning.h)
+# ------------------------------------------------------------------------------------------------
+def bsfp8_num_configs():
+    return int(lib().bsfp8_num_configs())
+
+
+def bsfp8_config_info(cfg):
+    out = (_I * 4)()
+    _check(lib().bsfp8_config_info(cfg, out), "bsfp8_config_info")
+    return dict(BM=out[0], NB=out[1], threads=out[2], CW=out[3])
+
+
+def bsfp8_plan_info(M, G, N, K, split_k=0, path=2):
+    out = (_I * 8)()
+    _check(lib().bsfp8_plan_info(M, G, N, K, split_k, path, out), "bsfp8_plan_info")
+    keys = ("cfg", "BM", "NB", "kchunks", "cps", "splits", "mblocks", "workgroups")
+    return dict(zip(keys, list(out)))
+
+
+def bsfp8_workspace_bytes_config(M, G, N, K, cfg, cps):
+    return int(lib().bsfp8_workspace_bytes_config(M, G, N, K, cfg, cps))
+
+
+def bsfp8_gemm_config(x, q, e, cfg, cps, ws=None, out=None, out_dtype="bf16"):
+    q = _codes(q)
+    G, N, K = q.shape
+    x, M, ldx = _x_view(x)
+    od = OUT_F32 if out_dtype in ("f32", torch.float32, OUT_F32) else OUT_BF16
+    if out is None:
+        out = torch.empty((M, G, N), dtype=torch.float32 if od == OUT_F32 else torch.bfloat16, device=x.device)
+    if ws is None:
+        n = bsfp8_workspace_bytes_config(max(M, 1), G, N, K, cfg, cps)
+        ws = torch.zeros(n, dtype=torch.uint8, device=x.device) if n else None
+    wsb = ws.numel() if ws is not None else 0
+    _check(lib().bsfp8_gemm_config(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), cfg, cps, _ptr(ws), wsb,
+                                   _ptr(out), od, _stream(x)), "bsfp8_gemm_config")
+    return out

@@ -1,0 +1,244 @@
+// C ABI of the bsfp8 library: argument checks, dispatch and the synchronous prepare calls.
+// Everything that computes runs in the HIP kernels of gemm.hip and prep.hip.
+
+#include <stdint.h>
+
+#include "bsfp8_tuning.h"
+#include "internal.h"
+
+using namespace bsfp8;
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Size checks shared by the GEMM entry points and the plan report; fills `shape`.
+int check_dims(int64_t M, int64_t G, int64_t N, int64_t K, int split_k, int64_t max_m,
+               GemmShape* shape) {
+  if (M < 0 || M > max_m || G < 1 || N < 32 || K < 32) return BSFP8_ESHAPE;
+  if (N % 32 || K % 32) return BSFP8_ESHAPE;
+  if (G > 4096 || N > (1 << 24) || K > (1 << 24) || G * N > (1 << 26)) return BSFP8_ESHAPE;
+  if (split_k < 0 || split_k > 64) return BSFP8_EINVAL;
+  shape->ldx = G * K;
+  shape->M = (int)M;
+  shape->G = (int)G;
+  shape->N = (int)N;
+  shape->K = (int)K;
+  return BSFP8_OK;
+}
+
+// Checks shared by the GEMM entry points; fills `shape`.
+int check_gemm(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+               const uint8_t* q, const uint8_t* e, void* y, int out_dtype, int split_k,
+               int64_t max_m, GemmShape* shape) {
+  if (out_dtype != BSFP8_OUT_BF16 && out_dtype != BSFP8_OUT_F32) return BSFP8_EINVAL;
+  int st = check_dims(M, G, N, K, split_k, max_m, shape);
+  if (st != BSFP8_OK) return st;
+  if (M > 0 && (!x || !q || !e || !y)) return BSFP8_EINVAL;
+  if (ldx < G * K || ldx % 8) return BSFP8_ESTRIDE;
+  if (M > 0 && (!aligned16(x) || !aligned16(q) || !aligned16(y))) return BSFP8_ESTRIDE;
+  shape->ldx = ldx;
+  return BSFP8_OK;
+}
+
+int run_gemm(int path, int64_t max_m, const uint16_t* x, int64_t ldx, int64_t M, int64_t G,
+             int64_t N, int64_t K, const uint8_t* q, const uint8_t* e, int split_k, void* ws,
+             size_t ws_bytes, void* y, int out_dtype, void* stream) {
+  GemmShape s;
+  int st = check_gemm(x, ldx, M, G, N, K, q, e, y, out_dtype, split_k, max_m, &s);
+  if (st != BSFP8_OK || M == 0) return st;
+  GemmPlan p;
+  st = plan_gemm(s, path, split_k, &p);
+  if (st != BSFP8_OK) return st;
+  if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned16(ws))) return BSFP8_EWORKSPACE;
+  return launch_gemm(s, p, x, q, e, ws, y, out_dtype == BSFP8_OUT_F32, as_stream(stream));
+}
+
+// Device counter for the synchronous prepare calls: allocate, run, read back, free.
+struct Counter {
+  unsigned long long* dev = nullptr;
+  ~Counter() {
+    if (dev) (void)hipFree(dev);
+  }
+  int init(hipStream_t s) {
+    if (hipMalloc(reinterpret_cast<void**>(&dev), sizeof(unsigned long long)) != hipSuccess) return BSFP8_EHIP;
+    return hip_status(hipMemsetAsync(dev, 0, sizeof(unsigned long long), s));
+  }
+  int read(hipStream_t s, unsigned long long* out) {
+    if (hipMemcpyAsync(out, dev, sizeof(*out), hipMemcpyDeviceToHost, s) != hipSuccess) return BSFP8_EHIP;
+    return hip_status(hipStreamSynchronize(s));
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* bsfp8_strerror(int status) {
+  switch (status) {
+    case BSFP8_OK: return "ok";
+    case BSFP8_NOT_EXACT: return "twin does not rebuild the weight exactly";
+    case BSFP8_EINVAL: return "invalid argument";
+    case BSFP8_ESHAPE: return "unsupported shape";
+    case BSFP8_ESCALE: return "block scale is not a positive finite power of two";
+    case BSFP8_ESTRIDE: return "bad leading dimension or alignment";
+    case BSFP8_EWORKSPACE: return "workspace missing or too small";
+    case BSFP8_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int bsfp8_abi_version(void) { return BSFP8_ABI_VERSION; }
+
+int bsfp8_scales_from_f32(const float* scales, int64_t rows, int64_t cols, uint8_t* exp_out,
+                          int64_t* n_bad_out, void* stream) {
+  if (rows < 0 || cols < 0) return BSFP8_ESHAPE;
+  const int64_t n = rows * cols;
+  if (n_bad_out) *n_bad_out = 0;
+  if (n == 0) return BSFP8_OK;
+  if (!scales || !exp_out) return BSFP8_EINVAL;
+  hipStream_t s = as_stream(stream);
+  Counter c;
+  int st = c.init(s);
+  if (st != BSFP8_OK) return st;
+  st = launch_scales_from_f32(scales, n, exp_out, c.dev, s);
+  if (st != BSFP8_OK) return st;
+  unsigned long long bad = 0;
+  st = c.read(s, &bad);
+  if (st != BSFP8_OK) return st;
+  if (n_bad_out) *n_bad_out = (int64_t)bad;
+  return bad ? BSFP8_ESCALE : BSFP8_OK;
+}
+
+int bsfp8_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t* q_out,
+                    uint8_t* e_out, uint8_t* block_ok, int64_t* n_bad_out, void* stream) {
+  if (G < 0 || R < 0 || D < 0 || R % 32 || D % 32) return BSFP8_ESHAPE;
+  if (n_bad_out) *n_bad_out = 0;
+  if (G * R * D == 0) return BSFP8_OK;
+  if (!w || !q_out || !e_out) return BSFP8_EINVAL;
+  if (!aligned16(w) || !aligned16(q_out)) return BSFP8_ESTRIDE;
+  hipStream_t s = as_stream(stream);
+  Counter c;
+  int st = c.init(s);
+  if (st != BSFP8_OK) return st;
+  st = launch_make_twin(w, G, R, D, q_out, e_out, block_ok, c.dev, s);
+  if (st != BSFP8_OK) return st;
+  unsigned long long bad = 0;
+  st = c.read(s, &bad);
+  if (st != BSFP8_OK) return st;
+  if (n_bad_out) *n_bad_out = (int64_t)bad;
+  return bad ? BSFP8_NOT_EXACT : BSFP8_OK;
+}
+
+int bsfp8_pad_k_weight(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
+                       int64_t K_pad, uint8_t* q_pad, uint8_t* e_pad, void* stream) {
+  if (G < 0 || N < 0 || K < 0 || N % 32 || K % 32 || K_pad % 32 || K_pad < K) return BSFP8_ESHAPE;
+  if (G * N * K_pad == 0) return BSFP8_OK;
+  if (!q_pad || !e_pad || (K > 0 && (!q || !e))) return BSFP8_EINVAL;
+  if ((K > 0 && !aligned16(q)) || !aligned16(q_pad)) return BSFP8_ESTRIDE;
+  return launch_pad_k_weight(q, e, G, N, K, K_pad, q_pad, e_pad, as_stream(stream));
+}
+
+int bsfp8_pad_k_input(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t K,
+                      int64_t K_pad, uint16_t* x_pad, void* stream) {
+  if (M < 0 || G < 1 || K < 0 || K % 32 || K_pad % 32 || K_pad < K) return BSFP8_ESHAPE;
+  if (ldx < G * K) return BSFP8_ESTRIDE;
+  if (M == 0 || K_pad == 0) return BSFP8_OK;
+  if (!x_pad || (K > 0 && !x)) return BSFP8_EINVAL;
+  return launch_pad_k_input(x, ldx, M, G, K, K_pad, x_pad, as_stream(stream));
+}
+
+int bsfp8_dequant(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
+                  uint16_t* w_out, void* stream) {
+  if (G < 0 || N < 0 || K < 0 || N % 32 || K % 32) return BSFP8_ESHAPE;
+  if (G * N * K == 0) return BSFP8_OK;
+  if (!q || !e || !w_out) return BSFP8_EINVAL;
+  if (!aligned16(q) || !aligned16(w_out)) return BSFP8_ESTRIDE;
+  return launch_dequant(q, e, G, N, K, w_out, as_stream(stream));
+}
+
+size_t bsfp8_workspace_bytes(int64_t M, int64_t G, int64_t N, int64_t K, int split_k) {
+  if (M <= 0 || G < 1 || N < 32 || K < 32 || N % 32 || K % 32 || split_k < 0 || split_k > 64) return 0;
+  if (M > 256 || G > 4096 || N > (1 << 24) || K > (1 << 24)) return 0;
+  GemmShape s{G * K, (int)M, (int)G, (int)N, (int)K};
+  size_t need = 0;
+  for (int path = PATH_SMALL; path <= PATH_MID; ++path) {
+    if (path == PATH_SMALL && M > 16) continue;
+    GemmPlan p;
+    if (plan_gemm(s, path, split_k, &p) == BSFP8_OK && p.ws_bytes > need) need = p.ws_bytes;
+  }
+  return need;
+}
+
+int bsfp8_gemm_small(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                     const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes,
+                     void* y, int out_dtype, void* stream) {
+  return run_gemm(PATH_SMALL, 16, x, ldx, M, G, N, K, q, e, split_k, ws, ws_bytes, y, out_dtype, stream);
+}
+
+int bsfp8_gemm_mid(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                   const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes,
+                   void* y, int out_dtype, void* stream) {
+  return run_gemm(PATH_MID, 256, x, ldx, M, G, N, K, q, e, split_k, ws, ws_bytes, y, out_dtype, stream);
+}
+
+int bsfp8_gemm(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+               const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes, void* y,
+               int out_dtype, void* stream) {
+  const int path = M <= 8 ? PATH_SMALL : PATH_MID;
+  return run_gemm(path, 256, x, ldx, M, G, N, K, q, e, split_k, ws, ws_bytes, y, out_dtype, stream);
+}
+
+int bsfp8_num_configs(void) { return num_gemm_configs(); }
+
+int bsfp8_config_info(int cfg, int* out) {
+  if (!out) return BSFP8_EINVAL;
+  return gemm_config_info(cfg, out);
+}
+
+int bsfp8_plan_info(int64_t M, int64_t G, int64_t N, int64_t K, int split_k, int path, int* out) {
+  if (!out) return BSFP8_EINVAL;
+  if (path < 0 || path > 2) return BSFP8_EINVAL;
+  const int p_eff = path == 2 ? (M <= 8 ? PATH_SMALL : PATH_MID) : path;
+  const int64_t max_m = p_eff == PATH_SMALL && path != 2 ? 16 : 256;
+  GemmShape s;
+  int st = check_dims(M, G, N, K, split_k, max_m, &s);
+  if (st != BSFP8_OK) return st;
+  if (M == 0) return BSFP8_ESHAPE;
+  GemmPlan p;
+  st = plan_gemm(s, p_eff, split_k, &p);
+  if (st != BSFP8_OK) return st;
+  out[0] = p.cfg;
+  out[1] = p.BM;
+  out[2] = p.NB;
+  out[3] = p.kchunks;
+  out[4] = p.cps;
+  out[5] = p.splits;
+  out[6] = p.mblocks;
+  out[7] = (int)((int64_t)p.splits * s.G * p.nblocks * p.mblocks);
+  return BSFP8_OK;
+}
+
+size_t bsfp8_workspace_bytes_config(int64_t M, int64_t G, int64_t N, int64_t K, int cfg, int cps) {
+  if (M <= 0 || M > 256 || G < 1 || N < 32 || K < 32 || N % 32 || K % 32 || cps < 1) return 0;
+  GemmShape s{G * K, (int)M, (int)G, (int)N, (int)K};
+  GemmPlan p;
+  if (plan_with(s, cfg, cps, &p) != BSFP8_OK) return 0;
+  return p.ws_bytes;
+}
+
+int bsfp8_gemm_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                      const uint8_t* q, const uint8_t* e, int cfg, int cps, void* ws,
+                      size_t ws_bytes, void* y, int out_dtype, void* stream) {
+  GemmShape s;
+  int st = check_gemm(x, ldx, M, G, N, K, q, e, y, out_dtype, 0, 256, &s);
+  if (st != BSFP8_OK || M == 0) return st;
+  GemmPlan p;
+  st = plan_with(s, cfg, cps, &p);
+  if (st != BSFP8_OK) return st;
+  if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned16(ws))) return BSFP8_EWORKSPACE;
+  return launch_gemm(s, p, x, q, e, ws, y, out_dtype == BSFP8_OUT_F32, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal declarations shared by the bsfp8 HIP sources (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bsfp8.h"
+
+namespace bsfp8 {
+
+// One output tile of a workgroup is BM x NB (rows of X x rows of W); K is walked in 128-wide
+// chunks. See gemm.hip for the meaning of each field.
+struct GemmShape {
+  int64_t ldx;
+  int M, G, N, K;
+};
+
+struct GemmPlan {
+  int cfg;          // index into the kernel configuration table
+  int BM, NB;       // workgroup tile
+  int kchunks;      // ceil(K / 128)
+  int cps;          // chunks per split
+  int splits;       // workgroups sharing one tile's K range
+  int mblocks;      // ceil(M / BM)
+  int nblocks;      // N / NB (per group)
+  size_t ws_bytes;  // workspace needed (0 when splits == 1)
+  size_t counter_bytes;
+};
+
+enum Path { PATH_SMALL = 0, PATH_MID = 1 };
+
+// Picks the kernel configuration and split for a shape; returns a bsfp8_status.
+int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan);
+// Plan for an explicit configuration index and chunks per split.
+int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan);
+int num_gemm_configs();
+// BM, NB, threads, chunks per wave per pass of a configuration.
+int gemm_config_info(int cfg, int* out);
+int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,
+                const uint8_t* e, void* ws, void* y, int out_f32, hipStream_t stream);
+
+int launch_scales_from_f32(const float* s, int64_t n, uint8_t* out, unsigned long long* bad,
+                           hipStream_t stream);
+int launch_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t* q, uint8_t* e,
+                     uint8_t* ok, unsigned long long* bad, hipStream_t stream);
+int launch_pad_k_weight(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
+                        int64_t K_pad, uint8_t* q_pad, uint8_t* e_pad, hipStream_t stream);
+int launch_pad_k_input(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t K,
+                       int64_t K_pad, uint16_t* x_pad, hipStream_t stream);
+int launch_dequant(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
+                   uint16_t* w, hipStream_t stream);
+
+inline int hip_status(hipError_t err) { return err == hipSuccess ? BSFP8_OK : BSFP8_EHIP; }
+
+}  // namespace bsfp8

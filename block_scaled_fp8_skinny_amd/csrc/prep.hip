@@ -1,0 +1,270 @@
+// Preparation kernels of the block-scaled fp8 weight path for gfx950: scale ingestion, the
+// exact-twin encoder, K padding and standalone dequantisation.
+
+#include "internal.h"
+
+namespace bsfp8 {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bits_of(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// ---------------------------------------------------------------------------------------------
+// fp32 block scales -> exponent bytes (page "shared_pad_k.py", _pad_weight: positive powers of
+// two only). One thread per scale; refused scales count into *bad and get byte 0.
+// ---------------------------------------------------------------------------------------------
+__global__ void scales_kernel(const uint32_t* s, int64_t n, uint8_t* out, unsigned long long* bad) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t u = s[i];
+  const uint32_t ef = (u >> 23) & 0xFF;
+  const bool ok = (u & 0x807FFFFFu) == 0 && ef >= 1 && ef <= 254;
+  out[i] = ok ? (uint8_t)ef : 0;
+  if (!ok) atomicAdd(bad, 1ull);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Twin encoder (page "wo_a_w8.py", make_twin). One wave per 32x32 block: lane l holds row l/2,
+// columns 16*(l&1) .. +15 of the block (two 16-byte loads).
+// ---------------------------------------------------------------------------------------------
+
+// Least e with max(amax, 2^-126) <= 448 * 2^e, from the bf16 pattern of amax (finite):
+// amax = (128 + f) * 2^(E - 134); 448 * 2^e = 7 * 2^(6 + e). For a normal amax the bound holds
+// with e = E - 135 when f <= 96 (mantissa <= 1.75) and needs e = E - 134 otherwise. Zero and
+// subnormal amax are raised to 2^-126, which gives e = -134, clamped to -127.
+__device__ __forceinline__ int block_exp(uint32_t amax_bits) {
+  const int E = (int)(amax_bits >> 7), f = (int)(amax_bits & 0x7F);
+  int e = (E == 0) ? -134 : (f <= 96 ? E - 135 : E - 134);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// e4m3 code of an fp32 value with |v| <= 448, round half to even (including the e4m3
+// subnormals, quantum 2^-9); magnitudes below 2^-10 give a signed zero.
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80;
+  const uint32_t a = u & 0x7FFFFFFF;
+  const uint32_t E = a >> 23;
+  uint32_t code;
+  if (E >= 121) {                                   // >= 2^-6: e4m3 normal range
+    const uint32_t keep = ((E - 120) << 3) | ((a >> 20) & 7);
+    const uint32_t rest = a & 0xFFFFF;
+    code = keep + ((rest > 0x80000u || (rest == 0x80000u && (keep & 1))) ? 1 : 0);
+  } else if (E == 0) {
+    code = 0;                                       // fp32 zero/subnormal: far below 2^-10
+  } else {
+    const uint32_t full = (a & 0x7FFFFF) | 0x800000; // value = full * 2^(E - 150)
+    const uint32_t sh = 141 - E;                     // quantum 2^-9 = 2^(E-150) * 2^sh
+    if (sh > 24) {
+      code = 0;
+    } else {
+      const uint32_t keep = full >> sh;
+      const uint32_t rest = full & ((1u << sh) - 1);
+      const uint32_t half = 1u << (sh - 1);
+      code = keep + ((rest > half || (rest == half && (keep & 1))) ? 1 : 0);
+    }
+  }
+  return sign | code;
+}
+
+__global__ void __launch_bounds__(256) make_twin_kernel(const uint16_t* w, int64_t nblk_r,
+                                                        int64_t nblk_c, int64_t D, int64_t nblocks,
+                                                        uint8_t* q, uint8_t* e, uint8_t* okv,
+                                                        unsigned long long* bad) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= nblocks) return;                       // whole wave exits together
+  const int64_t cb = blk % nblk_c;
+  const int64_t rb = (blk / nblk_c) % nblk_r;
+  const int64_t g = blk / (nblk_c * nblk_r);
+  const int64_t R = nblk_r * 32;
+  const int64_t row = g * R + rb * 32 + (lane >> 1);
+  const int64_t col = cb * 32 + (lane & 1) * 16;
+  const uint4* src = reinterpret_cast<const uint4*>(w + row * D + col);
+  const uint4 v0 = src[0], v1 = src[1];
+  uint32_t h[16];
+  const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[2 * i] = d[i] & 0xFFFF;
+    h[2 * i + 1] = d[i] >> 16;
+  }
+  uint32_t amax = 0;
+  bool finite = true;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t m = h[i] & 0x7FFF;
+    finite = finite && (m < 0x7F80);
+    amax = m > amax ? m : amax;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)amax, off);
+    amax = o > amax ? o : amax;
+  }
+  const bool all_finite = __all(finite);
+  const int eb = block_exp(amax);
+  const uint32_t eb_byte = (uint32_t)(eb + 127);
+  const float back_scale = __uint_as_float(eb_byte << 23);   // factor 2^e for the rebuild
+
+  uint32_t codes[16];
+  bool same = true;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float f = __uint_as_float(h[i] << 16);
+    const float sv = ldexpf(f, -eb);                          // exact (or below 2^-10)
+    codes[i] = e4m3_rne(sv);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    // bf16(e4m3(q) * 2^e) for two codes at once; exact RNE for every exponent byte
+    const bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[i] | (codes[i + 1] << 8),
+                                                                back_scale, false);
+    const uint32_t rb2 = bits_of(r);
+    same = same && ((rb2 & 0xFFFF) == h[i]) && ((rb2 >> 16) == h[i + 1]);
+  }
+  const bool ok = __all(same) && all_finite;
+  uint4 out;
+  uint32_t packed[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    packed[i] = codes[4 * i] | (codes[4 * i + 1] << 8) | (codes[4 * i + 2] << 16) | (codes[4 * i + 3] << 24);
+  out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  if (!all_finite) out = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  *reinterpret_cast<uint4*>(q + row * D + col) = out;
+  if (lane == 0) {
+    e[blk] = all_finite ? (uint8_t)eb_byte : (uint8_t)255;
+    if (okv) okv[blk] = ok ? 1 : 0;
+    if (!ok) atomicAdd(bad, 1ull);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// K padding of a twin (page "shared_pad_k.py", _pad_weight): zero codes, unit exponents.
+// One thread per 16 codes of the padded weight; one thread per padded exponent byte.
+// ---------------------------------------------------------------------------------------------
+__global__ void pad_codes_kernel(const uint8_t* q, int64_t rows, int64_t K, int64_t K_pad,
+                                 uint8_t* q_pad) {
+  const int64_t per_row = K_pad / 16;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * per_row) return;
+  const int64_t r = i / per_row, c = (i % per_row) * 16;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (c < K) v = *reinterpret_cast<const uint4*>(q + r * K + c);
+  *reinterpret_cast<uint4*>(q_pad + r * K_pad + c) = v;
+}
+
+__global__ void pad_exps_kernel(const uint8_t* e, int64_t rows, int64_t kb, int64_t kb_pad,
+                                uint8_t* e_pad) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * kb_pad) return;
+  const int64_t r = i / kb_pad, c = i % kb_pad;
+  e_pad[i] = c < kb ? e[r * kb + c] : (uint8_t)127;
+}
+
+// Activations (page "shared_pad_k.py", _pad_input): x [M][ldx] -> x_pad [M][G*K_pad] with a
+// zero tail per group. Vector form: one thread per 8 values; scalar form for odd strides.
+__global__ void pad_input_vec_kernel(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t K,
+                                     int64_t K_pad, uint16_t* x_pad) {
+  const int64_t per_row = G * K_pad / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M * per_row) return;
+  const int64_t m = i / per_row, c = (i % per_row) * 8;
+  const int64_t g = c / K_pad, k = c % K_pad;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (k < K) v = *reinterpret_cast<const uint4*>(x + m * ldx + g * K + k);
+  *reinterpret_cast<uint4*>(x_pad + m * G * K_pad + c) = v;
+}
+
+__global__ void pad_input_scalar_kernel(const uint16_t* x, int64_t ldx, int64_t M, int64_t G,
+                                        int64_t K, int64_t K_pad, uint16_t* x_pad) {
+  const int64_t per_row = G * K_pad;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M * per_row) return;
+  const int64_t m = i / per_row, c = i % per_row;
+  const int64_t g = c / K_pad, k = c % K_pad;
+  x_pad[i] = k < K ? x[m * ldx + g * K + k] : (uint16_t)0;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Standalone dequantisation (page "wo_a_w8.py", _dequant_kernel): one thread per 16 codes.
+// ---------------------------------------------------------------------------------------------
+__global__ void dequant_kernel(const uint8_t* q, const uint8_t* e, int64_t rows, int64_t K,
+                               uint16_t* w) {
+  const int64_t per_row = K / 16;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * per_row) return;
+  const int64_t r = i / per_row, c = (i % per_row) * 16;
+  // rows run over [G*N]; block rows over [G*N/32] in the same order
+  const uint32_t b = e[(r / 32) * (K / 32) + c / 32];
+  const float sc = __uint_as_float(b << 23);
+  const uint4 v = *reinterpret_cast<const uint4*>(q + r * K + c);
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o[2 * j] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[j], sc, false));
+    o[2 * j + 1] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[j], sc, true));
+  }
+  uint4* dst = reinterpret_cast<uint4*>(w + r * K + c);
+  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+inline unsigned grid_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+}  // namespace
+
+int launch_scales_from_f32(const float* s, int64_t n, uint8_t* out, unsigned long long* bad,
+                           hipStream_t stream) {
+  if (n == 0) return BSFP8_OK;
+  hipLaunchKernelGGL(scales_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint32_t*>(s), n, out, bad);
+  return hip_status(hipGetLastError());
+}
+
+int launch_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t* q, uint8_t* e,
+                     uint8_t* ok, unsigned long long* bad, hipStream_t stream) {
+  const int64_t nblocks = G * (R / 32) * (D / 32);
+  if (nblocks == 0) return BSFP8_OK;
+  hipLaunchKernelGGL(make_twin_kernel, dim3(grid_for(nblocks, 4)), dim3(256), 0, stream, w, R / 32,
+                     D / 32, D, nblocks, q, e, ok, bad);
+  return hip_status(hipGetLastError());
+}
+
+int launch_pad_k_weight(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
+                        int64_t K_pad, uint8_t* q_pad, uint8_t* e_pad, hipStream_t stream) {
+  const int64_t rows = G * N;
+  if (rows == 0) return BSFP8_OK;
+  hipLaunchKernelGGL(pad_codes_kernel, dim3(grid_for(rows * (K_pad / 16), 256)), dim3(256), 0,
+                     stream, q, rows, K, K_pad, q_pad);
+  hipLaunchKernelGGL(pad_exps_kernel, dim3(grid_for((rows / 32) * (K_pad / 32), 256)), dim3(256),
+                     0, stream, e, rows / 32, K / 32, K_pad / 32, e_pad);
+  return hip_status(hipGetLastError());
+}
+
+int launch_pad_k_input(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t K,
+                       int64_t K_pad, uint16_t* x_pad, hipStream_t stream) {
+  if (M == 0) return BSFP8_OK;
+  const bool vec = (ldx % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(x_pad) % 16 == 0);
+  if (vec)
+    hipLaunchKernelGGL(pad_input_vec_kernel, dim3(grid_for(M * G * K_pad / 8, 256)), dim3(256), 0,
+                       stream, x, ldx, M, G, K, K_pad, x_pad);
+  else
+    hipLaunchKernelGGL(pad_input_scalar_kernel, dim3(grid_for(M * G * K_pad, 256)), dim3(256), 0,
+                       stream, x, ldx, M, G, K, K_pad, x_pad);
+  return hip_status(hipGetLastError());
+}
+
+int launch_dequant(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K, uint16_t* w,
+                   hipStream_t stream) {
+  const int64_t rows = G * N;
+  if (rows == 0 || K == 0) return BSFP8_OK;
+  hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(rows * (K / 16), 256)), dim3(256), 0, stream, q,
+                     e, rows, K, w);
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace bsfp8

@@ -1,0 +1,161 @@
+/*
+ * bsfp8 -- block-scaled fp8 weight GEMM for small row counts on AMD MI355X (gfx950).
+ *
+ * The operation (page "recipes/docker-images/mia-tp4/adapter/wo_a_w8.py", module docstring and
+ * kernels _wo_a_partial_w8 / _wo_a_mid_kernel): a weight is stored as e4m3 ("float8_e4m3fn")
+ * codes q[g][n][k] plus one exponent byte b per 32x32 block; the weight value is
+ * bf16(e4m3(q) * 2^(b-127)), rebuilt exactly in registers. For bf16 activations X the library
+ * computes, per group g,
+ *
+ *     Y[m][g][n] = sum_k X[m][g*K + k] * W[g][n][k]
+ *
+ * with fp32 accumulation and a fixed summation order, and stores Y as bf16 (RNE) or fp32.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated "host". bf16 values are passed as their 16-bit
+ *     patterns (uint16_t). The caller owns every buffer; the library keeps no state between
+ *     calls and allocates nothing in the per-call functions.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Per-call functions
+ *     only enqueue work: they never synchronise or allocate, so they can be captured in a HIP
+ *     graph. The "prepare" functions are synchronous: they enqueue, wait for the stream and
+ *     return a verdict.
+ *   - Every shape, stride, alignment or scale-layout mismatch is reported as a negative status
+ *     before anything is enqueued; nothing is silently degraded (page
+ *     "recipes/docker-images/mia-tp4/adapter/shared_pad_k.py", module docstring, last paragraph).
+ *   - Sizes are int64_t; an empty problem (M == 0) is a valid no-op.
+ */
+#ifndef BSFP8_H
+#define BSFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSFP8_ABI_VERSION 1
+
+/* Symbols of the shared library; everything else in it is hidden. */
+#if defined(__GNUC__) || defined(__clang__)
+#define BSFP8_API __attribute__((visibility("default")))
+#else
+#define BSFP8_API
+#endif
+
+typedef enum bsfp8_status {
+  BSFP8_OK = 0,
+  BSFP8_NOT_EXACT = 1,      /* make_twin verdict: the twin does not rebuild the weight (not an error) */
+  BSFP8_EINVAL = -1,        /* null pointer where one is required, bad enum value */
+  BSFP8_ESHAPE = -2,        /* sizes out of range or not multiples of the 32x32 block */
+  BSFP8_ESCALE = -3,        /* a block scale is not a positive finite power of two */
+  BSFP8_ESTRIDE = -4,       /* leading dimension too small or misaligned, pointer not 16-byte aligned */
+  BSFP8_EWORKSPACE = -5,    /* workspace missing or smaller than bsfp8_workspace_bytes() */
+  BSFP8_EHIP = -6           /* a HIP runtime call failed */
+} bsfp8_status;
+
+typedef enum bsfp8_out {
+  BSFP8_OUT_BF16 = 0,       /* y is uint16_t bf16 patterns, round-half-to-even from fp32 */
+  BSFP8_OUT_F32 = 1         /* y is float (the LM-head logits of page
+                               "recipes/docker-images/mia-tp4/docs/tp4-adapters.md", row draft_head_fp8) */
+} bsfp8_out;
+
+/* Human-readable name of a status code (static string, never NULL). */
+BSFP8_API const char* bsfp8_strerror(int status);
+
+/* BSFP8_ABI_VERSION of the built library. */
+BSFP8_API int bsfp8_abi_version(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Prepare (load time; synchronous)
+ * ------------------------------------------------------------------------------------------ */
+
+/* fp32 block scales -> exponent bytes.
+ * Page "shared_pad_k.py", function _pad_weight: a block-fp8 weight [N,K] carries fp32 scales
+ * [N/32, K/32] that must be positive powers of two (zero fraction bits and > 0).
+ *   scales   : float [rows][cols], row-major, contiguous (device).
+ *   exp_out  : uint8_t [rows][cols] (device); byte = fp32 exponent field (2^(b-127) == scale).
+ *   n_bad_out: host, nullable; receives the number of refused scales.
+ * Refused: fraction bits set, zero, negative, subnormal, +inf, NaN. Returns BSFP8_ESCALE if any
+ * scale is refused (exp_out then holds 0 at those positions), BSFP8_ESHAPE if rows or cols < 0. */
+BSFP8_API int bsfp8_scales_from_f32(const float* scales, int64_t rows, int64_t cols, uint8_t* exp_out,
+                          int64_t* n_bad_out, void* stream);
+
+/* bf16 weight -> e4m3 twin, accepted only when it rebuilds the weight bit for bit.
+ * Page "wo_a_w8.py", function make_twin. Per 32x32 block: amax = max|w|; the block exponent e is
+ * the least integer with max(amax, 2^-126) <= 448 * 2^e, clamped to [-127, 127]; q = e4m3 RNE of
+ * w * 2^-e; the block is exact when bf16(e4m3(q) * 2^e) equals w in every bit.
+ *   w        : uint16_t bf16 [G][R][D] (device), R and D multiples of 32.
+ *   q_out    : uint8_t [G][R][D] (device).
+ *   e_out    : uint8_t [G][R/32][D/32] (device), byte = e + 127.
+ *   block_ok : uint8_t [G][R/32][D/32] (device, nullable): 1 exact, 0 not.
+ *   n_bad_out: host, nullable: number of blocks that are not exact.
+ * A block holding inf or NaN is never exact; it gets exponent byte 255 and codes 0x7F (e4m3 NaN).
+ * Returns BSFP8_OK when every block is exact, BSFP8_NOT_EXACT otherwise (the page then keeps the
+ * bf16 weight); outputs are written in both cases. */
+BSFP8_API int bsfp8_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t* q_out,
+                    uint8_t* e_out, uint8_t* block_ok, int64_t* n_bad_out, void* stream);
+
+/* Pad the contraction dimension of a twin: codes [G][N][K] -> [G][N][K_pad] with zero codes,
+ * exponents [G][N/32][K/32] -> [G][N/32][K_pad/32] with byte 127 (factor 1.0).
+ * Page "shared_pad_k.py", module docstring (WHAT THE PATCH DOES, item 1) and _pad_weight: the
+ * weight is padded with zeros and its scales with ones. K, K_pad multiples of 32, K_pad >= K.
+ * Asynchronous (no verdict). */
+BSFP8_API int bsfp8_pad_k_weight(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
+                       int64_t K_pad, uint8_t* q_pad, uint8_t* e_pad, void* stream);
+
+/* Standalone dequantisation of a twin to bf16 (page "wo_a_w8.py", _dequant_kernel and
+ * dequant_into_scratch): w_out[g][n][k] = bf16(e4m3(q) * 2^(b-127)), exact.
+ *   q: [G][N][K], e: [G][N/32][K/32], w_out: uint16_t [G][N][K] (all device, caller-owned). */
+BSFP8_API int bsfp8_dequant(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
+                  uint16_t* w_out, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Per call (asynchronous, graph-capturable, no allocation, no synchronisation)
+ * ------------------------------------------------------------------------------------------ */
+
+/* Pad activations: x [M][ldx] with group g at columns [g*K, (g+1)*K) -> x_pad [M][G*K_pad]
+ * (contiguous), group g at [g*K_pad, g*K_pad + K) and zeros in [g*K_pad + K, (g+1)*K_pad).
+ * Page "shared_pad_k.py", _pad_input (its tail stays zero). ldx >= G*K. */
+BSFP8_API int bsfp8_pad_k_input(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t K,
+                      int64_t K_pad, uint16_t* x_pad, void* stream);
+
+/* Workspace bytes the GEMM entry points need for this shape (0 when no split of K across
+ * workgroups is used). split_k as in the GEMM calls (0 = built-in table). The workspace holds
+ * fp32 split-K partials and one arrival counter per output tile. It must be ZERO-FILLED once
+ * after allocation; every call leaves the counters at zero again. One workspace must not be used
+ * by two calls that can run at the same time (e.g. on two streams). */
+BSFP8_API size_t bsfp8_workspace_bytes(int64_t M, int64_t G, int64_t N, int64_t K, int split_k);
+
+/* The GEMM. Page "wo_a_w8.py": _wo_a_partial_w8 (2..8 rows) and _wo_a_mid_kernel (9..192 rows).
+ *   x       : uint16_t bf16 [M][ldx] (device, 16-byte aligned), group g at columns [g*K,(g+1)*K);
+ *             ldx >= G*K and ldx % 8 == 0.
+ *   q, e    : twin codes [G][N][K] and exponent bytes [G][N/32][K/32] (device, 16-byte aligned);
+ *             N and K multiples of 32. Exponent byte 255 and e4m3 NaN codes give NaN outputs.
+ *   split_k : number of workgroups that share one output tile's K range (fixed-order reduction);
+ *             0 = the built-in table for this shape; otherwise 1..64.
+ *   ws      : workspace of ws_bytes >= bsfp8_workspace_bytes(M,G,N,K,split_k) (may be NULL when
+ *             that is 0).
+ *   y       : [M][G][N] contiguous, bf16 (uint16_t) or float per out_dtype (device, 16-byte
+ *             aligned); must not overlap x, q, e or ws.
+ * Summation order: each output is an fp32 sum over 128-wide K chunks in a fixed order that
+ * depends only on (M, G, N, split_k) and on K rounded up to a multiple of 128, so results are
+ * bitwise reproducible run to run, and K zero-padded within the same multiple of 128 (e.g.
+ * 576 -> 640) gives bitwise the same Y (page "shared_pad_k.py", LOSSLESS).
+ * bsfp8_gemm_small takes 1 <= M <= 16, bsfp8_gemm_mid 1 <= M <= 256; bsfp8_gemm picks small for
+ * M <= 8 and mid above (page "wo_a_w8.py", module docstring: 2..8 rows vs 9..192 rows). */
+BSFP8_API int bsfp8_gemm_small(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                     const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes,
+                     void* y, int out_dtype, void* stream);
+BSFP8_API int bsfp8_gemm_mid(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                   const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes,
+                   void* y, int out_dtype, void* stream);
+BSFP8_API int bsfp8_gemm(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+               const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes,
+               void* y, int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSFP8_H */

@@ -1,0 +1,45 @@
+/*
+ * bsfp8 tuning interface: run the GEMM with an explicit kernel configuration, and describe the
+ * plan the built-in table picks. For sweeps and reports; applications use bsfp8.h.
+ *
+ * The GEMM computed is the one of bsfp8_gemm (page "recipes/docker-images/mia-tp4/adapter/
+ * wo_a_w8.py", kernels _wo_a_partial_w8 and _wo_a_mid_kernel, whose launch parameters are
+ * likewise a row-count table of tile sizes and splits).
+ */
+#ifndef BSFP8_TUNING_H
+#define BSFP8_TUNING_H
+
+#include "bsfp8.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Number of compiled kernel configurations (valid `cfg` values are 0 .. n-1). */
+BSFP8_API int bsfp8_num_configs(void);
+
+/* Tile of configuration `cfg`: out[0] = rows of X per workgroup (BM), out[1] = weight rows per
+ * workgroup (NB), out[2] = threads per workgroup, out[3] = chunks per wave per pass.
+ * Returns BSFP8_EINVAL for an unknown cfg. `out` is host memory of 4 ints. */
+BSFP8_API int bsfp8_config_info(int cfg, int* out);
+
+/* Plan the built-in table picks. path: 0 = small, 1 = mid, 2 = what bsfp8_gemm picks.
+ * out (host, 8 ints): cfg, BM, NB, kchunks, chunks per split, splits, m-blocks, workgroups.
+ * Returns a status as the GEMM calls would for this shape. */
+BSFP8_API int bsfp8_plan_info(int64_t M, int64_t G, int64_t N, int64_t K, int split_k, int path, int* out);
+
+/* Workspace bytes for an explicit configuration and chunks per split (cps >= 1). */
+BSFP8_API size_t bsfp8_workspace_bytes_config(int64_t M, int64_t G, int64_t N, int64_t K, int cfg, int cps);
+
+/* The GEMM with an explicit configuration `cfg` and `cps` 128-wide K chunks per split (the
+ * number of splits is ceil(ceil(K/128) / cps)). Arguments and errors otherwise as bsfp8_gemm;
+ * 1 <= M <= 256. N must be a multiple of the configuration's NB (else BSFP8_ESHAPE). */
+BSFP8_API int bsfp8_gemm_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                      const uint8_t* q, const uint8_t* e, int cfg, int cps, void* ws,
+                      size_t ws_bytes, void* y, int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSFP8_TUNING_H */

@@ -1,0 +1,90 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the headers declare, and its
+host-side logic (status strings, plans, workspace sizes, argument checks that return before any
+GPU work) behaves as documented. No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp8_skinny_amd as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from block_scaled_fp8_skinny_amd import build
+        build.build()
+    return B.lib()
+
+
+def _declared():
+    names = set()
+    for h in ("bsfp8.h", "bsfp8_tuning.h"):
+        with open(os.path.join(ROOT, "include", h)) as f:
+            names |= set(re.findall(r"BSFP8_API\s+[\w\s\*]*?\b(bsfp8_\w+)\s*\(", f.read()))
+    return names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 16
+    raw = ctypes.CDLL(B.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(raw, n), n
+    assert set(B._SIGS) == names      # the binding covers exactly the declared entry points
+
+
+def test_status_strings_and_version(lib):
+    assert lib.bsfp8_abi_version() == 1
+    for st in (0, 1, -1, -2, -3, -4, -5, -6):
+        assert B.strerror(st) and B.strerror(st) != "unknown status"
+    assert B.strerror(42) == "unknown status"
+
+
+def test_workspace_and_plans(lib):
+    # the headline decode shape splits K over workgroups: partials + counters
+    p = B.bsfp8_plan_info(6, 2, 1024, 4096)
+    assert p["splits"] * p["cps"] >= p["kchunks"] and p["workgroups"] >= 256
+    ws = B.bsfp8_workspace_bytes(6, 2, 1024, 4096)
+    assert ws >= p["splits"] * 6 * 2 * 1024 * 4 if p["splits"] > 1 else ws == 0
+    # K and K padded inside the same 128-chunk count get the same plan
+    assert B.bsfp8_plan_info(6, 1, 5120, 576) == B.bsfp8_plan_info(6, 1, 5120, 640)
+    # explicit split_k
+    p8 = B.bsfp8_plan_info(6, 2, 1024, 4096, split_k=8)
+    assert p8["splits"] == 8
+    assert B.bsfp8_workspace_bytes(6, 2, 1024, 4096, 1) == 0
+    # the LM-head shape keeps one chunk map for every row count (per-row fp32 logits identical)
+    maps = {tuple(B.bsfp8_plan_info(m, 1, 32768, 5120)[k] for k in ("kchunks", "cps", "splits"))
+            for m in (16, 64, 128)}
+    assert len(maps) == 1
+    for cfg in range(B.bsfp8_num_configs()):
+        info = B.bsfp8_config_info(cfg)
+        assert info["BM"] % 16 == 0 and info["NB"] % 16 == 0 and info["threads"] % 64 == 0
+
+
+def test_argument_checks_return_before_gpu_work(lib):
+    null = ctypes.c_void_p(0)
+    G = lib.bsfp8_gemm
+    # bad out dtype, bad shapes, split_k out of range, null pointers, bad ldx: all host checks
+    assert G(null, 64, 1, 1, 64, 64, null, null, 0, null, 0, null, 7, null) == B.EINVAL
+    assert G(null, 64, 1, 1, 64, 40, null, null, 0, null, 0, null, 0, null) == B.ESHAPE
+    assert G(null, 64, 300, 1, 64, 64, null, null, 0, null, 0, null, 0, null) == B.ESHAPE
+    assert G(null, 64, 1, 1, 64, 64, null, null, 65, null, 0, null, 0, null) == B.EINVAL
+    assert G(null, 64, 1, 1, 64, 64, null, null, 0, null, 0, null, 0, null) == B.EINVAL
+    assert lib.bsfp8_gemm_small(null, 64, 17, 1, 64, 64, null, null, 0, null, 0, null, 0, null) == B.ESHAPE
+    assert G(null, 64, 0, 1, 64, 64, null, null, 0, null, 0, null, 0, null) == B.OK   # empty: no-op
+    fake = ctypes.c_void_p(4096)
+    assert G(fake, 60, 1, 1, 64, 64, fake, fake, 0, null, 0, fake, 0, null) == B.ESTRIDE
+    assert G(fake, 68, 1, 1, 64, 64, fake, fake, 0, null, 0, fake, 0, null) == B.ESTRIDE
+    assert G(ctypes.c_void_p(4104), 64, 1, 1, 64, 64, fake, fake, 0, null, 0, fake, 0, null) == B.ESTRIDE
+    # a split plan without its workspace
+    assert G(fake, 8192, 6, 2, 1024, 4096, fake, fake, 8, null, 0, fake, 0, null) == B.EWORKSPACE
+    bad = ctypes.c_int64(0)
+    assert lib.bsfp8_make_twin(null, 1, 33, 32, null, null, null, ctypes.byref(bad), null) == B.ESHAPE
+    assert lib.bsfp8_pad_k_weight(null, null, 1, 32, 64, 48, null, null, null) == B.ESHAPE
+    assert lib.bsfp8_pad_k_input(null, 10, 1, 1, 32, 64, null, null) == B.ESTRIDE
+    assert lib.bsfp8_dequant(null, null, 1, 32, 40, null, null) == B.ESHAPE
+    assert lib.bsfp8_scales_from_f32(null, -1, 2, null, ctypes.byref(bad), null) == B.ESHAPE

@@ -1,0 +1,226 @@
+"""GPU parity of the block-scaled fp8 GEMM against the CPU oracle, through the C ABI.
+
+Sizes here span several workgroup tiles, m-blocks, splits and ragged K tails while the float64
+oracle still finishes in seconds; full workload sizes are in test_gpu_workloads.py."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_skinny_amd as B
+import oracle
+import synthetic as S
+from parity import bf16_bits, check_bf16, check_f32, to_gpu_bf16, to_gpu_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, M, G, N, K, ldx=None, elo=110, ehi=130):
+    r = S.rng(seed)
+    ldx = ldx or G * K
+    x = S.bf16_normal(r, (M, ldx))
+    q = S.e4m3_codes(r, (G, N, K))
+    e = S.exponent_bytes(r, (G, N // 32, K // 32), elo, ehi)
+    return x, q, e
+
+
+def _run(entry, x, q, e, G, K, split_k=0, out_dtype="bf16"):
+    xt = to_gpu_bf16(x)
+    y = getattr(B, entry)(xt, to_gpu_u8(q), to_gpu_u8(e), split_k=split_k, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y
+
+
+SHAPES = [
+    (1, 1, 32, 32), (2, 2, 64, 160), (6, 1, 96, 576), (8, 2, 128, 1024), (5, 3, 64, 416),
+    (16, 1, 256, 2304), (7, 2, 192, 4096),
+]
+
+
+@pytest.mark.parametrize("M,G,N,K", SHAPES)
+@pytest.mark.parametrize("entry", ["bsfp8_gemm_small", "bsfp8_gemm"])
+def test_gemm_small_parity(entry, M, G, N, K):
+    x, q, e = _inputs(100 + M + K, M, G, N, K)
+    y = _run(entry, x, q, e, G, K)
+    assert y.shape == (M, G, N)
+    check_bf16(bf16_bits(y), x, G, N, K, q, e)
+
+
+@pytest.mark.parametrize("M,G,N,K", [(9, 2, 128, 1024), (17, 1, 64, 800), (33, 2, 128, 640),
+                                     (64, 1, 96, 4096), (100, 2, 64, 1152), (192, 1, 128, 512),
+                                     (256, 1, 64, 256)])
+def test_gemm_mid_parity(M, G, N, K):
+    x, q, e = _inputs(200 + M + K, M, G, N, K)
+    y = _run("bsfp8_gemm_mid", x, q, e, G, K)
+    check_bf16(bf16_bits(y), x, G, N, K, q, e)
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 3, 8, 64])
+def test_explicit_split_k(split_k):
+    M, G, N, K = 6, 2, 128, 2048
+    x, q, e = _inputs(300 + split_k, M, G, N, K)
+    y = _run("bsfp8_gemm", x, q, e, G, K, split_k=split_k)
+    check_bf16(bf16_bits(y), x, G, N, K, q, e)
+
+
+def test_every_kernel_configuration():
+    """Each compiled configuration, with a few chunks-per-split values, on a shape with several
+    m-blocks (where the tile is smaller than M), a ragged K tail and every N tile width."""
+    G, N, K = 2, 256, 800
+    for cfg in range(B.bsfp8_num_configs()):
+        info = B.bsfp8_config_info(cfg)
+        M = min(2 * info["BM"] - 3, 256)
+        x, q, e = _inputs(400 + cfg, M, G, N, K)
+        exact = oracle.gemm_exact_f64(x, G, N, K, q, e)
+        for cps in (1, 2, 7):
+            print(f"cfg {cfg} {info} cps {cps} M {M}", flush=True)
+            y = B.bsfp8_gemm_config(to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e), cfg, cps)
+            torch.cuda.synchronize()
+            check_bf16(bf16_bits(y), x, G, N, K, q, e, exact=exact)
+
+
+def test_fp32_output():
+    M, G, N, K = 12, 1, 256, 1536
+    x, q, e = _inputs(500, M, G, N, K, elo=118, ehi=122)
+    y = _run("bsfp8_gemm", x, q, e, G, K, out_dtype="f32")
+    assert y.dtype == torch.float32
+    check_f32(y.cpu().numpy(), x, G, N, K, q, e)
+
+
+def test_integer_exact_inputs_are_bitwise():
+    # small integers times integer-valued codes at factor 1: every partial sum is an exact fp32
+    # integer, so any summation order must equal the oracle bit for bit
+    M, G, N, K = 8, 2, 128, 1024
+    r = S.rng(600)
+    x = S.small_int_bf16(r, (M, G * K), -4, 4)
+    vals = oracle.decode_e4m3(np.arange(256))
+    codes = np.array([c for c in range(256) if np.isfinite(vals[c]) and vals[c] == int(vals[c])
+                      and abs(vals[c]) <= 16], dtype=np.uint8)
+    q = codes[r.integers(0, codes.size, (G, N, K))]
+    e = np.full((G, N // 32, K // 32), 127, dtype=np.uint8)
+    for entry, sk in (("bsfp8_gemm", 0), ("bsfp8_gemm", 3), ("bsfp8_gemm_mid", 0)):
+        y = bf16_bits(_run(entry, x, q, e, G, K, split_k=sk))
+        ref = oracle.gemm(x, G, N, K, q, e)
+        nz = (ref & 0x7FFF) != 0
+        assert np.array_equal(y[nz], ref[nz]), entry
+        assert np.all((y[~nz] & 0x7FFF) == 0)
+
+
+def test_one_hot_rows_give_the_weights_bitwise():
+    M, G, N, K = 4, 2, 128, 640
+    r = S.rng(601)
+    q = S.e4m3_codes(r, (G, N, K))
+    e = S.exponent_bytes(r, (G, N // 32, K // 32), 110, 130)
+    W = oracle.dequant_bf16(q, e)
+    ks = [0, 129, 383, 639]
+    for g in range(G):
+        x = np.zeros((M, G * K), dtype=np.uint16)
+        for m, k in enumerate(ks):
+            x[m, g * K + k] = 0x3F80
+        y = bf16_bits(_run("bsfp8_gemm", x, q, e, G, K))
+        for m, k in enumerate(ks):
+            want = W[g, :, k]
+            nz = (want & 0x7FFF) != 0
+            assert np.array_equal(y[m, g][nz], want[nz])
+            assert np.all((y[m, 1 - g] & 0x7FFF) == 0)
+
+
+def test_strided_and_3d_activation_layouts():
+    M, G, N, K = 5, 2, 64, 256
+    ldx = G * K + 24
+    x, q, e = _inputs(700, M, G, N, K, ldx=ldx)
+    xt = to_gpu_bf16(x)
+    y2 = B.bsfp8_gemm(xt, to_gpu_u8(q), to_gpu_u8(e))          # [M, ldx] with ldx > G*K
+    y3 = B.bsfp8_gemm(xt.as_strided((M, G, K), (ldx, K, 1)), to_gpu_u8(q), to_gpu_u8(e))
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y3)
+    check_bf16(bf16_bits(y2), x[:, : G * K], G, N, K, q, e)
+
+
+def test_run_to_run_bitwise_determinism():
+    M, G, N, K = 8, 2, 1024, 4096
+    x, q, e = _inputs(800, M, G, N, K, elo=115, ehi=125)
+    xt, qt, et = to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e)
+    for sk in (0, 8, 32):
+        ws = B.workspace(M, G, N, K, sk)
+        first = B.bsfp8_gemm(xt, qt, et, split_k=sk, ws=ws)
+        for _ in range(50):
+            again = B.bsfp8_gemm(xt, qt, et, split_k=sk, ws=ws)
+            assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+    torch.cuda.synchronize()
+
+
+def test_determinism_under_concurrent_load():
+    M, G, N, K = 6, 2, 1024, 4096
+    x, q, e = _inputs(801, M, G, N, K, elo=115, ehi=125)
+    xt, qt, et = to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e)
+    ref = B.bsfp8_gemm(xt, qt, et, split_k=8)
+    side = torch.cuda.Stream()
+    ws_main = B.workspace(M, G, N, K, 8)
+    ws_side = B.workspace(M, G, N, K, 8)
+    outs = []
+    torch.cuda.synchronize()
+    for i in range(20):
+        with torch.cuda.stream(side):
+            B.bsfp8_gemm(xt, qt, et, split_k=8, ws=ws_side)
+        outs.append(B.bsfp8_gemm(xt, qt, et, split_k=8, ws=ws_main))
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+
+
+def test_graph_replays_match_eager():
+    M, G, N, K = 6, 2, 1024, 4096
+    x, q, e = _inputs(802, M, G, N, K, elo=115, ehi=125)
+    xt, qt, et = to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e)
+    ws = B.workspace(M, G, N, K, 0)
+    out = torch.empty((M, G, N), dtype=torch.bfloat16, device="cuda")
+    eager = B.bsfp8_gemm(xt, qt, et, ws=ws).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.bsfp8_gemm(xt, qt, et, ws=ws, out=out)          # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.bsfp8_gemm(xt, qt, et, ws=ws, out=out)
+    for i in range(5):
+        out.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), i
+        B.bsfp8_gemm(xt, qt, et, ws=ws)                    # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_empty_and_error_cases():
+    G, N, K = 1, 64, 128
+    q = torch.zeros((G, N, K), dtype=torch.uint8, device="cuda")
+    e = torch.full((G, N // 32, K // 32), 127, dtype=torch.uint8, device="cuda")
+    x0 = torch.zeros((0, K), dtype=torch.bfloat16, device="cuda")
+    y0 = B.bsfp8_gemm(x0, q, e)
+    assert y0.shape == (0, G, N)
+    x = torch.zeros((17, K), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.BsfpError) as ei:
+        B.bsfp8_gemm_small(x, q, e)                         # small path takes at most 16 rows
+    assert ei.value.status == B.ESHAPE
+    with pytest.raises(B.BsfpError) as ei:
+        B.bsfp8_gemm(torch.zeros((257, K), dtype=torch.bfloat16, device="cuda"), q, e)
+    assert ei.value.status == B.ESHAPE
+    q_bad = torch.zeros((G, N, 100), dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.BsfpError) as ei:
+        B.bsfp8_gemm(torch.zeros((2, 100), dtype=torch.bfloat16, device="cuda"), q_bad,
+                     torch.zeros((1, 2, 3), dtype=torch.uint8, device="cuda"))
+    assert ei.value.status == B.ESHAPE
+    xs = torch.zeros((4, K + 3), dtype=torch.bfloat16, device="cuda")[:, :K]   # ldx % 8 != 0
+    with pytest.raises(B.BsfpError) as ei:
+        B.bsfp8_gemm(xs, q, e)
+    assert ei.value.status == B.ESTRIDE
+    n = B.bsfp8_workspace_bytes(6, 2, 1024, 4096, 8)
+    assert n > 0
+    small_ws = torch.zeros(n - 16, dtype=torch.uint8, device="cuda")
+    qq = torch.zeros((2, 1024, 4096), dtype=torch.uint8, device="cuda")
+    ee = torch.full((2, 32, 128), 127, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.BsfpError) as ei:
+        B.bsfp8_gemm(torch.zeros((6, 8192), dtype=torch.bfloat16, device="cuda"), qq, ee, split_k=8, ws=small_ws)
+    assert ei.value.status == B.EWORKSPACE
+    torch.cuda.synchronize()
