@@ -4,27 +4,36 @@
 // codes plus one exponent byte per 32x32 block and each tile is rebuilt exactly in bf16
 // registers before a bf16 MFMA with fp32 accumulation (page
 // "recipes/docker-images/mia-tp4/adapter/wo_a_w8.py": kernels _wo_a_partial_w8 and
-// _wo_a_mid_kernel; the split-K partials are summed in a fixed order, as its mid-path notes ask).
+// _wo_a_mid_kernel; its notes ask that split-K partials be summed in a fixed order).
 //
 // Design (gfx950, wave64):
 //  * MFMA v_mfma_f32_16x16x32_bf16 with the WEIGHT as the A operand (16 rows of W) and X^T as
-//    the B operand (16 rows of X), so D[n][m] holds four consecutive n per lane: one 8- or
-//    16-byte store per lane in the epilogue.
+//    the B operand (16 rows of X): D[n][m] holds four consecutive n per lane.
 //  * K is walked in 128-wide chunks. In a chunk each lane loads two 16-byte pieces of one weight
 //    row (k offsets 16*q and 64 + 16*q for lane group q = lane/16), i.e. a wave reads whole
 //    128-byte lines of 16 rows, straight from HBM into VGPRs.
+//  * Every global load is a raw buffer load: out-of-range offsets return zero, so masked
+//    pieces (ragged K tail, rows beyond M) need no branches, and the compiler can wait for each
+//    load individually. Dequant and MFMA of the first chunks therefore overlap the arrival of
+//    the later ones, and a multi-pass workgroup prefetches the next pass (X, exponents and
+//    weights) into registers before computing the current one.
 //  * Dequant is v_cvt_scalef32_pk_bf16_fp8: 2 codes -> 2 bf16 scaled by the block factor in one
 //    instruction, exact for every code and exponent byte 0..254 (checked on the hardware).
-//  * X and the exponent bytes of the workgroup's K range are staged in LDS; X is stored in MFMA
-//    fragment order (1 KB per 64-lane fragment), so every fragment read is one conflict-free
-//    ds_read_b128 per lane.
-//  * Waves of a workgroup split the n rows (NWN) and the chunks (NWK); partial tiles of the NWK
-//    waves are summed through LDS in ascending wave order. Workgroups can further split K
-//    (splits > 1): each writes fp32 partials, and the last to arrive at a tile (an atomic arrival
-//    counter) sums them in ascending split order and stores Y. The order never depends on which
-//    workgroup arrives last, so results are bitwise reproducible.
-//  * The map chunk -> (split, wave, step) depends only on the chunk index and the plan, not on
-//    K, so zero-padding K inside the same number of chunks leaves every fp32 sum unchanged.
+//  * X and the exponent bytes of a pass are staged in LDS; X is stored in MFMA fragment order
+//    and each thread writes the slot of its own lane, so every ds_write_b128 and ds_read_b128
+//    of a wave touches 1 KB of consecutive LDS (no bank conflicts). Rows at or beyond M are not
+//    written at all: they feed only MFMA output columns that are never stored.
+//  * Waves of a workgroup split the n rows (NWN) and the chunks (NWK); the NWK partial tiles are
+//    summed through LDS in ascending wave order. Workgroups may further split K (splits > 1).
+//    Their partials meet in a binary tree of pairwise combines: at each node the two partners
+//    swap their fp32 value into one 64-bit slot with an atomic exchange; the second to arrive
+//    gets the first one's value back, adds (a + b == b + a exactly in IEEE arithmetic, so the
+//    sum does not depend on who arrives first), clears the slot for the next call and carries
+//    the sum to the parent node. The tree's shape is fixed by the split index, so every output
+//    is bitwise reproducible, and the exchange carries the data itself: no counters, no fences,
+//    no waiting for stores to drain.
+//  * The map chunk -> (split, pass, wave, step) depends only on the chunk index and the plan,
+//    not on K, so zero-padding K inside the same chunk count leaves every fp32 sum unchanged.
 //  * Workgroup ids are remapped so that consecutive logical tiles run on the same XCD
 //    (workgroups are dealt round-robin over the 8 XCDs): splits sharing an X slab and m-blocks
 //    sharing a weight tile hit the same L2.
@@ -39,19 +48,24 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int KCH = 128;   // K per chunk
+constexpr int KCH = 128;                 // K per chunk
 constexpr int WAVE = 64;
+constexpr int MAX_LEVELS = 7;            // splits <= 64 -> at most 6 tree levels
+constexpr uint32_t OOB = 0x80000000u;    // buffer offset beyond every descriptor's range
+constexpr int RSRC_WORD3 = 0x00020000;   // raw buffer descriptor word 3 for gfx9-class GPUs
 
 struct KParams {
   const uint16_t* x;
-  int64_t ldx;
   const uint8_t* q;
   const uint8_t* e;
   void* y;
-  float* part;
-  uint32_t* counters;
+  unsigned long long* slots;             // pairwise-combine slots (splits > 1)
+  int64_t ldx;
+  uint32_t x_bytes, q_bytes, e_bytes;    // extents of the three buffer descriptors
   int M, G, N, K;
   int kchunks, cps, splits, mblocks, nblocks, out_f32;
+  int levels;
+  int level_base[MAX_LEVELS];            // first slot array of each tree level
 };
 
 __device__ __forceinline__ uint32_t bits_of(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
@@ -74,11 +88,58 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return bits_of(v);
 }
 
+__device__ __forceinline__ uint16_t to_bf16(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Logical workgroup index such that each XCD (hardware slot blockIdx % 8) owns a contiguous
 // range of logical indices.
 __device__ __forceinline__ int xcd_logical(int i, int nwg) {
   const int xcd = i & 7, idx = i >> 3, per = nwg >> 3, rem = nwg & 7;
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+}
+
+// Pairwise-combine tree over the split index for up to NV outputs of one lane (see the header
+// comment). v[i] is this split's partial of output i, off[i] its element index, live[i] whether
+// the lane owns it. All exchanges of one tree level are issued before any result is used, so a
+// level costs one round trip to memory. On return live[i] says whether this lane finished output
+// i (its total is then in v[i]).
+template <int NV>
+__device__ __forceinline__ void combine_splits(const KParams& p, int s, float (&v)[NV],
+                                               const size_t (&off)[NV], bool (&live)[NV]) {
+  const size_t mgn = (size_t)p.M * p.G * p.N;
+  int idx = s, cnt = p.splits;
+  for (int lv = 0; lv < p.levels; ++lv) {
+    if ((idx ^ 1) < cnt) {
+      unsigned long long* base = p.slots + (size_t)(p.level_base[lv] + (idx >> 1)) * mgn;
+      unsigned long long old[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        old[i] = live[i] ? atomicExch(base + off[i], (1ull << 32) | __float_as_uint(v[i])) : 0ull;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (!live[i]) continue;
+        if (old[i] == 0ull) {
+          live[i] = false;                          // the partner finishes this node
+        } else {
+          v[i] = __uint_as_float((uint32_t)old[i]) + v[i];
+          __hip_atomic_store(base + off[i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    idx >>= 1;
+    cnt = (cnt + 1) >> 1;
+  }
+}
+
+__device__ __forceinline__ void store_out(const KParams& p, size_t off, float v) {
+  if (p.out_f32)
+    reinterpret_cast<float*>(p.y)[off] = v;
+  else
+    reinterpret_cast<uint16_t*>(p.y)[off] = to_bf16(v);
 }
 
 template <int MT, int NT, int NWN, int NWK, int CW>
@@ -88,18 +149,18 @@ gemm_kernel(KParams p) {
   constexpr int BM = 16 * MT;
   constexpr int NB = 16 * NT * NWN;
   constexpr int PCH = NWK * CW;                     // chunks per pass
-  constexpr int XBYTES = PCH * 4 * MT * 1024;       // X fragments of one pass
+  constexpr int XSLOTS = PCH * 4 * MT * WAVE;       // 16-byte X fragment slots of one pass
+  constexpr int XBYTES = XSLOTS * 16;
   constexpr int EROWS = NB >= 32 ? NB / 32 : 1;
   constexpr int ECOLS = PCH * 4;
-  constexpr int XUNITS = BM * PCH * 16;             // 16-byte pieces of the pass's X tile
-  static_assert(XUNITS % NTHR == 0, "X staging must divide evenly over the threads");
-  constexpr int XPT = XUNITS / NTHR;
+  static_assert(XSLOTS % NTHR == 0, "X staging must divide evenly over the threads");
+  static_assert(EROWS * ECOLS <= NTHR, "one exponent byte per thread");
+  constexpr int XPT = XSLOTS / NTHR;
   constexpr int REDBYTES = (NWK - 1) * NWN * MT * NT * WAVE * 16;
-  static_assert(REDBYTES <= XBYTES, "the reduction buffer aliases the X buffer");
+  static_assert(REDBYTES <= XBYTES, "the wave reduction aliases the X buffer");
 
   __shared__ __attribute__((aligned(16))) uint8_t x_lds[XBYTES];
   __shared__ uint8_t e_lds[EROWS * ECOLS];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -114,51 +175,51 @@ gemm_kernel(KParams p) {
   const int g = t % p.G;
   const int s = t / p.G;
 
+  const int K = p.K, M = p.M, N = p.N, G = p.G;
   const int n0 = nb * NB, m0 = mb * BM;
   const int c_begin = s * p.cps;
   const int c_end = min(c_begin + p.cps, p.kchunks);
   const int npass = (c_end - c_begin + PCH - 1) / PCH;
-  const int K = p.K, M = p.M;
+  const int KB = K / 32;
 
-  const uint8_t* qg = p.q + (size_t)g * p.N * K;
-  const uint8_t* eg = p.e + (size_t)g * (p.N / 32) * (K / 32);
-  const uint16_t* xg = p.x + (size_t)g * K;
-  const int nrow = n0 + wn * 16 * NT + r16;         // + 16*ts: the weight row this lane loads
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, (int)p.x_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.q, 0, (int)p.q_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((void*)p.e, 0, (int)p.e_bytes, RSRC_WORD3);
+
+  // weight rows of this lane (+16*ts): byte offset of the row start in q
+  const int nrow = n0 + wn * 16 * NT + r16;
+  const uint32_t qrow = (uint32_t)(g * N + nrow) * (uint32_t)K;
   const int erow0 = n0 / 32;
+  const uint32_t ebase = (uint32_t)(g * (N / 32) + erow0) * (uint32_t)KB;
 
-  f32x4_t acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int pass = 0; pass < npass; ++pass) {
+  // ---- loaders (all branch-free; masked pieces read as zero) ----
+  auto load_x = [&](int pass, uint4 (&xr)[XPT]) {
     const int pc0 = c_begin + pass * PCH;
     const int pch = min(PCH, c_end - pc0);
-    if (pass) __syncthreads();                      // LDS of the previous pass fully consumed
-
-    // (1) X pieces of this pass (L2-resident, issued first so the waits below cover them only)
-    uint4 xv[XPT];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int u = tid + i * NTHR;
-      const int ml = u / (PCH * 16), kl = (u % (PCH * 16)) * 8;
-      const int m = m0 + ml, k = pc0 * KCH + kl;
-      xv[i] = make_uint4(0, 0, 0, 0);
-      if (m < M && kl < pch * KCH && k < K)
-        xv[i] = *reinterpret_cast<const uint4*>(xg + (size_t)m * p.ldx + k);
+      const int f = tid + i * NTHR;
+      const int blk = f >> 6, L = f & 63;
+      const int cp = blk / (4 * MT), jj = (blk / MT) & 3, mt = blk % MT;
+      const int m = m0 + mt * 16 + (L & 15);
+      const int k = (pc0 + cp) * KCH + (jj >> 1) * 64 + (L >> 4) * 16 + (jj & 1) * 8;
+      const bool ok = m < M && cp < pch && k < K;
+      const uint32_t off = (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K + k) * 2);
+      xr[i] = load16(rx, ok ? off : OOB);
     }
-    // (2) exponent bytes of this pass
-    uint32_t ev = 0;
-    static_assert(EROWS * ECOLS <= NTHR, "one exponent byte per thread");
-    const bool e_thread = tid < EROWS * ECOLS;
-    if (e_thread) {
-      const int er = tid / ECOLS, ec = tid % ECOLS;
-      const int kb = pc0 * 4 + ec;
-      if (ec < pch * 4 && kb < K / 32) ev = eg[(size_t)(erow0 + er) * (K / 32) + kb];
-    }
-    // (3) this wave's weight pieces, streamed from HBM into registers
-    uint4 wv[CW][NT][2];
+  };
+  auto load_e = [&](int pass) -> uint32_t {
+    const int pc0 = c_begin + pass * PCH;
+    const int pch = min(PCH, c_end - pc0);
+    const int er = tid / ECOLS, ec = tid % ECOLS;
+    const int kb = pc0 * 4 + ec;
+    const bool ok = tid < EROWS * ECOLS && ec < pch * 4 && kb < KB;
+    const uint32_t off = ebase + (uint32_t)(er * KB + kb);
+    return __builtin_amdgcn_raw_buffer_load_b8(re, (int)(ok ? off : OOB), 0, 0);
+  };
+  auto load_w = [&](int pass, uint4 (&wr)[CW][NT][2]) {
+    const int pc0 = c_begin + pass * PCH;
+    const int pch = min(PCH, c_end - pc0);
 #pragma unroll
     for (int j = 0; j < CW; ++j) {
       const int cp = wk + j * NWK;
@@ -167,25 +228,32 @@ gemm_kernel(KParams p) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int k = (pc0 + cp) * KCH + h * 64 + q4 * 16;
-          wv[j][ts][h] = make_uint4(0, 0, 0, 0);
-          if (cp < pch && k < K)
-            wv[j][ts][h] = *reinterpret_cast<const uint4*>(qg + (size_t)(nrow + ts * 16) * K + k);
+          const bool ok = cp < pch && k < K;
+          wr[j][ts][h] = load16(rq, ok ? qrow + (uint32_t)(ts * 16 * K + k) : OOB);
         }
     }
-    // (4) stage X in fragment order and the exponents
+  };
+  auto stage = [&](int pass, const uint4 (&xr)[XPT], uint32_t ev) {
+    if (pass) __syncthreads();                      // the previous pass is fully consumed
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int u = tid + i * NTHR;
-      const int ml = u / (PCH * 16), kl = (u % (PCH * 16)) * 8;
-      const int cp = kl / KCH, kk = kl % KCH;
-      const int jj = (kk / 64) * 2 + ((kk % 16) / 8);
-      const int fl = ((kk % 64) / 16) * 16 + (ml % 16);
-      *reinterpret_cast<uint4*>(x_lds + ((((cp * 4 + jj) * MT + ml / 16) * 64 + fl) * 16)) = xv[i];
+      const int f = tid + i * NTHR;
+      const int mt = (f >> 6) % MT;
+      if (m0 + mt * 16 + (f & 15) < M) *reinterpret_cast<uint4*>(x_lds + f * 16) = xr[i];
     }
-    if (e_thread) e_lds[tid] = (uint8_t)ev;
+    if (tid < EROWS * ECOLS) e_lds[tid] = (uint8_t)ev;
     __syncthreads();
+  };
 
-    // (5) dequant + MFMA, chunk by chunk in a fixed order
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int pass, const uint4 (&wr)[CW][NT][2]) {
+    const int pc0 = c_begin + pass * PCH;
+    const int pch = min(PCH, c_end - pc0);
 #pragma unroll
     for (int j = 0; j < CW; ++j) {
       const int cp = wk + j * NWK;
@@ -195,7 +263,7 @@ gemm_kernel(KParams p) {
           const int er = (nrow + ts * 16) / 32 - erow0;
           const float sc0 = block_scale(e_lds[er * ECOLS + cp * 4 + (q4 >> 1)]);
           const float sc1 = block_scale(e_lds[er * ECOLS + cp * 4 + 2 + (q4 >> 1)]);
-          const uint4 a = wv[j][ts][0], b = wv[j][ts][1];
+          const uint4 a = wr[j][ts][0], b = wr[j][ts][1];
           const bf16x8_t w0 = dequant8(a.x, a.y, sc0);
           const bf16x8_t w1 = dequant8(a.z, a.w, sc0);
           const bf16x8_t w2 = dequant8(b.x, b.y, sc1);
@@ -217,6 +285,30 @@ gemm_kernel(KParams p) {
         }
       }
     }
+  };
+
+  // ---- main loop: two register sets for the weights, next pass prefetched ----
+  uint4 xr[XPT];
+  uint4 wa[CW][NT][2], wb[CW][NT][2];
+  load_x(0, xr);                                    // X first (L2-resident), then exponents,
+  uint32_t ev = load_e(0);                          // then the HBM weight stream
+  load_w(0, wa);
+  for (int pass = 0; pass < npass; pass += 2) {
+    stage(pass, xr, ev);
+    if (pass + 1 < npass) {
+      load_x(pass + 1, xr);
+      ev = load_e(pass + 1);
+      load_w(pass + 1, wb);
+    }
+    compute(pass, wa);
+    if (pass + 1 >= npass) break;
+    stage(pass + 1, xr, ev);
+    if (pass + 2 < npass) {
+      load_x(pass + 2, xr);
+      ev = load_e(pass + 2);
+      load_w(pass + 2, wa);
+    }
+    compute(pass + 1, wb);
   }
 
   // Sum the NWK waves' tiles in ascending wave order (through LDS, aliasing the X buffer).
@@ -231,44 +323,17 @@ gemm_kernel(KParams p) {
           red[((((wk - 1) * NWN + wn) * MT + mt) * NT + ts) * WAVE + lane] = acc[mt][ts];
     }
     __syncthreads();
-    if (wk == 0) {
+    if (wk != 0) return;
 #pragma unroll
-      for (int w = 1; w < NWK; ++w)
+    for (int w = 1; w < NWK; ++w)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int ts = 0; ts < NT; ++ts)
-            acc[mt][ts] += red[((((w - 1) * NWN + wn) * MT + mt) * NT + ts) * WAVE + lane];
-    }
+        for (int ts = 0; ts < NT; ++ts)
+          acc[mt][ts] += red[((((w - 1) * NWN + wn) * MT + mt) * NT + ts) * WAVE + lane];
   }
 
-  const int G = p.G, N = p.N;
   if (p.splits == 1) {
-    if (wk == 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = m0 + mt * 16 + r16;
-        if (m < M) {
-#pragma unroll
-          for (int ts = 0; ts < NT; ++ts) {
-            const int n = n0 + wn * 16 * NT + ts * 16 + q4 * 4;
-            const size_t off = ((size_t)m * G + g) * N + n;
-            const f32x4_t v = acc[mt][ts];
-            if (p.out_f32) {
-              *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + off) = v;
-            } else {
-              uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + off) = o;
-            }
-          }
-        }
-      }
-    }
-    return;
-  }
-
-  // splits > 1: publish this split's partial tile, then the last arriver reduces.
-  if (wk == 0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = m0 + mt * 16 + r16;
@@ -276,38 +341,225 @@ gemm_kernel(KParams p) {
 #pragma unroll
         for (int ts = 0; ts < NT; ++ts) {
           const int n = n0 + wn * 16 * NT + ts * 16 + q4 * 4;
-          *reinterpret_cast<f32x4_t*>(p.part + (((size_t)s * M + m) * G + g) * N + n) = acc[mt][ts];
+          const size_t off = ((size_t)m * G + g) * N + n;
+          const f32x4_t v = acc[mt][ts];
+          if (p.out_f32) {
+            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + off) = v;
+          } else {
+            const uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + off) = o;
+          }
         }
       }
     }
+    return;
   }
-  __threadfence();                                  // release: partials visible device-wide
-  __syncthreads();
-  const int tile = (g * p.nblocks + nb) * p.mblocks + mb;
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(p.counters + tile, 1u);
-    s_last = (prev == (uint32_t)(p.splits - 1));
+
+  // splits > 1: pairwise-combine tree over the split index.
+  constexpr int NV = MT * NT * 4;
+  float v[NV];
+  size_t off[NV];
+  bool live[NV];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = (mt * NT + ts) * 4 + r;
+        const int m = m0 + mt * 16 + r16;
+        const int n = n0 + wn * 16 * NT + ts * 16 + q4 * 4 + r;
+        v[i] = acc[mt][ts][r];
+        off[i] = ((size_t)m * G + g) * N + n;
+        live[i] = m < M;
+      }
+  combine_splits<NV>(p, s, v, off, live);
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (live[i]) store_out(p, off[i], v[i]);
+}
+
+// Small-M kernel (at most 16 rows of X per workgroup, one pass over its K range). The weight
+// pieces go straight from HBM into the lane's MFMA registers. The workgroup's X rows (only the
+// rows below M) and exponent bytes are first loaded densely and coalesced, once per workgroup,
+// into LDS: X row-major with a 16-byte pad per row, so both the row-wise writes and the
+// fragment reads (16 rows at one k per 16 lanes) hit distinct banks. These L2-resident loads are
+// issued before the weight stream; each chunk's dequant + MFMA then waits only for its own
+// weight pieces. Each wave owns the chunks wk, wk + NWK, ... of the workgroup's range, so an
+// output's fp32 sum is the same ascending chain of chunks as in gemm_kernel with the same NWK
+// and chunks per split.
+template <int NT, int NWN, int NWK, int CW>
+__global__ void __launch_bounds__(WAVE * NWN * NWK)
+gemm_direct_kernel(KParams p) {
+  constexpr int NTHR = WAVE * NWN * NWK;
+  constexpr int NB = 16 * NT * NWN;
+  constexpr int PCH = NWK * CW;                     // chunks of the workgroup
+  constexpr int ROWB = PCH * KCH * 2 + 16;          // LDS bytes per X row (padded)
+  constexpr int XPIECES = 16 * PCH * 16;            // 16-byte pieces of 16 full rows
+  constexpr int XPT = (XPIECES + NTHR - 1) / NTHR;
+  constexpr int EROWS = NB >= 32 ? NB / 32 : 1;
+  constexpr int ECOLS = PCH * 4;
+  static_assert(EROWS * ECOLS <= NTHR, "one exponent byte per thread");
+  constexpr int RED = NWK > 1 ? (NWK - 1) * NWN * NT * WAVE : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t x_lds[16 * ROWB];
+  __shared__ uint8_t e_lds[EROWS * ECOLS];
+  __shared__ f32x4_t red[RED];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % NWN, wk = wave / NWN;
+  const int q4 = lane >> 4, r16 = lane & 15;
+
+  int t = xcd_logical(blockIdx.x, gridDim.x);
+  const int mb = t % p.mblocks;
+  t /= p.mblocks;
+  const int nb = t % p.nblocks;
+  t /= p.nblocks;
+  const int g = t % p.G;
+  const int s = t / p.G;
+
+  const int K = p.K, M = p.M, N = p.N, G = p.G;
+  const int n0 = nb * NB, m0 = mb * 16;
+  const int c_begin = s * p.cps;
+  const int c_end = min(c_begin + p.cps, p.kchunks);
+  const int KB = K / 32;
+  const int rows = min(16, M - m0);                 // X rows of this workgroup
+  const int k_lo = c_begin * KCH;
+
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, (int)p.x_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.q, 0, (int)p.q_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((void*)p.e, 0, (int)p.e_bytes, RSRC_WORD3);
+
+  // (1) X rows [m0, m0+rows) x k in [k_lo, k_lo + PCH*128): piece i of a row is 8 values
+  // (only ceil(rows * PCH * 16 / NTHR) of the XPT load slots are issued: a uniform bound)
+  const int xn = (rows * PCH * 16 + NTHR - 1) / NTHR;
+  uint4 xv[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int f = tid + i * NTHR;
+    const int row = f / (PCH * 16), pc = f % (PCH * 16);
+    const int k = k_lo + pc * 8;
+    const bool ok = f < rows * PCH * 16 && k < K && k < c_end * KCH;
+    const uint32_t off = (uint32_t)(((int64_t)(m0 + row) * p.ldx + (int64_t)g * K + k) * 2);
+    if (i < xn) xv[i] = load16(rx, ok ? off : OOB);
   }
+  // exponent bytes: EROWS block rows x the workgroup's K blocks
+  uint32_t ev;
+  {
+    const int er = tid / ECOLS, ec = tid % ECOLS;
+    const int kb = c_begin * 4 + ec;
+    const bool ok = tid < EROWS * ECOLS && kb < KB && kb < c_end * 4;
+    const uint32_t off = (uint32_t)((g * (N / 32) + n0 / 32 + er) * KB + kb);
+    ev = __builtin_amdgcn_raw_buffer_load_b8(re, (int)(ok ? off : OOB), 0, 0);
+  }
+  // Every wave's X and exponent requests enter the CU's memory pipeline before any weight
+  // request (a bare s_barrier: it waits for no data), so they are not queued behind HBM misses.
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NTHR > WAVE) __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  // (2) the weight pieces (HBM)
+  const int nrow = n0 + wn * 16 * NT + r16;         // + 16*ts
+  const uint32_t qrow = (uint32_t)(g * N + nrow) * (uint32_t)K;
+  uint4 wr[CW][NT][2];
+#pragma unroll
+  for (int j = 0; j < CW; ++j) {
+    const int c = c_begin + wk + j * NWK;
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = c * KCH + h * 64 + q4 * 16;
+        wr[j][ts][h] = load16(rq, (c < c_end && k < K) ? qrow + (uint32_t)(ts * 16 * K + k) : OOB);
+      }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // (3) stage X and the exponents in LDS
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int f = tid + i * NTHR;
+    const int row = f / (PCH * 16), pc = f % (PCH * 16);
+    if (i < xn && f < rows * PCH * 16) *reinterpret_cast<uint4*>(x_lds + row * ROWB + pc * 16) = xv[i];
+  }
+  if (tid < EROWS * ECOLS) e_lds[tid] = (uint8_t)ev;
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();                                  // acquire: see every split's partial
-  const int rows = min(BM, M - m0);
-  constexpr int C4 = NB / 4;
-  for (int idx = tid; idx < rows * C4; idx += NTHR) {
-    const int m = m0 + idx / C4, n = n0 + (idx % C4) * 4;
-    const size_t stride = (size_t)M * G * N;
-    const float* src = p.part + ((size_t)m * G + g) * N + n;
-    f32x4_t v = *reinterpret_cast<const f32x4_t*>(src);
-    for (int sp = 1; sp < p.splits; ++sp) v += *reinterpret_cast<const f32x4_t*>(src + sp * stride);
-    const size_t off = ((size_t)m * G + g) * N + n;
-    if (p.out_f32) {
-      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + off) = v;
-    } else {
-      uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + off) = o;
+  // (4) dequant + MFMA, chunk by chunk in ascending order. Chunks beyond the range were loaded
+  //     as zeros and add exact zeros; computing them unconditionally keeps every load ahead of
+  //     the first MFMA. X rows at or beyond M hold stale LDS data: they feed only MFMA output
+  //     columns that are never stored. Their reads stay inside the x_lds tile.
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int ts = 0; ts < NT; ++ts) acc[ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* xrow = x_lds + r16 * ROWB + q4 * 32;
+#pragma unroll
+  for (int j = 0; j < CW; ++j) {
+    const int cl = wk + j * NWK;                    // chunk index inside the workgroup
+    const bf16x8_t x0 = *reinterpret_cast<const bf16x8_t*>(xrow + cl * 256);
+    const bf16x8_t x1 = *reinterpret_cast<const bf16x8_t*>(xrow + cl * 256 + 16);
+    const bf16x8_t x2 = *reinterpret_cast<const bf16x8_t*>(xrow + cl * 256 + 128);
+    const bf16x8_t x3 = *reinterpret_cast<const bf16x8_t*>(xrow + cl * 256 + 144);
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) {
+      const int er = (nrow + ts * 16) / 32 - n0 / 32;
+      const float sc0 = block_scale(e_lds[er * ECOLS + cl * 4 + (q4 >> 1)]);
+      const float sc1 = block_scale(e_lds[er * ECOLS + cl * 4 + 2 + (q4 >> 1)]);
+      const uint4 a = wr[j][ts][0], b = wr[j][ts][1];
+      f32x4_t c = acc[ts];
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(a.x, a.y, sc0), x0, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(a.z, a.w, sc0), x1, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(b.x, b.y, sc1), x2, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(b.z, b.w, sc1), x3, c, 0, 0, 0);
+      acc[ts] = c;
     }
   }
-  if (tid == 0) p.counters[tile] = 0;               // ready for the next call
+  // (5) waves along K: ascending-order sum through LDS
+  if constexpr (NWK > 1) {
+    if (wk > 0) {
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) red[(((wk - 1) * NWN + wn) * NT + ts) * WAVE + lane] = acc[ts];
+    }
+    __syncthreads();
+    if (wk != 0) return;
+#pragma unroll
+    for (int w = 1; w < NWK; ++w)
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) acc[ts] += red[(((w - 1) * NWN + wn) * NT + ts) * WAVE + lane];
+  }
+  // (6) output
+  const int m = m0 + r16;
+  const bool mrow = m < M;
+  if (p.splits == 1) {
+    if (mrow) {
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) {
+        const int n = n0 + wn * 16 * NT + ts * 16 + q4 * 4;
+        const size_t o = ((size_t)m * G + g) * N + n;
+        const f32x4_t v = acc[ts];
+        if (p.out_f32) {
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + o) = v;
+        } else {
+          const uint2 w2 = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + o) = w2;
+        }
+      }
+    }
+    return;
+  }
+  constexpr int NV = NT * 4;
+  float v[NV];
+  size_t off[NV];
+  bool live[NV];
+#pragma unroll
+  for (int ts = 0; ts < NT; ++ts)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[ts * 4 + r] = acc[ts][r];
+      off[ts * 4 + r] = ((size_t)m * G + g) * N + n0 + wn * 16 * NT + ts * 16 + q4 * 4 + r;
+      live[ts * 4 + r] = mrow;
+    }
+  combine_splits<NV>(p, s, v, off, live);
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (live[i]) store_out(p, off[i], v[i]);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -318,9 +570,11 @@ typedef void (*KernelFn)(KParams);
 struct Config {
   int MT, NT, NWN, NWK, CW;
   KernelFn fn;
+  bool direct;                           // gemm_direct_kernel: one pass, at most 16 rows per block
 };
 
-#define CFG(MT, NT, NWN, NWK, CW) {MT, NT, NWN, NWK, CW, gemm_kernel<MT, NT, NWN, NWK, CW>}
+#define CFG(MT, NT, NWN, NWK, CW) {MT, NT, NWN, NWK, CW, gemm_kernel<MT, NT, NWN, NWK, CW>, false}
+#define DCFG(NT, NWN, NWK, CW) {1, NT, NWN, NWK, CW, gemm_direct_kernel<NT, NWN, NWK, CW>, true}
 
 const Config kConfigs[] = {
     CFG(1, 1, 4, 1, 4),   // 0  small: 64 rows, one wave per 16 rows, 4 chunks per wave
@@ -333,15 +587,33 @@ const Config kConfigs[] = {
     CFG(1, 1, 1, 1, 8),   // 7  small: 16 rows, one wave
     CFG(1, 1, 2, 2, 4),   // 8  small: 32 rows, 2x2 waves
     CFG(2, 1, 4, 1, 4),   // 9  mid: 32 x 64 tile
-    CFG(4, 1, 4, 1, 4),   // 10 mid: 64 x 64 tile
+    CFG(4, 1, 4, 1, 2),   // 10 mid: 64 x 64 tile
     CFG(4, 2, 2, 1, 2),   // 11 mid: 64 x 64 tile, two n-subtiles per wave
     CFG(2, 2, 2, 2, 2),   // 12 mid: 32 x 64 tile, 2 waves along K
     CFG(1, 2, 2, 2, 2),   // 13 small: 16 x 64 tile, 2 n-subtiles per wave
-    CFG(4, 2, 4, 1, 2),   // 14 mid: 64 x 128 tile
+    CFG(4, 2, 4, 1, 1),   // 14 mid: 64 x 128 tile
     CFG(2, 1, 2, 1, 4),   // 15 mid: 32 x 32 tile
-    CFG(4, 1, 2, 1, 4),   // 16 mid: 64 x 32 tile
+    CFG(4, 1, 2, 1, 2),   // 16 mid: 64 x 32 tile
+    CFG(1, 1, 2, 4, 4),   // 17 small: 32 rows, 4 waves along K, 4 chunks each
+    CFG(1, 1, 4, 2, 4),   // 18 small: 64 rows, 2 waves along K
+    DCFG(1, 1, 4, 4),     // 19 direct: 16 rows, 4 waves along K x 4 chunks
+    DCFG(1, 1, 8, 4),     // 20 direct: 16 rows, 8 waves along K x 4 chunks
+    DCFG(1, 1, 4, 2),     // 21 direct: 16 rows, 4 waves along K x 2 chunks
+    DCFG(1, 2, 4, 2),     // 22 direct: 32 rows, 4 waves along K x 2 chunks
+    DCFG(1, 1, 2, 4),     // 23 direct: 16 rows, 2 waves along K x 4 chunks
+    DCFG(1, 1, 4, 8),     // 24 direct: 16 rows, 4 waves along K x 8 chunks
+    DCFG(1, 2, 2, 4),     // 25 direct: 32 rows, 2 waves along K x 4 chunks
+    DCFG(1, 4, 1, 4),     // 26 direct: 64 rows, 1 wave along K x 4 chunks
+    DCFG(1, 1, 8, 2),     // 27 direct: 16 rows, 8 waves along K x 2 chunks
+    DCFG(2, 1, 4, 4),     // 28 direct: 32 rows (2 subtiles per wave), 4 waves along K
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+
+int tree_levels(int splits) {
+  int lv = 0;
+  for (int c = splits; c > 1; c = (c + 1) >> 1) ++lv;
+  return lv;
+}
 
 }  // namespace
 
@@ -354,6 +626,9 @@ int gemm_config_info(int cfg, int* out) {
   out[1] = 16 * c.NT * c.NWN;
   out[2] = WAVE * c.NWN * c.NWK;
   out[3] = c.CW;
+  out[4] = c.NWN;
+  out[5] = c.NWK;
+  out[6] = c.direct ? 1 : 0;
   return BSFP8_OK;
 }
 
@@ -370,31 +645,43 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   if (p.kchunks == 0) p.kchunks = 1;
   if (cps <= 0) return BSFP8_EINVAL;
   p.cps = cps < p.kchunks ? cps : p.kchunks;
+  if (c.direct && p.cps > c.NWK * c.CW) return BSFP8_EINVAL;   // one pass only
   p.splits = (p.kchunks + p.cps - 1) / p.cps;
+  if (p.splits > 64) return BSFP8_EINVAL;
   p.mblocks = (s.M + p.BM - 1) / p.BM;
   p.nblocks = s.N / p.NB;
   if (p.splits > 1) {
-    const size_t tiles = (size_t)s.G * p.nblocks * p.mblocks;
-    p.counter_bytes = (tiles * 4 + 255) & ~(size_t)255;
-    p.ws_bytes = p.counter_bytes + (size_t)p.splits * s.M * s.G * s.N * 4;
+    // one 64-bit slot per output element and tree node
+    size_t nodes = 0;
+    for (int c2 = p.splits; c2 > 1; c2 = (c2 + 1) >> 1) nodes += (size_t)(c2 >> 1);
+    p.ws_bytes = nodes * (size_t)s.M * s.G * s.N * 8;
   }
   *plan = p;
   return BSFP8_OK;
 }
 
-// Built-in choice. The key uses ceil(K/128), never K itself, so K and K zero-padded inside the
-// same chunk count get the same plan (and the same fp32 sums).
+// Built-in choice. The plan depends on K only through ceil(K/128), so K and K zero-padded
+// inside the same chunk count get the same plan (and the same fp32 sums). For wide weights
+// (at least 1024 tiles of 16 rows, e.g. an LM-head vocabulary shard) every row count uses one
+// wave per K range and no split: each output's fp32 sum is then the same chain of MFMAs for
+// every M, so a row's result does not depend on how many rows share the call.
 int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
   const int kchunks = (s.K + KCH - 1) / KCH > 0 ? (s.K + KCH - 1) / KCH : 1;
   const bool n64 = (s.N % 64) == 0;
+  const long long tiles16 = (long long)s.G * s.N / 16;
   int cfg, cps;
-  if (path == PATH_SMALL || s.M <= 16) {
+  if (tiles16 >= 1024) {
+    cps = kchunks;
+    if (path == PATH_SMALL || s.M <= 16) cfg = n64 ? 0 : 3;
+    else if (s.M <= 32) cfg = n64 ? 9 : 15;
+    else cfg = n64 ? 10 : 16;
+  } else if (path == PATH_SMALL || s.M <= 16) {
     if (kchunks <= 8) {
-      cfg = 7;                       // short K: one wave per 16 rows, no split
+      cfg = 25;                      // short K: register kernel, 32 rows, 2 waves along K, no split
       cps = kchunks;
     } else {
-      cfg = n64 ? 0 : 3;
-      cps = 4;
+      cfg = 20;                      // register kernel, 16 rows, 8 waves along K x 4 chunks
+      cps = 32;
     }
   } else if (s.M <= 32) {
     cfg = n64 ? 9 : 15;
@@ -409,14 +696,20 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
 
 int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,
                 const uint8_t* e, void* ws, void* y, int out_f32, hipStream_t stream) {
-  KParams k;
+  KParams k{};
   k.x = x;
-  k.ldx = s.ldx;
   k.q = q;
   k.e = e;
   k.y = y;
-  k.counters = reinterpret_cast<uint32_t*>(ws);
-  k.part = p.splits > 1 ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + p.counter_bytes) : nullptr;
+  k.slots = reinterpret_cast<unsigned long long*>(ws);
+  k.ldx = s.ldx;
+  const int64_t xb = ((int64_t)(s.M - 1) * s.ldx + (int64_t)s.G * s.K) * 2;
+  const int64_t qb = (int64_t)s.G * s.N * s.K;
+  const int64_t eb = (int64_t)s.G * (s.N / 32) * (s.K / 32);
+  if (xb >= (int64_t)OOB || qb >= (int64_t)OOB || eb >= (int64_t)OOB) return BSFP8_ESHAPE;
+  k.x_bytes = (uint32_t)xb;
+  k.q_bytes = (uint32_t)qb;
+  k.e_bytes = (uint32_t)eb;
   k.M = s.M;
   k.G = s.G;
   k.N = s.N;
@@ -427,6 +720,12 @@ int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const 
   k.mblocks = p.mblocks;
   k.nblocks = p.nblocks;
   k.out_f32 = out_f32;
+  k.levels = tree_levels(p.splits);
+  int base = 0, lv = 0;
+  for (int c2 = p.splits; c2 > 1; c2 = (c2 + 1) >> 1) {
+    k.level_base[lv++] = base;
+    base += c2 >> 1;
+  }
   const Config& c = kConfigs[p.cfg];
   const long long nwg = (long long)p.splits * s.G * p.nblocks * p.mblocks;
   if (nwg <= 0 || nwg > 0x7fffffffLL) return BSFP8_ESHAPE;

@@ -25,7 +25,6 @@ struct GemmPlan {
   int mblocks;      // ceil(M / BM)
   int nblocks;      // N / NB (per group)
   size_t ws_bytes;  // workspace needed (0 when splits == 1)
-  size_t counter_bytes;
 };
 
 enum Path { PATH_SMALL = 0, PATH_MID = 1 };

@@ -19,8 +19,12 @@ extern "C" {
 BSFP8_API int bsfp8_num_configs(void);
 
 /* Tile of configuration `cfg`: out[0] = rows of X per workgroup (BM), out[1] = weight rows per
- * workgroup (NB), out[2] = threads per workgroup, out[3] = chunks per wave per pass.
- * Returns BSFP8_EINVAL for an unknown cfg. `out` is host memory of 4 ints. */
+ * workgroup (NB), out[2] = threads per workgroup, out[3] = 128-wide K chunks per wave per pass,
+ * out[4] = waves along the weight rows, out[5] = waves along K (each output's fp32 sum is the
+ * ascending chain of the chunks one wave owns, so two plans with the same waves along K and the
+ * same chunks per split give bitwise the same outputs), out[6] = 1 for a one-pass register
+ * kernel (at most 16 rows of X per workgroup; chunks per split <= out[3] * out[5]).
+ * Returns BSFP8_EINVAL for an unknown cfg. `out` is host memory of 7 ints. */
 BSFP8_API int bsfp8_config_info(int cfg, int* out);
 
 /* Plan the built-in table picks. path: 0 = small, 1 = mid, 2 = what bsfp8_gemm picks.

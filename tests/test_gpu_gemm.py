@@ -71,7 +71,8 @@ def test_every_kernel_configuration():
         M = min(2 * info["BM"] - 3, 256)
         x, q, e = _inputs(400 + cfg, M, G, N, K)
         exact = oracle.gemm_exact_f64(x, G, N, K, q, e)
-        for cps in (1, 2, 7):
+        cps_list = (1, 2, 7) if not info["direct"] else sorted({1, 2, info["CW"] * info["NWK"]})
+        for cps in cps_list:
             print(f"cfg {cfg} {info} cps {cps} M {M}", flush=True)
             y = B.bsfp8_gemm_config(to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e), cfg, cps)
             torch.cuda.synchronize()
