@@ -7,9 +7,12 @@ cycle through enough distinct weight copies (>= 512 MiB, twice the 256 MiB Infin
 every call streams its weights from HBM. The timed calls are captured once in a HIP graph and
 replayed (as the pages time their kernels), between a synchronize and HIP events on both sides.
 
-value = effective weight-stream GB/s = (e4m3 bytes + exponent bytes) / wall time per call.
-roofline.achieved = algorithmic bytes (weights + exponents + X + Y) / mean kernel duration, where
-the kernel duration is measured with HIP events around each call, on the launch stream.
+value = effective weight-stream GB/s = (e4m3 bytes + exponent bytes) / time per call.
+roofline.achieved = algorithmic bytes (weights + exponents + X + Y) / time per call.
+The time per call is the timed graph replay (HIP events on the launch stream around it) divided
+by the number of calls in it: the average launch duration, gaps between launches included, which
+rocprofv3's average kernel duration for the same command matches within a few percent. HIP events
+around single eager calls are also reported; they include host launch gaps.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--m M]
        [--no-cpu-baseline] [--all FILE]
@@ -61,6 +64,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--all", default=None, help="also time every workload and row count; write JSON lines here")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB, 20 times (counter calibration)")
     return p.parse_args()
 
 
@@ -148,8 +153,8 @@ def time_workload(name, M, steps, warmup, split_k=0):
                copy_bytes=copy_bytes, wall_us_per_call=wall_us, kernel_us_mean=kern_us_mean,
                kernel_us_median=kern_us_median, weight_stream_gbs_wall=copy_bytes / (wall_us * 1e3),
                algorithmic_bytes=w_b + e_b + x_b + y_b, flops=2 * M * G * N * K,
-               algorithmic_gbs_kernel=(w_b + e_b + x_b + y_b) / (kern_us_mean * 1e3),
-               tflops_kernel=2 * M * G * N * K / (kern_us_mean * 1e6), wall_ms_total=wall_ms)
+               algorithmic_gbs=(w_b + e_b + x_b + y_b) / (wall_us * 1e3),
+               tflops=2 * M * G * N * K / (wall_us * 1e6), wall_ms_total=wall_ms)
     del qs, es
     torch.cuda.empty_cache()
     return res
@@ -170,7 +175,7 @@ def cpu_baseline(name, M, seconds):
     r = S.rng(9000 + M)
     x = S.bf16_normal(r, (M, G * K))
     calls, t_total = 0, 0.0
-    while t_total < seconds and calls < 50:
+    while t_total < seconds:
         q = S.e4m3_codes(r, (G, N, K))
         e = S.exponent_bytes(r, (G, N // 32, K // 32), elo, ehi)
         t0 = time.perf_counter()
@@ -213,6 +218,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 20}), flush=True)
+        return
     M = args.m or WORKLOADS[args.workload][3]
     r = time_workload(args.workload, M, args.steps, args.warmup, args.split_k)
     G, N, K = r["G"], r["N"], r["K"]
@@ -233,10 +247,10 @@ def main():
                    "weight_copies": r["copies"], "copy_bytes": r["copy_bytes"], "plan": r["plan"]},
         "us_per_call": round(r["wall_us_per_call"], 3),
         "pct_hbm_peak": round(100 * r["weight_stream_gbs_wall"] / HBM_PEAK_GBS, 1),
-        "kernel_us_mean": round(r["kernel_us_mean"], 3),
-        "kernel_us_median": round(r["kernel_us_median"], 3),
-        "roofline": {"bound": "hbm", "achieved": round(r["algorithmic_gbs_kernel"], 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(r["algorithmic_gbs_kernel"] / HBM_PEAK_GBS, 4),
+        "eager_event_us_per_call_mean": round(r["kernel_us_mean"], 3),
+        "eager_event_us_per_call_median": round(r["kernel_us_median"], 3),
+        "roofline": {"bound": "hbm", "achieved": round(r["algorithmic_gbs"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(r["algorithmic_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(args.workload, M),
                      "algorithmic_bytes_per_launch": r["algorithmic_bytes"]},
         "baseline_ref": "pages (GB10, other hardware): twin path 2.20 ms / 43 layers = 51.2 us/call at M=6",

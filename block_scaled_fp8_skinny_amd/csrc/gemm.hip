@@ -683,12 +683,15 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
       cfg = 20;                      // register kernel, 16 rows, 8 waves along K x 4 chunks
       cps = 32;
     }
-  } else if (s.M <= 32) {
-    cfg = n64 ? 9 : 15;
-    cps = 4;
+  } else if (s.M <= 64) {
+    cfg = 20;                        // register kernel per 16-row block of X, no split
+    cps = 32;
+  } else if (s.M <= 128) {
+    cfg = n64 ? 18 : 3;              // staged, 16 rows of X, 2 waves along K, no split
+    cps = kchunks;
   } else {
-    cfg = n64 ? 10 : 16;
-    cps = 4;
+    cfg = n64 ? 12 : 15;             // staged, 32 rows of X, 2 waves along K, no split
+    cps = kchunks;
   }
   if (split_k > 0) cps = (kchunks + split_k - 1) / split_k;
   return plan_with(s, cfg, cps, plan);
