@@ -64,6 +64,7 @@ struct KParams {
   uint32_t x_bytes, q_bytes, e_bytes;    // extents of the three buffer descriptors
   int M, G, N, K;
   int kchunks, cps, splits, mblocks, nblocks, out_f32;
+  int nwg;                               // grid size (gridDim would be read from the dispatch packet)
   int levels;
   int level_base[MAX_LEVELS];            // first slot array of each tree level
 };
@@ -95,11 +96,30 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Weight stream: read once per call, so it is loaded non-temporally ("nt") and does not evict
+// the activation slab, which every workgroup of the call re-reads from L2.
+constexpr int CPOL_NT = 2;
+__device__ __forceinline__ uint4 load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CPOL_NT);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Logical workgroup index such that each XCD (hardware slot blockIdx % 8) owns a contiguous
 // range of logical indices.
+// (Branch-free: XCDs below `rem` hold per + 1 workgroups, the others per.)
 __device__ __forceinline__ int xcd_logical(int i, int nwg) {
   const int xcd = i & 7, idx = i >> 3, per = nwg >> 3, rem = nwg & 7;
-  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  return xcd * per + min(xcd, rem) + idx;
+}
+
+// Fetch every kernel argument at entry: an empty asm that reads the fields makes the compiler
+// issue all the scalar argument loads together (one round trip) instead of in dependent rounds.
+__device__ __forceinline__ void prefetch_args(const KParams& p) {
+  asm volatile("" ::"s"(p.x), "s"(p.q), "s"(p.e), "s"(p.y), "s"(p.slots), "s"(p.ldx));
+  asm volatile("" ::"s"(p.x_bytes), "s"(p.q_bytes), "s"(p.e_bytes), "s"(p.M), "s"(p.G), "s"(p.N),
+               "s"(p.K));
+  asm volatile("" ::"s"(p.kchunks), "s"(p.cps), "s"(p.splits), "s"(p.mblocks), "s"(p.nblocks),
+               "s"(p.out_f32), "s"(p.nwg));
 }
 
 // Pairwise-combine tree over the split index for up to NV outputs of one lane (see the header
@@ -162,12 +182,13 @@ gemm_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t x_lds[XBYTES];
   __shared__ uint8_t e_lds[EROWS * ECOLS];
 
+  prefetch_args(p);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave % NWN, wk = wave / NWN;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  int t = xcd_logical(blockIdx.x, gridDim.x);
+  int t = xcd_logical(blockIdx.x, p.nwg);
   const int mb = t % p.mblocks;
   t /= p.mblocks;
   const int nb = t % p.nblocks;
@@ -229,7 +250,7 @@ gemm_kernel(KParams p) {
         for (int h = 0; h < 2; ++h) {
           const int k = (pc0 + cp) * KCH + h * 64 + q4 * 16;
           const bool ok = cp < pch && k < K;
-          wr[j][ts][h] = load16(rq, ok ? qrow + (uint32_t)(ts * 16 * K + k) : OOB);
+          wr[j][ts][h] = load16_stream(rq, ok ? qrow + (uint32_t)(ts * 16 * K + k) : OOB);
         }
     }
   };
@@ -405,12 +426,13 @@ gemm_direct_kernel(KParams p) {
   __shared__ uint8_t e_lds[EROWS * ECOLS];
   __shared__ f32x4_t red[RED];
 
+  prefetch_args(p);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave % NWN, wk = wave / NWN;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  int t = xcd_logical(blockIdx.x, gridDim.x);
+  int t = xcd_logical(blockIdx.x, p.nwg);
   const int mb = t % p.mblocks;
   t /= p.mblocks;
   const int nb = t % p.nblocks;
@@ -469,7 +491,7 @@ gemm_direct_kernel(KParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int k = c * KCH + h * 64 + q4 * 16;
-        wr[j][ts][h] = load16(rq, (c < c_end && k < K) ? qrow + (uint32_t)(ts * 16 * K + k) : OOB);
+        wr[j][ts][h] = load16_stream(rq, (c < c_end && k < K) ? qrow + (uint32_t)(ts * 16 * K + k) : OOB);
       }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -732,6 +754,7 @@ int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const 
   const Config& c = kConfigs[p.cfg];
   const long long nwg = (long long)p.splits * s.G * p.nblocks * p.mblocks;
   if (nwg <= 0 || nwg > 0x7fffffffLL) return BSFP8_ESHAPE;
+  k.nwg = (int)nwg;
   hipLaunchKernelGGL(c.fn, dim3((unsigned)nwg), dim3(WAVE * c.NWN * c.NWK), 0, stream, k);
   return hip_status(hipGetLastError());
 }
