@@ -38,6 +38,8 @@
 //    (workgroups are dealt round-robin over the 8 XCDs): splits sharing an X slab and m-blocks
 //    sharing a weight tile hit the same L2.
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace bsfp8 {
@@ -584,19 +586,521 @@ gemm_direct_kernel(KParams p) {
     if (live[i]) store_out(p, off[i], v[i]);
 }
 
+// Register kernel for mid row counts: BM = 16*MT rows of X and NB = 16*NT weight rows per
+// workgroup, NWK waves along K, one pass over the workgroup's K range. The waves of a workgroup
+// share nothing (each owns the chunks wk, wk + NWK, ...), so there is no LDS limit on the tile's
+// K extent; a ring of D chunk buffers per wave keeps D chunks of loads in flight (chunk j + D is
+// issued as soon as chunk j has been consumed).
+//  * X is read coalesced: each group of four lanes reads 64 contiguous bytes of one row (the MFMA
+//    layout would have every four lanes on four rows, i.e. four cache lines per quad). Each wave
+//    then turns its chunk into the MFMA layout through a private LDS tile: 16 rows x 256 bytes
+//    per 16-row block, granule g of row r stored at slot g ^ f(r) with f(r) = 4*(r%4) + r/4, so
+//    the coalesced writes (4 rows x 4 granules per 16 lanes) and the fragment reads (16 rows x
+//    one granule) both touch 16 distinct bank groups.
+//  * The weight pieces go straight into the MFMA registers, as in the other kernels.
+//  * The NWK partial tiles meet in LDS (each wave writes its own X area, so no barrier is needed
+//    before) and each wave sums, in ascending wave order, and stores its share of the tiles.
+template <int MT, int NT, int NWK, int CW, int D>
+__global__ void __launch_bounds__(WAVE * NWK)
+gemm_rows_kernel(KParams p) {
+  constexpr int NTHR = WAVE * NWK;
+  constexpr int BM = 16 * MT;
+  constexpr int NB = 16 * NT;
+  constexpr int PCH = NWK * CW;                     // chunks of the workgroup
+  constexpr int EROWS = NB >= 32 ? NB / 32 : 1;
+  constexpr int ECOLS = PCH * 4;
+  constexpr int TILES = MT * NT;
+  constexpr int TPW = (TILES + NWK - 1) / NWK;      // tiles summed and stored per wave
+  constexpr int XG = MT * 256;                      // 16-byte granules of one wave's X chunk
+  static_assert(EROWS * ECOLS <= NTHR, "one exponent byte per thread");
+  static_assert(D >= 1 && D <= CW, "ring depth");
+  static_assert(TILES * WAVE <= XG, "a wave's partial tiles fit in its X area");
+  __shared__ uint8_t e_lds[EROWS * ECOLS];
+  __shared__ uint4 xs[NWK * XG];
+
+  prefetch_args(p);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wk = tid >> 6;
+  const int q4 = lane >> 4, r16 = lane & 15;
+  const int cr = lane >> 2, cp = lane & 3;          // coalesced X: row cr, granule cp of 4
+
+  int t = xcd_logical(blockIdx.x, p.nwg);
+  const int mb = t % p.mblocks;
+  t /= p.mblocks;
+  const int nb = t % p.nblocks;
+  t /= p.nblocks;
+  const int g = t % p.G;
+  const int s = t / p.G;
+
+  const int K = p.K, M = p.M, N = p.N, G = p.G;
+  const int n0 = nb * NB, m0 = mb * BM;
+  const int c_begin = s * p.cps;
+  const int c_end = min(c_begin + p.cps, p.kchunks);
+  const int KB = K / 32;
+
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, (int)p.x_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.q, 0, (int)p.q_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((void*)p.e, 0, (int)p.e_bytes, RSRC_WORD3);
+
+  // exponent bytes: EROWS block rows x the workgroup's K blocks, one per thread, issued first
+  uint32_t ev;
+  {
+    const int er = tid / ECOLS, ec = tid % ECOLS;
+    const int kb = c_begin * 4 + ec;
+    const bool ok = tid < EROWS * ECOLS && kb < KB && kb < c_end * 4;
+    const uint32_t off = (uint32_t)((g * (N / 32) + n0 / 32 + er) * KB + kb);
+    ev = __builtin_amdgcn_raw_buffer_load_b8(re, (int)(ok ? off : OOB), 0, 0);
+  }
+
+  // X rows m0 + 16*mt + cr of this lane's coalesced loads (zero beyond M)
+  uint32_t xrow[MT];
+  bool xok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = m0 + mt * 16 + cr;
+    xok[mt] = m < M;
+    xrow[mt] = xok[mt] ? (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K) * 2) : 0u;
+  }
+  const uint32_t qrow = (uint32_t)(g * N + n0 + r16) * (uint32_t)K;   // weight row n0 + r16 (+16*ts)
+
+  // Chunk j of this wave is chunk c = c_begin + wk + j*NWK. X load i covers k in
+  // [c*128 + 32i, +32) of 16 rows; weight piece h covers k in c*128 + 64h + 16*q4 + [0, 16) of the
+  // lane's weight row. Out-of-range pieces read as zero.
+  struct Buf {
+    uint4 w[NT][2];
+    uint4 x[MT][4];
+  };
+  auto load = [&](int j, Buf& b) {
+    const int c = c_begin + wk + j * NWK;
+    const bool cok = c < c_end;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = c * KCH + 32 * i + 8 * cp;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        b.x[mt][i] = load16(rx, cok && k < K && xok[mt] ? xrow[mt] + (uint32_t)k * 2 : OOB);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = c * KCH + h * 64 + q4 * 16;
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts)
+        b.w[ts][h] = load16_stream(rq, cok && k < K ? qrow + (uint32_t)(ts * 16 * K + k) : OOB);
+    }
+  };
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) acc[mt][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4* const xw = xs + wk * XG;                   // this wave's X area
+  const int fw = ((cr & 3) << 2) | (cr >> 2);       // slot swizzle of the row this lane writes
+  const int fr = ((r16 & 3) << 2) | (r16 >> 2);     // ... and of the row it reads
+  auto compute = [&](int j, const Buf& b) {
+    const int cl = wk + j * NWK;                    // chunk index inside the workgroup
+    // X chunk -> LDS (row-major, swizzled) -> MFMA fragments: lane (r16, q4) takes the k values
+    // 64h + 16*q4 + 8u + [0, 8) of row r16 for MFMA 2h + u, the k values of its weight piece h.
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xw[mt * 256 + cr * 16 + ((4 * i + cp) ^ fw)] = b.x[mt][i];
+    bf16x8_t xf[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int gr = 8 * (f >> 1) + 2 * q4 + (f & 1);
+        xf[mt][f] = __builtin_bit_cast(bf16x8_t, xw[mt * 256 + r16 * 16 + (gr ^ fr)]);
+      }
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) {
+      const int er = (n0 + ts * 16 + r16) / 32 - n0 / 32;
+      const float sc0 = block_scale(e_lds[er * ECOLS + cl * 4 + (q4 >> 1)]);
+      const float sc1 = block_scale(e_lds[er * ECOLS + cl * 4 + 2 + (q4 >> 1)]);
+      const bf16x8_t w0 = dequant8(b.w[ts][0].x, b.w[ts][0].y, sc0);
+      const bf16x8_t w1 = dequant8(b.w[ts][0].z, b.w[ts][0].w, sc0);
+      const bf16x8_t w2 = dequant8(b.w[ts][1].x, b.w[ts][1].y, sc1);
+      const bf16x8_t w3 = dequant8(b.w[ts][1].z, b.w[ts][1].w, sc1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4_t c = acc[mt][ts];
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, xf[mt][0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, xf[mt][1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2, xf[mt][2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w3, xf[mt][3], c, 0, 0, 0);
+        acc[mt][ts] = c;
+      }
+    }
+  };
+
+  // Ring of D chunk buffers; chunks beyond the range were loaded as zeros and add exact zeros,
+  // so every wave runs the same straight-line sequence.
+  Buf ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) load(j, ring[j]);
+  __builtin_amdgcn_sched_barrier(0);
+  if (tid < EROWS * ECOLS) e_lds[tid] = (uint8_t)ev;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < CW; ++j) {
+    compute(j, ring[j % D]);
+    if (j + D < CW) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(j + D, ring[j % D]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Sum the NWK partial tiles in ascending wave order; wave w finishes tiles w, w + NWK, ...
+  f32x4_t v4[TPW];
+  int tix[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    tix[i] = NWK > 1 ? wk + i * NWK : i;
+    v4[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  if constexpr (NWK > 1) {
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(xs);  // wave w, tile tt: red[w*XG + tt*WAVE + lane]
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) red[wk * XG + (mt * NT + ts) * WAVE + lane] = acc[mt][ts];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      if (tix[i] < TILES) {
+        f32x4_t a = red[tix[i] * WAVE + lane];
+#pragma unroll
+        for (int w = 1; w < NWK; ++w) a += red[w * XG + tix[i] * WAVE + lane];
+        v4[i] = a;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) v4[i] = acc[i / NT][i % NT];
+  }
+
+  if (p.splits == 1) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int mt = tix[i] / NT, ts = tix[i] % NT;
+      const int m = m0 + mt * 16 + r16;
+      if (tix[i] < TILES && m < M) {
+        const size_t o = ((size_t)m * G + g) * N + n0 + ts * 16 + q4 * 4;
+        const f32x4_t v = v4[i];
+        if (p.out_f32) {
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + o) = v;
+        } else {
+          const uint2 w2 = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + o) = w2;
+        }
+      }
+    }
+    return;
+  }
+  constexpr int NV = TPW * 4;
+  float v[NV];
+  size_t off[NV];
+  bool live[NV];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int mt = tix[i] / NT, ts = tix[i] % NT;
+    const int m = m0 + mt * 16 + r16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[i * 4 + r] = v4[i][r];
+      off[i * 4 + r] = ((size_t)m * G + g) * N + n0 + ts * 16 + q4 * 4 + r;
+      live[i * 4 + r] = tix[i] < TILES && m < M;
+    }
+  }
+  combine_splits<NV>(p, s, v, off, live);
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (live[i]) store_out(p, off[i], v[i]);
+}
+
+// Tile kernel for many rows or wide weights: a BM x NB output tile per workgroup, BM = 16*MT*NWM
+// rows of X and NB = 16*NT*NWN weight rows, NWM x NWN waves (each a 16*MT x 16*NT sub-tile), one
+// 128-wide K chunk per step (K must be a multiple of 128).
+//  * Both operands stream from memory straight into LDS with the buffer loads' LDS mode (no
+//    VGPRs), through a ring of D stages: D - 1 chunks are in flight while one is computed. In a
+//    stage, the X chunk is row-major (16 lanes fill one 256-byte row, each lane fetching the
+//    granule that belongs in its slot), granule g of row r at slot g ^ (r % 16): the MFMA
+//    fragment reads (16 rows x one granule per quarter wave) then run without LDS bank conflicts
+//    (measured with the LDS bank-conflict counter; the XOR with r % 16 is one of the patterns that
+//    measure conflict-free on gfx950). The weight chunk is read with eight lanes per
+//    row (128 contiguous bytes per row and load: HBM streams this at about 6.7 TB/s on the
+//    wide-weight shapes, the MFMA lane order - four lanes per row - at about 4.6) and stored
+//    row-major, granule g of row R at slot g ^ (R/2 % 8), which spreads the fragment reads (16
+//    rows x one granule) over 16 bank groups.
+//  * The loads into LDS are not tracked by the compiler: each wave waits for its own loads of
+//    chunk j with an explicit s_waitcnt on the vector memory counter (every wave issues the same
+//    number of loads per chunk, out-of-range ones included), then one barrier per chunk makes the
+//    stage visible to all waves and guarantees that every wave has finished chunk j - 1, whose
+//    stage is refilled next.
+//  * The exponent bytes of the workgroup's K range are staged once.
+//  * With splits > 1 each workgroup stores its fp32 partial tile to the workspace [S][M][G][N]
+//    and a second kernel sums the partials in ascending split order.
+constexpr int TILE_MAX_CPS = 64;                    // exponent staging: at most 64 chunks per split
+
+// Workgroup barrier for the LDS ring: every LDS read of this wave has completed (lgkmcnt 0) and
+// no memory access moves across it, but - unlike __syncthreads(), whose fence would also wait for
+// the loads still streaming into the other stages - it does not wait for the vector memory
+// counter.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Buffer loads in LDS mode: lane l's bytes land at LDS address lds + l*size (lds is wave-uniform,
+// passed in M0; the compiler cannot prove that values derived from the wave index are uniform,
+// hence the readfirstlane). Written as inline assembly so that the compiler neither reorders them nor adds
+// waits of its own for them (it would wait for every load in flight before any LDS read); the
+// kernel counts them itself with wait_vmcnt_le.
+typedef uint32_t lds_addr_t;
+template <typename T>
+__device__ __forceinline__ lds_addr_t lds_addr(const T* p) {
+  return (lds_addr_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
+}
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_addr_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load16_stream(__amdgpu_buffer_rsrc_t r, lds_addr_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, lds_addr_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  // s_waitcnt with vmcnt = N (6 bits split over [3:0] and [15:14]), expcnt and lgkmcnt at max
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int MT, int NT, int NWM, int NWN, int D, int GI>
+__global__ void __launch_bounds__(WAVE * NWM * NWN)
+gemm_tile_kernel(KParams p) {
+  constexpr int NWAVE = NWM * NWN;
+  constexpr int NTHR = WAVE * NWAVE;
+  constexpr int BM = 16 * MT * NWM;
+  constexpr int NB = 16 * NT * NWN;
+  constexpr int XST = BM * 16;                      // 16-byte granules of an X stage
+  constexpr int WST = NB * 8;                       // ... of a weight stage (NB rows x 128 bytes)
+  constexpr int XI = BM / 4;                        // X loads per chunk (64 lanes = 4 rows)
+  constexpr int WI = NB / 8;                        // weight loads per chunk (16 rows x 64 bytes)
+  constexpr int PCX = XI / NWAVE, PCW = WI / NWAVE;
+  constexpr int PC = PCX + PCW;                     // loads per wave per chunk
+  constexpr int EROWS = NB / 32;
+  constexpr int ESTR = TILE_MAX_CPS * 4;            // bytes per exponent row (64 lanes x 4)
+  static_assert(XI % NWAVE == 0 && WI % NWAVE == 0, "every wave issues the same loads");
+  static_assert(GI >= 1 && D >= GI + 1 && (D - 2) * PC <= 63, "ring depth, issue group, counter range");
+  static_assert(NB % 32 == 0, "whole exponent block rows");
+  __shared__ uint4 ring[D][XST + WST];
+  __shared__ uint8_t e_lds[EROWS * ESTR];
+
+  prefetch_args(p);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int q4 = lane >> 4, r16 = lane & 15;
+
+  int t = xcd_logical(blockIdx.x, p.nwg);
+  const int mb = t % p.mblocks;
+  t /= p.mblocks;
+  const int nb = t % p.nblocks;
+  t /= p.nblocks;
+  const int g = t % p.G;
+  const int s = t / p.G;
+
+  const int K = p.K, M = p.M, N = p.N, G = p.G;
+  const int n0 = nb * NB, m0 = mb * BM;
+  const int c_begin = s * p.cps;
+  const int c_end = min(c_begin + p.cps, p.kchunks);
+  const int nch = c_end - c_begin;
+  const int KB = K / 32;
+
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, (int)p.x_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.q, 0, (int)p.q_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((void*)p.e, 0, (int)p.e_bytes, RSRC_WORD3);
+
+  // exponent bytes of the whole range, one 4-byte word (one chunk) per lane and block row,
+  // loaded first (K is a multiple of 128, so every word is aligned)
+  for (int er = wave; er < EROWS; er += NWAVE) {
+    const int kb = (c_begin + lane) * 4;
+    const uint32_t off = (uint32_t)((g * (N / 32) + n0 / 32 + er) * KB + kb);
+    lds_load4(re, lds_addr(e_lds + er * ESTR), lane < nch && kb < KB ? off : OOB);
+  }
+
+  // This lane's share of the loads of a chunk (the chunk index only adds c*128 to the offsets).
+  //  X load t: rows 4*i .. 4*i+3 (i = wave + t*NWAVE); the lane fills row 4i + q4, slot r16 with
+  //  granule r16 ^ (row % 16) of that row.
+  uint32_t xoff[PCX];
+  bool xok[PCX];
+#pragma unroll
+  for (int u = 0; u < PCX; ++u) {
+    const int i = wave + u * NWAVE;
+    const int row = 4 * i + q4;
+    const int gsrc = r16 ^ (row & 15);
+    const int m = m0 + row;
+    xok[u] = m < M;
+    xoff[u] = xok[u] ? (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K + gsrc * 8) * 2) : 0u;
+  }
+  //  weight load t: i = wave + t*NWAVE covers weight rows 8i .. 8i+7, eight lanes per row (128
+  //  contiguous bytes per row: the DRAM-friendly width); the lane fills row R = 8i + lane/8, slot
+  //  lane%8 with granule (lane%8) ^ ((R/2) % 8) of the row's chunk.
+  uint32_t woff[PCW];
+#pragma unroll
+  for (int u = 0; u < PCW; ++u) {
+    const int i = wave + u * NWAVE;
+    const int row = 8 * i + (lane >> 3);
+    const int gsrc = (lane & 7) ^ ((row >> 1) & 7);
+    woff[u] = (uint32_t)(g * N + n0 + row) * (uint32_t)K + 16 * gsrc;
+  }
+  auto issue = [&](int j) {
+    const int c = c_begin + j;
+    const bool cok = c < c_end;
+    const uint4* st = ring[j % D];
+#pragma unroll
+    for (int u = 0; u < PCX; ++u) {
+      const int i = wave + u * NWAVE;
+      lds_load16(rx, lds_addr(st + 4 * i * 16), cok && xok[u] ? xoff[u] + (uint32_t)(c * KCH * 2) : OOB);
+    }
+#pragma unroll
+    for (int u = 0; u < PCW; ++u) {
+      const int i = wave + u * NWAVE;
+      lds_load16_stream(rq, lds_addr(st + XST + i * 64), cok ? woff[u] + (uint32_t)(c * KCH) : OOB);
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < D - GI; ++j) issue(j);
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) acc[mt][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = r16;                               // slot swizzle of the X rows this lane reads
+  const int wsw = (r16 >> 1) & 7;                   // ... and of its weight row
+  // Chunks are issued in groups of GI (consecutive 128-byte pieces of each weight row arrive
+  // back to back, which keeps DRAM pages open), at the first step of each group, into the GI
+  // stages the previous group used. Before that issue D - 1 - GI chunks follow chunk j; at step r
+  // of a group, D - 1 - r.
+  auto step = [&](int j, auto rc) {
+    constexpr int r = decltype(rc)::value;
+    wait_vmcnt_le<(r == 0 ? D - 1 - GI : D - 1 - r) * PC>();   // this wave's loads of chunk j
+    lds_barrier();                                  // ... everyone's; chunk j-1 is consumed
+    if constexpr (r == 0) {
+#pragma unroll
+      for (int t = 0; t < GI; ++t) issue(j + D - GI + t);
+    }
+    if (j >= nch) return;                           // padding step of the last group
+    const uint4* st = ring[j % D];
+    bf16x8_t xf[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint4* xrow = st + (wm * 16 * MT + mt * 16 + r16) * 16;
+      xf[mt][0] = __builtin_bit_cast(bf16x8_t, xrow[(2 * q4) ^ fr]);
+      xf[mt][1] = __builtin_bit_cast(bf16x8_t, xrow[(2 * q4 + 1) ^ fr]);
+      xf[mt][2] = __builtin_bit_cast(bf16x8_t, xrow[(8 + 2 * q4) ^ fr]);
+      xf[mt][3] = __builtin_bit_cast(bf16x8_t, xrow[(9 + 2 * q4) ^ fr]);
+    }
+    const int e0 = j * 4 + (q4 >> 1);
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) {
+      const int tile = wn * NT + ts;
+      const uint4* wrow = st + XST + (16 * tile + r16) * 8;
+      const uint4 a = wrow[q4 ^ wsw];
+      const uint4 b = wrow[(4 + q4) ^ wsw];
+      const int er = (16 * tile + r16) >> 5;
+      const float sc0 = block_scale(e_lds[er * ESTR + e0]);
+      const float sc1 = block_scale(e_lds[er * ESTR + e0 + 2]);
+      const bf16x8_t w0 = dequant8(a.x, a.y, sc0);
+      const bf16x8_t w1 = dequant8(a.z, a.w, sc0);
+      const bf16x8_t w2 = dequant8(b.x, b.y, sc1);
+      const bf16x8_t w3 = dequant8(b.z, b.w, sc1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4_t c = acc[mt][ts];
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, xf[mt][0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, xf[mt][1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2, xf[mt][2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w3, xf[mt][3], c, 0, 0, 0);
+        acc[mt][ts] = c;
+      }
+    }
+  };
+  for (int j0 = 0; j0 < nch; j0 += GI) {
+    step(j0, std::integral_constant<int, 0>{});
+    if constexpr (GI > 1) step(j0 + 1, std::integral_constant<int, 1 % GI>{});
+    if constexpr (GI > 2) step(j0 + 2, std::integral_constant<int, 2 % GI>{});
+    if constexpr (GI > 3) step(j0 + 3, std::integral_constant<int, 3 % GI>{});
+  }
+  wait_vmcnt_le<0>();                               // no load may still be writing LDS at exit
+
+  // output: this wave's sub-tile, or its fp32 partial for the reduce kernel
+  float* const part = reinterpret_cast<float*>(p.slots);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = m0 + wm * 16 * MT + mt * 16 + r16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) {
+      const size_t o = ((size_t)m * G + g) * N + n0 + wn * 16 * NT + ts * 16 + q4 * 4;
+      const f32x4_t v = acc[mt][ts];
+      if (p.splits > 1) {
+        *reinterpret_cast<f32x4_t*>(part + (size_t)s * M * G * N + o) = v;
+      } else if (p.out_f32) {
+        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + o) = v;
+      } else {
+        const uint2 w2 = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + o) = w2;
+      }
+    }
+  }
+}
+
+// Split-K reduction for the tile kernel: Y = sum over s = 0, 1, ..., S-1 of the partials, added
+// in that order in fp32, then rounded once to the output type. Four outputs per thread.
+__global__ void __launch_bounds__(256)
+reduce_splits_kernel(const float* __restrict__ part, void* __restrict__ y, int64_t n4, int splits,
+                     int out_f32) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4_t* p4 = reinterpret_cast<const f32x4_t*>(part);
+  f32x4_t a = p4[i];
+  for (int s = 1; s < splits; ++s) a += p4[(int64_t)s * n4 + i];
+  if (out_f32) {
+    reinterpret_cast<f32x4_t*>(y)[i] = a;
+  } else {
+    reinterpret_cast<uint2*>(y)[i] = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // configuration table
 // ---------------------------------------------------------------------------------------------
 typedef void (*KernelFn)(KParams);
 
+enum Kind { STAGED = 0, DIRECT = 1, ROWS = 2, TILE = 3 };
+
 struct Config {
-  int MT, NT, NWN, NWK, CW;
+  int MT, NT, NWM, NWN, NWK, CW;         // TILE: CW = chunks in flight
   KernelFn fn;
-  bool direct;                           // gemm_direct_kernel: one pass, at most 16 rows per block
+  int kind;                              // DIRECT and ROWS kernels make one pass over their range
 };
 
-#define CFG(MT, NT, NWN, NWK, CW) {MT, NT, NWN, NWK, CW, gemm_kernel<MT, NT, NWN, NWK, CW>, false}
-#define DCFG(NT, NWN, NWK, CW) {1, NT, NWN, NWK, CW, gemm_direct_kernel<NT, NWN, NWK, CW>, true}
+#define CFG(MT, NT, NWN, NWK, CW) {MT, NT, 1, NWN, NWK, CW, gemm_kernel<MT, NT, NWN, NWK, CW>, STAGED}
+#define DCFG(NT, NWN, NWK, CW) {1, NT, 1, NWN, NWK, CW, gemm_direct_kernel<NT, NWN, NWK, CW>, DIRECT}
+#define RCFG(MT, NT, NWK, CW, D) {MT, NT, 1, 1, NWK, CW, gemm_rows_kernel<MT, NT, NWK, CW, D>, ROWS}
+#define TCFG(MT, NT, NWM, NWN, D, GI) {MT, NT, NWM, NWN, 1, D, gemm_tile_kernel<MT, NT, NWM, NWN, D, GI>, TILE}
 
 const Config kConfigs[] = {
     CFG(1, 1, 4, 1, 4),   // 0  small: 64 rows, one wave per 16 rows, 4 chunks per wave
@@ -628,6 +1132,31 @@ const Config kConfigs[] = {
     DCFG(1, 4, 1, 4),     // 26 direct: 64 rows, 1 wave along K x 4 chunks
     DCFG(1, 1, 8, 2),     // 27 direct: 16 rows, 8 waves along K x 2 chunks
     DCFG(2, 1, 4, 4),     // 28 direct: 32 rows (2 subtiles per wave), 4 waves along K
+    RCFG(1, 1, 8, 4, 4),  // 29 rows: 16 x 16 tile, 8 waves along K x 4 chunks, all in flight
+    RCFG(1, 2, 8, 4, 4),  // 30 rows: 16 x 32 tile
+    RCFG(2, 2, 8, 4, 2),  // 31 rows: 32 x 32 tile, two chunks in flight per wave
+    RCFG(3, 2, 8, 4, 2),  // 32 rows: 48 x 32 tile
+    RCFG(4, 2, 8, 4, 2),  // 33 rows: 64 x 32 tile
+    RCFG(2, 2, 8, 4, 4),  // 34 rows: 32 x 32 tile, all four chunks in flight
+    RCFG(2, 1, 8, 4, 4),  // 35 rows: 32 x 16 tile
+    RCFG(3, 2, 8, 4, 3),  // 36 rows: 48 x 32 tile, three chunks in flight
+    RCFG(2, 2, 4, 8, 2),  // 37 rows: 32 x 32 tile, 4 waves along K x 8 chunks
+    RCFG(3, 1, 8, 4, 4),  // 38 rows: 48 x 16 tile
+    TCFG(1, 2, 1, 4, 7, 4),   // 39 tile: 16 x 128, 4 waves of 16 x 32, 7 stages, issued 4 at a time
+    TCFG(1, 2, 2, 4, 6, 4),   // 40 tile: 32 x 128, 8 waves of 16 x 32, 6 stages
+    TCFG(2, 2, 2, 4, 4, 2),   // 41 tile: 64 x 128, 8 waves of 32 x 32, 4 stages, 2 at a time
+    TCFG(3, 2, 2, 4, 3, 1),   // 42 tile: 96 x 128, 8 waves of 48 x 32, 3 stages
+    TCFG(4, 2, 2, 4, 3, 1),   // 43 tile: 128 x 128, 8 waves of 64 x 32, 3 stages
+    TCFG(4, 4, 2, 2, 3, 1),   // 44 tile: 128 x 128, 4 waves of 64 x 64, 3 stages
+    TCFG(2, 4, 2, 2, 4, 2),   // 45 tile: 64 x 128, 4 waves of 32 x 64, 4 stages
+    TCFG(2, 2, 2, 2, 6, 4),   // 46 tile: 64 x 64, 4 waves of 32 x 32, 6 stages
+    TCFG(3, 2, 2, 2, 4, 2),   // 47 tile: 96 x 64, 4 waves of 48 x 32, 4 stages
+    TCFG(1, 4, 1, 2, 7, 4),   // 48 tile: 16 x 128, 2 waves of 16 x 64, 7 stages
+    TCFG(1, 2, 1, 2, 8, 4),   // 49 tile: 16 x 64, 2 waves of 16 x 32, 8 stages
+    TCFG(2, 2, 1, 4, 6, 4),   // 50 tile: 32 x 128, 4 waves of 32 x 32, 6 stages
+    TCFG(1, 2, 1, 4, 7, 1),   // 51 tile: 16 x 128, 4 waves of 16 x 32, 7 stages, one at a time
+    TCFG(1, 1, 1, 4, 12, 4),  // 52 tile: 16 x 64, 4 waves of 16 x 16, 12 stages
+    TCFG(2, 2, 2, 4, 4, 1),   // 53 tile: 64 x 128, 8 waves of 32 x 32, 4 stages, one at a time
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -644,13 +1173,13 @@ int num_gemm_configs() { return kNumConfigs; }
 int gemm_config_info(int cfg, int* out) {
   if (cfg < 0 || cfg >= kNumConfigs) return BSFP8_EINVAL;
   const Config& c = kConfigs[cfg];
-  out[0] = 16 * c.MT;
+  out[0] = 16 * c.MT * c.NWM;
   out[1] = 16 * c.NT * c.NWN;
-  out[2] = WAVE * c.NWN * c.NWK;
+  out[2] = WAVE * c.NWM * c.NWN * c.NWK;
   out[3] = c.CW;
   out[4] = c.NWN;
   out[5] = c.NWK;
-  out[6] = c.direct ? 1 : 0;
+  out[6] = c.kind;
   return BSFP8_OK;
 }
 
@@ -660,19 +1189,23 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   const Config& c = kConfigs[cfg];
   GemmPlan p{};
   p.cfg = cfg;
-  p.BM = 16 * c.MT;
+  p.BM = 16 * c.MT * c.NWM;
   p.NB = 16 * c.NT * c.NWN;
   if (s.N % p.NB) return BSFP8_ESHAPE;
   p.kchunks = (s.K + KCH - 1) / KCH;
   if (p.kchunks == 0) p.kchunks = 1;
   if (cps <= 0) return BSFP8_EINVAL;
   p.cps = cps < p.kchunks ? cps : p.kchunks;
-  if (c.direct && p.cps > c.NWK * c.CW) return BSFP8_EINVAL;   // one pass only
+  if ((c.kind == DIRECT || c.kind == ROWS) && p.cps > c.NWK * c.CW) return BSFP8_EINVAL;  // one pass
+  if (c.kind == TILE && (p.cps > TILE_MAX_CPS || s.K % KCH != 0)) return BSFP8_EINVAL;
   p.splits = (p.kchunks + p.cps - 1) / p.cps;
   if (p.splits > 64) return BSFP8_EINVAL;
   p.mblocks = (s.M + p.BM - 1) / p.BM;
   p.nblocks = s.N / p.NB;
-  if (p.splits > 1) {
+  if (c.kind == TILE) {
+    // fp32 partials [splits][M][G][N], summed by the reduce kernel
+    if (p.splits > 1) p.ws_bytes = (size_t)p.splits * s.M * s.G * s.N * 4;
+  } else if (p.splits > 1) {
     // one 64-bit slot per output element and tree node
     size_t nodes = 0;
     for (int c2 = p.splits; c2 > 1; c2 = (c2 + 1) >> 1) nodes += (size_t)(c2 >> 1);
@@ -682,38 +1215,41 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   return BSFP8_OK;
 }
 
-// Built-in choice. The plan depends on K only through ceil(K/128), so K and K zero-padded
-// inside the same chunk count get the same plan (and the same fp32 sums). For wide weights
-// (at least 1024 tiles of 16 rows, e.g. an LM-head vocabulary shard) every row count uses one
-// wave per K range and no split: each output's fp32 sum is then the same chain of MFMAs for
-// every M, so a row's result does not depend on how many rows share the call.
+// Built-in choice (measured on MI355X, cold weights, graph replay). The plan depends on K only
+// through ceil(K/128) (and, for the tile kernel, on K being a whole number of chunks), so K and K
+// zero-padded inside the same chunk count get the same plan and the same fp32 sums.
+//  * Wide weights (at least 1024 tiles of 16 rows, e.g. an LM-head vocabulary shard): the tile
+//    kernel, one split, for every row count. Each output's fp32 sum is then the same ascending
+//    chain of chunks and MFMAs whatever the tile, so a row's result does not depend on how many
+//    rows share the call.
+//  * Few rows (at most 32): the one-pass register kernel with X rows in LDS, one 16-row block of X
+//    per workgroup.
+//  * More rows: the register kernel with both operands in registers and 16-48 rows of X per
+//    workgroup (no split while the K range fits one pass of 32 chunks).
 int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
   const int kchunks = (s.K + KCH - 1) / KCH > 0 ? (s.K + KCH - 1) / KCH : 1;
   const bool n64 = (s.N % 64) == 0;
+  const bool tile_ok = s.K % KCH == 0 && kchunks <= TILE_MAX_CPS && s.N % 128 == 0;
   const long long tiles16 = (long long)s.G * s.N / 16;
   int cfg, cps;
   if (tiles16 >= 1024) {
     cps = kchunks;
-    if (path == PATH_SMALL || s.M <= 16) cfg = n64 ? 0 : 3;
+    if (tile_ok) cfg = s.M <= 16 ? 51 : s.M <= 64 ? 53 : 43;
+    else if (path == PATH_SMALL || s.M <= 16) cfg = n64 ? 0 : 3;
     else if (s.M <= 32) cfg = n64 ? 9 : 15;
     else cfg = n64 ? 10 : 16;
-  } else if (path == PATH_SMALL || s.M <= 16) {
-    if (kchunks <= 8) {
-      cfg = 25;                      // short K: register kernel, 32 rows, 2 waves along K, no split
+  } else if (path == PATH_SMALL || s.M <= 32) {
+    if (s.M <= 16 && kchunks <= 8) {
+      cfg = 25;                      // short K: 32 weight rows, 2 waves along K, no split
       cps = kchunks;
     } else {
-      cfg = 20;                      // register kernel, 16 rows, 8 waves along K x 4 chunks
+      cfg = 20;                      // 16 weight rows, 8 waves along K x 4 chunks
       cps = 32;
     }
-  } else if (s.M <= 64) {
-    cfg = 20;                        // register kernel per 16-row block of X, no split
-    cps = 32;
-  } else if (s.M <= 128) {
-    cfg = n64 ? 18 : 3;              // staged, 16 rows of X, 2 waves along K, no split
-    cps = kchunks;
   } else {
-    cfg = n64 ? 12 : 15;             // staged, 32 rows of X, 2 waves along K, no split
-    cps = kchunks;
+    // rows kernel: 16 x 32 (M <= 64), 32 x 32 (<= 128), 48 x 32 (<= 192), 64 x 32 tiles
+    cfg = s.M <= 64 ? 30 : s.M <= 128 ? 31 : s.M <= 192 ? 32 : 33;
+    cps = kchunks < 32 ? kchunks : 32;
   }
   if (split_k > 0) cps = (kchunks + split_k - 1) / split_k;
   return plan_with(s, cfg, cps, plan);
@@ -755,7 +1291,12 @@ int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const 
   const long long nwg = (long long)p.splits * s.G * p.nblocks * p.mblocks;
   if (nwg <= 0 || nwg > 0x7fffffffLL) return BSFP8_ESHAPE;
   k.nwg = (int)nwg;
-  hipLaunchKernelGGL(c.fn, dim3((unsigned)nwg), dim3(WAVE * c.NWN * c.NWK), 0, stream, k);
+  hipLaunchKernelGGL(c.fn, dim3((unsigned)nwg), dim3(WAVE * c.NWM * c.NWN * c.NWK), 0, stream, k);
+  if (c.kind == TILE && p.splits > 1) {
+    const int64_t n4 = (int64_t)s.M * s.G * s.N / 4;
+    hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const float*>(ws), y, n4, p.splits, out_f32);
+  }
   return hip_status(hipGetLastError());
 }
 

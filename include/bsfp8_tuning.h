@@ -22,8 +22,12 @@ BSFP8_API int bsfp8_num_configs(void);
  * workgroup (NB), out[2] = threads per workgroup, out[3] = 128-wide K chunks per wave per pass,
  * out[4] = waves along the weight rows, out[5] = waves along K (each output's fp32 sum is the
  * ascending chain of the chunks one wave owns, so two plans with the same waves along K and the
- * same chunks per split give bitwise the same outputs), out[6] = 1 for a one-pass register
- * kernel (at most 16 rows of X per workgroup; chunks per split <= out[3] * out[5]).
+ * same chunks per split give bitwise the same outputs), out[6] = kernel kind: 0 = staged
+ * (multi-pass, X in LDS), 1 = one-pass with the X rows in LDS (at most 16 rows of X per
+ * workgroup), 2 = one-pass with both operands in registers, 3 = tile kernel (X shared through
+ * LDS; out[3] = chunks in flight; with more than one split each workgroup writes an fp32 partial
+ * tile and a second kernel adds the partials in ascending split order). For kinds 1 and 2 the
+ * chunks per split must be at most out[3] * out[5]; for kind 3 at most 64.
  * Returns BSFP8_EINVAL for an unknown cfg. `out` is host memory of 7 ints. */
 BSFP8_API int bsfp8_config_info(int cfg, int* out);
 

@@ -64,14 +64,19 @@ def test_explicit_split_k(split_k):
 
 def test_every_kernel_configuration():
     """Each compiled configuration, with a few chunks-per-split values, on a shape with several
-    m-blocks (where the tile is smaller than M), a ragged K tail and every N tile width."""
-    G, N, K = 2, 256, 800
+    m-blocks (where the tile is smaller than M), a ragged K tail (the tile kernel takes K in
+    whole 128-wide chunks) and every N tile width."""
+    G, N = 2, 256
     for cfg in range(B.bsfp8_num_configs()):
         info = B.bsfp8_config_info(cfg)
+        K = 768 if info["kind"] == 3 else 800
         M = min(2 * info["BM"] - 3, 256)
         x, q, e = _inputs(400 + cfg, M, G, N, K)
         exact = oracle.gemm_exact_f64(x, G, N, K, q, e)
-        cps_list = (1, 2, 7) if not info["direct"] else sorted({1, 2, info["CW"] * info["NWK"]})
+        if info["kind"] in (1, 2):          # one pass: chunks per split <= CW * NWK
+            cps_list = sorted({1, 2, info["CW"] * info["NWK"]})
+        else:                               # several splits, and one split over all the chunks
+            cps_list = (1, 2, (K + 127) // 128)
         for cps in cps_list:
             print(f"cfg {cfg} {info} cps {cps} M {M}", flush=True)
             y = B.bsfp8_gemm_config(to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e), cfg, cps)
