@@ -876,11 +876,12 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, lds_addr_t l
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory", "m0");
 }
 
+// Wait until at most N of this wave's vector memory loads are outstanding (loads complete in
+// order); no memory access of the kernel moves across it.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_le() {
-  // s_waitcnt with vmcnt = N (6 bits split over [3:0] and [15:14]), expcnt and lgkmcnt at max
   static_assert(N >= 0 && N <= 63, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <int MT, int NT, int NWM, int NWN, int D, int GI>
@@ -1067,6 +1068,199 @@ gemm_tile_kernel(KParams p) {
   }
 }
 
+// Decode kernel (at most XR rows of X per workgroup, one pass over its K range; K a multiple of
+// 128). The weight is the A operand as everywhere; what differs is how the bytes arrive: all of
+// them stream into LDS with the buffer loads' LDS mode, so the loads are issued at once and cost
+// no VGPRs:
+//  * the exponent words of the workgroup's range (one 4-byte word = one chunk of a block row);
+//  * the workgroup's X rows, dense, one granule of padding per row (fragment reads of 16 lanes
+//    then hit 16 distinct bank groups);
+//  * each wave's weight chunks, eight lanes per weight row: 128 contiguous bytes per row and
+//    load, which HBM streams far better than the MFMA order (64 bytes per row), stored row-major
+//    with granule g of row R at slot g ^ (R/2 % 8) (conflict-free fragment reads).
+// Each wave counts its own loads: it waits for its exponent and X loads and meets the others at
+// a barrier (X is shared), then computes each of its chunks as soon as that chunk's weight pieces
+// have landed. Out-of-range loads are issued too (so that every wave's count is fixed), but what
+// they leave in LDS is never used: chunks past the range are skipped, and X rows at or beyond M
+// feed only output columns that are not stored. Waves along K are summed through LDS in ascending order, as in the other one-pass
+// kernels, so an output's fp32 sum is the same chain of chunks as in gemm_direct_kernel with the
+// same NWK and chunks per split.
+template <int NT, int NWN, int NWK, int CW, int XR>
+__global__ void __launch_bounds__(WAVE * NWN * NWK)
+gemm_decode_kernel(KParams p) {
+  constexpr int NWAVE = NWN * NWK;
+  constexpr int NB = 16 * NT * NWN;
+  constexpr int PCH = NWK * CW;                     // chunks of the workgroup
+  constexpr int ROWG = PCH * 16 + 1;                // granules per LDS X row (one of padding)
+  constexpr int XI = XR * PCH / 4;                  // X loads: 1 KB = 4 chunks of one row
+  constexpr int XPW = XI / NWAVE;
+  constexpr int WPW = CW * NT * 2;                  // weight loads per wave
+  constexpr int EROWS = NB >= 32 ? NB / 32 : 1;
+  static_assert(XI % NWAVE == 0 && XPW >= 1, "every wave issues the same X loads");
+  static_assert(PCH <= 64 && EROWS <= NWAVE, "one exponent load per block row");
+  static_assert((XR & (XR - 1)) == 0 && XR <= 16, "X rows: a power of two up to 16");
+  static_assert(XPW + WPW + 1 <= 63, "vector memory counter range");
+  __shared__ uint4 x_lds[XR * ROWG];
+  __shared__ uint4 w_lds[NWAVE * CW * NT * 128];
+  __shared__ uint32_t e_lds[EROWS * 64];
+  __shared__ f32x4_t red[NWK > 1 ? (NWK - 1) * NWN * NT * WAVE : 1];
+
+  prefetch_args(p);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % NWN, wk = wave / NWN;
+  const int q4 = lane >> 4, r16 = lane & 15;
+
+  int t = xcd_logical(blockIdx.x, p.nwg);
+  const int mb = t % p.mblocks;
+  t /= p.mblocks;
+  const int nb = t % p.nblocks;
+  t /= p.nblocks;
+  const int g = t % p.G;
+  const int s = t / p.G;
+
+  const int K = p.K, M = p.M, N = p.N, G = p.G;
+  const int n0 = nb * NB, m0 = mb * XR;
+  const int c_begin = s * p.cps;
+  const int c_end = min(c_begin + p.cps, p.kchunks);
+  const int KB = K / 32;
+
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, (int)p.x_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.q, 0, (int)p.q_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((void*)p.e, 0, (int)p.e_bytes, RSRC_WORD3);
+
+  // (1) exponent words: wave er loads block row er, lane l the word of chunk c_begin + l
+  if (wave < EROWS) {
+    const int c = c_begin + lane;
+    const uint32_t off = (uint32_t)((g * (N / 32) + n0 / 32 + wave) * KB + c * 4);
+    lds_load4(re, lds_addr(e_lds + wave * 64), c < c_end ? off : OOB);
+  }
+  // (2) X rows m0 .. m0+XR-1 over the workgroup's chunks: load i covers row i / (PCH/4), granules
+  //     64*(i % (PCH/4)) .. +63 of the row's range (rows at or beyond M read as zero)
+#pragma unroll
+  for (int u = 0; u < XPW; ++u) {
+    const int i = wave + u * NWAVE;
+    const int row = i / (PCH / 4), pc = i % (PCH / 4);
+    const int m = m0 + row;
+    const int k = c_begin * KCH + (pc * 64 + lane) * 8;
+    const uint32_t off = (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K + k) * 2);
+    lds_load16(rx, lds_addr(x_lds + row * ROWG + pc * 64), m < M && k < c_end * KCH ? off : OOB);
+  }
+  // (3) this wave's weight chunks: load (j, ts, v) covers rows 8v .. 8v+7 of its 16-row tile ts,
+  //     the lane fills row R = 8v + lane/8, slot lane%8 with granule (lane%8) ^ (R/2 % 8)
+  uint4* const wbase = w_lds + wave * CW * NT * 128;
+  {
+    const int R0 = lane >> 3;
+    const uint32_t qrow = (uint32_t)(g * N + n0 + wn * 16 * NT + R0) * (uint32_t)K;
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      const int c = c_begin + wk + j * NWK;
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const int R = 8 * v + R0;
+          const int gsrc = (lane & 7) ^ ((R >> 1) & 7);
+          const uint32_t off = qrow + (uint32_t)((ts * 16 + 8 * v) * K + c * KCH + gsrc * 16);
+          lds_load16_stream(rq, lds_addr(wbase + (j * NT + ts) * 128 + v * 64), c < c_end ? off : OOB);
+        }
+    }
+  }
+  wait_vmcnt_le<WPW>();                             // this wave's exponent and X loads
+  lds_barrier();                                    // ... everyone's
+
+  // (4) dequant + MFMA, chunk by chunk in ascending order, each once its own weights are in
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int ts = 0; ts < NT; ++ts) acc[ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint4* xrow = x_lds + (r16 & (XR - 1)) * ROWG;   // rows beyond XR feed unused columns
+  const uint8_t* eb = reinterpret_cast<const uint8_t*>(e_lds);
+  const int wsw = (r16 >> 1) & 7;
+  auto chunk = [&](int j) {
+    const int cl = wk + j * NWK;                    // chunk index inside the workgroup
+    // (a chunk past the range was not loaded: its LDS holds nothing defined)
+    if (c_begin + cl >= c_end) return;
+    const bf16x8_t x0 = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 2 * q4]);
+    const bf16x8_t x1 = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 2 * q4 + 1]);
+    const bf16x8_t x2 = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 8 + 2 * q4]);
+    const bf16x8_t x3 = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 9 + 2 * q4]);
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) {
+      const int er = (n0 + wn * 16 * NT + ts * 16 + r16) / 32 - n0 / 32;
+      const float sc0 = block_scale(eb[er * 256 + cl * 4 + (q4 >> 1)]);
+      const float sc1 = block_scale(eb[er * 256 + cl * 4 + 2 + (q4 >> 1)]);
+      const uint4* wt = wbase + (j * NT + ts) * 128 + r16 * 8;
+      const uint4 a = wt[q4 ^ wsw], b = wt[(4 + q4) ^ wsw];
+      f32x4_t c = acc[ts];
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(a.x, a.y, sc0), x0, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(a.z, a.w, sc0), x1, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(b.x, b.y, sc1), x2, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(b.z, b.w, sc1), x3, c, 0, 0, 0);
+      acc[ts] = c;
+    }
+  };
+  wait_vmcnt_le<(CW - 1) * NT * 2>();
+  chunk(0);
+  if constexpr (CW > 1) { wait_vmcnt_le<(CW - 2 >= 0 ? CW - 2 : 0) * NT * 2>(); chunk(1); }
+  if constexpr (CW > 2) { wait_vmcnt_le<(CW - 3 >= 0 ? CW - 3 : 0) * NT * 2>(); chunk(2); }
+  if constexpr (CW > 3) { wait_vmcnt_le<(CW - 4 >= 0 ? CW - 4 : 0) * NT * 2>(); chunk(3); }
+  if constexpr (CW > 4) { wait_vmcnt_le<(CW - 5 >= 0 ? CW - 5 : 0) * NT * 2>(); chunk(4); }
+  if constexpr (CW > 5) { wait_vmcnt_le<(CW - 6 >= 0 ? CW - 6 : 0) * NT * 2>(); chunk(5); }
+  if constexpr (CW > 6) { wait_vmcnt_le<(CW - 7 >= 0 ? CW - 7 : 0) * NT * 2>(); chunk(6); }
+  if constexpr (CW > 7) { wait_vmcnt_le<(CW - 8 >= 0 ? CW - 8 : 0) * NT * 2>(); chunk(7); }
+  static_assert(CW <= 8, "chunks per wave");
+
+  // (5) waves along K: ascending-order sum through LDS
+  if constexpr (NWK > 1) {
+    if (wk > 0) {
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) red[(((wk - 1) * NWN + wn) * NT + ts) * WAVE + lane] = acc[ts];
+    }
+    __syncthreads();
+    if (wk != 0) return;
+#pragma unroll
+    for (int w = 1; w < NWK; ++w)
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) acc[ts] += red[(((w - 1) * NWN + wn) * NT + ts) * WAVE + lane];
+  }
+  // (6) output
+  const int m = m0 + r16;
+  const bool mrow = r16 < XR && m < M;
+  if (p.splits == 1) {
+    if (mrow) {
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) {
+        const int n = n0 + wn * 16 * NT + ts * 16 + q4 * 4;
+        const size_t o = ((size_t)m * G + g) * N + n;
+        const f32x4_t v = acc[ts];
+        if (p.out_f32) {
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + o) = v;
+        } else {
+          const uint2 w2 = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + o) = w2;
+        }
+      }
+    }
+    return;
+  }
+  constexpr int NV = NT * 4;
+  float v[NV];
+  size_t off[NV];
+  bool live[NV];
+#pragma unroll
+  for (int ts = 0; ts < NT; ++ts)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[ts * 4 + r] = acc[ts][r];
+      off[ts * 4 + r] = ((size_t)m * G + g) * N + n0 + wn * 16 * NT + ts * 16 + q4 * 4 + r;
+      live[ts * 4 + r] = mrow;
+    }
+  combine_splits<NV>(p, s, v, off, live);
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (live[i]) store_out(p, off[i], v[i]);
+}
+
 // Split-K reduction for the tile kernel: Y = sum over s = 0, 1, ..., S-1 of the partials, added
 // in that order in fp32, then rounded once to the output type. Four outputs per thread.
 __global__ void __launch_bounds__(256)
@@ -1089,17 +1283,18 @@ reduce_splits_kernel(const float* __restrict__ part, void* __restrict__ y, int64
 // ---------------------------------------------------------------------------------------------
 typedef void (*KernelFn)(KParams);
 
-enum Kind { STAGED = 0, DIRECT = 1, ROWS = 2, TILE = 3 };
+enum Kind { STAGED = 0, DIRECT = 1, ROWS = 2, TILE = 3, DECODE = 4 };
 
 struct Config {
-  int MT, NT, NWM, NWN, NWK, CW;         // TILE: CW = chunks in flight
+  int MT, NT, NWM, NWN, NWK, CW;         // TILE: CW = chunks in flight; DECODE: MT*16 = X rows
   KernelFn fn;
-  int kind;                              // DIRECT and ROWS kernels make one pass over their range
+  int kind;                              // DIRECT, ROWS and DECODE kernels make one pass
 };
 
 #define CFG(MT, NT, NWN, NWK, CW) {MT, NT, 1, NWN, NWK, CW, gemm_kernel<MT, NT, NWN, NWK, CW>, STAGED}
 #define DCFG(NT, NWN, NWK, CW) {1, NT, 1, NWN, NWK, CW, gemm_direct_kernel<NT, NWN, NWK, CW>, DIRECT}
 #define RCFG(MT, NT, NWK, CW, D) {MT, NT, 1, 1, NWK, CW, gemm_rows_kernel<MT, NT, NWK, CW, D>, ROWS}
+#define ECFG(NT, NWN, NWK, CW, XR) {XR, NT, 1, NWN, NWK, CW, gemm_decode_kernel<NT, NWN, NWK, CW, XR>, DECODE}
 #define TCFG(MT, NT, NWM, NWN, D, GI) {MT, NT, NWM, NWN, 1, D, gemm_tile_kernel<MT, NT, NWM, NWN, D, GI>, TILE}
 
 const Config kConfigs[] = {
@@ -1157,6 +1352,14 @@ const Config kConfigs[] = {
     TCFG(1, 2, 1, 4, 7, 1),   // 51 tile: 16 x 128, 4 waves of 16 x 32, 7 stages, one at a time
     TCFG(1, 1, 1, 4, 12, 4),  // 52 tile: 16 x 64, 4 waves of 16 x 16, 12 stages
     TCFG(2, 2, 2, 4, 4, 1),   // 53 tile: 64 x 128, 8 waves of 32 x 32, 4 stages, one at a time
+    ECFG(1, 1, 8, 4, 8),      // 54 decode: 8 rows of X x 16 weight rows, 8 waves along K x 4 chunks
+    ECFG(1, 1, 4, 8, 8),      // 55 decode: 4 waves along K x 8 chunks
+    ECFG(1, 2, 4, 4, 8),      // 56 decode: 32 weight rows, 4 waves along K x 4 chunks
+    ECFG(1, 1, 4, 4, 8),      // 57 decode: 16 weight rows, 4 waves along K x 4 chunks
+    ECFG(1, 2, 2, 4, 8),      // 58 decode: 32 weight rows, 2 waves along K x 4 chunks
+    ECFG(1, 1, 4, 2, 8),      // 59 decode: 16 weight rows, 4 waves along K x 2 chunks
+    ECFG(1, 1, 8, 2, 8),      // 60 decode: 16 weight rows, 8 waves along K x 2 chunks
+    ECFG(1, 1, 4, 4, 16),     // 61 decode: 16 rows of X, 4 waves along K x 4 chunks
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1173,7 +1376,7 @@ int num_gemm_configs() { return kNumConfigs; }
 int gemm_config_info(int cfg, int* out) {
   if (cfg < 0 || cfg >= kNumConfigs) return BSFP8_EINVAL;
   const Config& c = kConfigs[cfg];
-  out[0] = 16 * c.MT * c.NWM;
+  out[0] = c.kind == DECODE ? c.MT : 16 * c.MT * c.NWM;
   out[1] = 16 * c.NT * c.NWN;
   out[2] = WAVE * c.NWM * c.NWN * c.NWK;
   out[3] = c.CW;
@@ -1189,14 +1392,16 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   const Config& c = kConfigs[cfg];
   GemmPlan p{};
   p.cfg = cfg;
-  p.BM = 16 * c.MT * c.NWM;
+  p.BM = c.kind == DECODE ? c.MT : 16 * c.MT * c.NWM;
   p.NB = 16 * c.NT * c.NWN;
   if (s.N % p.NB) return BSFP8_ESHAPE;
   p.kchunks = (s.K + KCH - 1) / KCH;
   if (p.kchunks == 0) p.kchunks = 1;
   if (cps <= 0) return BSFP8_EINVAL;
   p.cps = cps < p.kchunks ? cps : p.kchunks;
-  if ((c.kind == DIRECT || c.kind == ROWS) && p.cps > c.NWK * c.CW) return BSFP8_EINVAL;  // one pass
+  if ((c.kind == DIRECT || c.kind == ROWS || c.kind == DECODE) && p.cps > c.NWK * c.CW)
+    return BSFP8_EINVAL;                                        // one pass
+  if (c.kind == DECODE && s.K % KCH != 0) return BSFP8_EINVAL;  // whole exponent words per chunk
   if (c.kind == TILE && (p.cps > TILE_MAX_CPS || s.K % KCH != 0)) return BSFP8_EINVAL;
   p.splits = (p.kchunks + p.cps - 1) / p.cps;
   if (p.splits > 64) return BSFP8_EINVAL;
@@ -1216,12 +1421,17 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
 }
 
 // Built-in choice (measured on MI355X, cold weights, graph replay). The plan depends on K only
-// through ceil(K/128) (and, for the tile kernel, on K being a whole number of chunks), so K and K
-// zero-padded inside the same chunk count get the same plan and the same fp32 sums.
+// through ceil(K/128) and on whether K is a whole number of chunks; where that changes the kernel,
+// the fp32 chain of every output stays the same, so K and K zero-padded inside the same chunk
+// count give the same sums.
 //  * Wide weights (at least 1024 tiles of 16 rows, e.g. an LM-head vocabulary shard): the tile
 //    kernel, one split, for every row count. Each output's fp32 sum is then the same ascending
 //    chain of chunks and MFMAs whatever the tile, so a row's result does not depend on how many
 //    rows share the call.
+//  * Decode rows (at most 8): the decode kernel (everything streamed into LDS) when K is whole
+//    128-wide chunks; otherwise the one-pass kernel with X rows in LDS and the same waves and
+//    chunks, whose fp32 chains are the same, so K zero-padded to whole chunks (576 -> 640) gives
+//    bitwise the same Y on the faster kernel.
 //  * Few rows (at most 32): the one-pass register kernel with X rows in LDS, one 16-row block of X
 //    per workgroup.
 //  * More rows: the register kernel with both operands in registers and 16-48 rows of X per
@@ -1238,6 +1448,17 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
     else if (path == PATH_SMALL || s.M <= 16) cfg = n64 ? 0 : 3;
     else if (s.M <= 32) cfg = n64 ? 9 : 15;
     else cfg = n64 ? 10 : 16;
+  } else if (s.M <= 8) {
+    // decode kernel when K is whole chunks, else the one-pass kernel with the same waves and
+    // chunks (the same fp32 chains: K zero-padded to whole chunks gives bitwise the same Y)
+    const bool whole = s.K % KCH == 0;
+    if (kchunks <= 8) {
+      cfg = whole ? 59 : 21;         // 16 weight rows, 4 waves along K x 2 chunks
+      cps = kchunks;
+    } else {
+      cfg = whole ? 54 : 20;         // 16 weight rows, 8 waves along K x 4 chunks
+      cps = kchunks < 32 ? kchunks : 32;
+    }
   } else if (path == PATH_SMALL || s.M <= 32) {
     if (s.M <= 16 && kchunks <= 8) {
       cfg = 25;                      // short K: 32 weight rows, 2 waves along K, no split

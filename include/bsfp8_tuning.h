@@ -26,8 +26,10 @@ BSFP8_API int bsfp8_num_configs(void);
  * (multi-pass, X in LDS), 1 = one-pass with the X rows in LDS (at most 16 rows of X per
  * workgroup), 2 = one-pass with both operands in registers, 3 = tile kernel (X shared through
  * LDS; out[3] = chunks in flight; with more than one split each workgroup writes an fp32 partial
- * tile and a second kernel adds the partials in ascending split order). For kinds 1 and 2 the
- * chunks per split must be at most out[3] * out[5]; for kind 3 at most 64.
+ * tile and a second kernel adds the partials in ascending split order), 4 = one-pass decode
+ * kernel (X, exponents and weights streamed into LDS; out[0] rows of X per workgroup). For kinds
+ * 1, 2 and 4 the chunks per split must be at most out[3] * out[5]; for kind 3 at most 64. Kinds 3
+ * and 4 take K in whole 128-wide chunks (K % 128 == 0).
  * Returns BSFP8_EINVAL for an unknown cfg. `out` is host memory of 7 ints. */
 BSFP8_API int bsfp8_config_info(int cfg, int* out);
 

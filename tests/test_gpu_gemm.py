@@ -64,16 +64,16 @@ def test_explicit_split_k(split_k):
 
 def test_every_kernel_configuration():
     """Each compiled configuration, with a few chunks-per-split values, on a shape with several
-    m-blocks (where the tile is smaller than M), a ragged K tail (the tile kernel takes K in
-    whole 128-wide chunks) and every N tile width."""
+    m-blocks (where the tile is smaller than M), a ragged K tail (the tile and decode kernels
+    take K in whole 128-wide chunks) and every N tile width."""
     G, N = 2, 256
     for cfg in range(B.bsfp8_num_configs()):
         info = B.bsfp8_config_info(cfg)
-        K = 768 if info["kind"] == 3 else 800
+        K = 768 if info["kind"] in (3, 4) else 800
         M = min(2 * info["BM"] - 3, 256)
         x, q, e = _inputs(400 + cfg, M, G, N, K)
         exact = oracle.gemm_exact_f64(x, G, N, K, q, e)
-        if info["kind"] in (1, 2):          # one pass: chunks per split <= CW * NWK
+        if info["kind"] in (1, 2, 4):       # one pass: chunks per split <= CW * NWK
             cps_list = sorted({1, 2, info["CW"] * info["NWK"]})
         else:                               # several splits, and one split over all the chunks
             cps_list = (1, 2, (K + 127) // 128)
