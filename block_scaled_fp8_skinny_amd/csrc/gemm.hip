@@ -1080,11 +1080,11 @@ gemm_tile_kernel(KParams p) {
 //    with granule g of row R at slot g ^ (R/2 % 8) (conflict-free fragment reads).
 // Each wave counts its own loads: it waits for its exponent and X loads and meets the others at
 // a barrier (X is shared), then computes each of its chunks as soon as that chunk's weight pieces
-// have landed. Out-of-range loads are issued too (so that every wave's count is fixed), but what
-// they leave in LDS is never used: chunks past the range are skipped, and X rows at or beyond M
-// feed only output columns that are not stored. Waves along K are summed through LDS in ascending order, as in the other one-pass
-// kernels, so an output's fp32 sum is the same chain of chunks as in gemm_direct_kernel with the
-// same NWK and chunks per split.
+// have landed. Out-of-range weight loads are issued too (so that every wave's count of them is
+// fixed), but what they leave in LDS is never used: chunks past the range are skipped, and X rows
+// at or beyond M (not loaded at all) feed only output columns that are not stored. Waves along K
+// are summed through LDS in ascending order, as in the other one-pass kernels, so an output's fp32
+// sum is the same chain of chunks as in gemm_direct_kernel with the same NWK and chunks per split.
 template <int NT, int NWN, int NWK, int CW, int XR>
 __global__ void __launch_bounds__(WAVE * NWN * NWK)
 gemm_decode_kernel(KParams p) {
@@ -1136,7 +1136,8 @@ gemm_decode_kernel(KParams p) {
     lds_load4(re, lds_addr(e_lds + wave * 64), c < c_end ? off : OOB);
   }
   // (2) X rows m0 .. m0+XR-1 over the workgroup's chunks: load i covers row i / (PCH/4), granules
-  //     64*(i % (PCH/4)) .. +63 of the row's range (rows at or beyond M read as zero)
+  //     64*(i % (PCH/4)) .. +63 of the row's range. Rows at or beyond M are not loaded (the waits
+  //     below count only the weight loads issued after these, so the number may vary).
 #pragma unroll
   for (int u = 0; u < XPW; ++u) {
     const int i = wave + u * NWAVE;
@@ -1144,7 +1145,7 @@ gemm_decode_kernel(KParams p) {
     const int m = m0 + row;
     const int k = c_begin * KCH + (pc * 64 + lane) * 8;
     const uint32_t off = (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K + k) * 2);
-    lds_load16(rx, lds_addr(x_lds + row * ROWG + pc * 64), m < M && k < c_end * KCH ? off : OOB);
+    if (m < M) lds_load16(rx, lds_addr(x_lds + row * ROWG + pc * 64), k < c_end * KCH ? off : OOB);
   }
   // (3) this wave's weight chunks: load (j, ts, v) covers rows 8v .. 8v+7 of its 16-row tile ts,
   //     the lane fills row R = 8v + lane/8, slot lane%8 with granule (lane%8) ^ (R/2 % 8)
@@ -1428,7 +1429,8 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
 //    kernel, one split, for every row count. Each output's fp32 sum is then the same ascending
 //    chain of chunks and MFMAs whatever the tile, so a row's result does not depend on how many
 //    rows share the call.
-//  * Decode rows (at most 8): the decode kernel (everything streamed into LDS) when K is whole
+//  * Decode rows (at most 8, or 16 with a long K): the decode kernel (everything streamed into
+//    LDS, 8 rows of X per workgroup) when K is whole
 //    128-wide chunks; otherwise the one-pass kernel with X rows in LDS and the same waves and
 //    chunks, whose fp32 chains are the same, so K zero-padded to whole chunks (576 -> 640) gives
 //    bitwise the same Y on the faster kernel.
@@ -1448,9 +1450,10 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
     else if (path == PATH_SMALL || s.M <= 16) cfg = n64 ? 0 : 3;
     else if (s.M <= 32) cfg = n64 ? 9 : 15;
     else cfg = n64 ? 10 : 16;
-  } else if (s.M <= 8) {
-    // decode kernel when K is whole chunks, else the one-pass kernel with the same waves and
-    // chunks (the same fp32 chains: K zero-padded to whole chunks gives bitwise the same Y)
+  } else if (s.M <= 8 || (s.M <= 16 && kchunks > 8)) {
+    // decode kernel (8 rows of X per workgroup) when K is whole chunks, else the one-pass kernel
+    // with the same waves and chunks (the same fp32 chains: K zero-padded to whole chunks gives
+    // bitwise the same Y)
     const bool whole = s.K % KCH == 0;
     if (kchunks <= 8) {
       cfg = whole ? 59 : 21;         // 16 weight rows, 4 waves along K x 2 chunks
