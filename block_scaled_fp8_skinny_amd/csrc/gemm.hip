@@ -591,13 +591,13 @@ gemm_direct_kernel(KParams p) {
 // share nothing (each owns the chunks wk, wk + NWK, ...), so there is no LDS limit on the tile's
 // K extent; a ring of D chunk buffers per wave keeps D chunks of loads in flight (chunk j + D is
 // issued as soon as chunk j has been consumed).
-//  * X is read coalesced: each group of four lanes reads 64 contiguous bytes of one row (the MFMA
-//    layout would have every four lanes on four rows, i.e. four cache lines per quad). Each wave
+//  * X is read coalesced, eight lanes per row (128 contiguous bytes per row and load). Each wave
 //    then turns its chunk into the MFMA layout through a private LDS tile: 16 rows x 256 bytes
-//    per 16-row block, granule g of row r stored at slot g ^ f(r) with f(r) = 4*(r%4) + r/4, so
-//    the coalesced writes (4 rows x 4 granules per 16 lanes) and the fragment reads (16 rows x
-//    one granule) both touch 16 distinct bank groups.
-//  * The weight pieces go straight into the MFMA registers, as in the other kernels.
+//    per 16-row block, granule g of row r at slot g ^ r, which the fragment reads (16 rows x one
+//    granule) cross without bank conflicts.
+//  * The weights are read eight lanes per row (128 contiguous bytes per row and load, which HBM
+//    streams far better than the MFMA order's 64) and reordered through a second per-wave LDS
+//    tile, row-major with granule g of row R at slot g ^ (R/2 % 8).
 //  * The NWK partial tiles meet in LDS (each wave writes its own X area, so no barrier is needed
 //    before) and each wave sums, in ascending wave order, and stores its share of the tiles.
 template <int MT, int NT, int NWK, int CW, int D>
@@ -617,12 +617,13 @@ gemm_rows_kernel(KParams p) {
   static_assert(TILES * WAVE <= XG, "a wave's partial tiles fit in its X area");
   __shared__ uint8_t e_lds[EROWS * ECOLS];
   __shared__ uint4 xs[NWK * XG];
+  __shared__ uint4 wsm[NWK * NT * 128];            // each wave's weight chunk, 16 rows x 8 granules per tile
 
   prefetch_args(p);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wk = tid >> 6;
   const int q4 = lane >> 4, r16 = lane & 15;
-  const int cr = lane >> 2, cp = lane & 3;          // coalesced X: row cr, granule cp of 4
+  const int cr = lane >> 3, cp = lane & 7;          // coalesced X: row cr (+8), granule cp (+8)
 
   int t = xcd_logical(blockIdx.x, p.nwg);
   const int mb = t % p.mblocks;
@@ -652,20 +653,24 @@ gemm_rows_kernel(KParams p) {
     ev = __builtin_amdgcn_raw_buffer_load_b8(re, (int)(ok ? off : OOB), 0, 0);
   }
 
-  // X rows m0 + 16*mt + cr of this lane's coalesced loads (zero beyond M)
-  uint32_t xrow[MT];
-  bool xok[MT];
+  // X rows m0 + 16*mt + 8*hr + cr of this lane's coalesced loads (zero beyond M)
+  uint32_t xrow[MT][2];
+  bool xok[MT][2];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = m0 + mt * 16 + cr;
-    xok[mt] = m < M;
-    xrow[mt] = xok[mt] ? (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K) * 2) : 0u;
-  }
-  const uint32_t qrow = (uint32_t)(g * N + n0 + r16) * (uint32_t)K;   // weight row n0 + r16 (+16*ts)
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int hr = 0; hr < 2; ++hr) {
+      const int m = m0 + mt * 16 + 8 * hr + cr;
+      xok[mt][hr] = m < M;
+      xrow[mt][hr] = xok[mt][hr] ? (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K) * 2) : 0u;
+    }
+  // weights, eight lanes per row: load v of tile ts covers rows 8v .. 8v+7, the lane takes row
+  // 8v + lane/8, bytes 16*(lane%8) of the chunk
+  const uint32_t qrow8 = (uint32_t)(g * N + n0 + (lane >> 3)) * (uint32_t)K;
 
-  // Chunk j of this wave is chunk c = c_begin + wk + j*NWK. X load i covers k in
-  // [c*128 + 32i, +32) of 16 rows; weight piece h covers k in c*128 + 64h + 16*q4 + [0, 16) of the
-  // lane's weight row. Out-of-range pieces read as zero.
+  // Chunk j of this wave is chunk c = c_begin + wk + j*NWK. X load i covers rows 8*(i%2) .. +7 of
+  // a 16-row block, k in [c*128 + 64*(i/2), +64) (eight lanes per row, 128 bytes); weight load v
+  // covers the chunk's 128 bytes of 8 weight rows. Out-of-range pieces read as zero.
   struct Buf {
     uint4 w[NT][2];
     uint4 x[MT][4];
@@ -675,18 +680,17 @@ gemm_rows_kernel(KParams p) {
     const bool cok = c < c_end;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int k = c * KCH + 32 * i + 8 * cp;
+      const int k = c * KCH + 64 * (i >> 1) + 8 * cp;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        b.x[mt][i] = load16(rx, cok && k < K && xok[mt] ? xrow[mt] + (uint32_t)k * 2 : OOB);
+        b.x[mt][i] = load16(rx, cok && k < K && xok[mt][i & 1] ? xrow[mt][i & 1] + (uint32_t)k * 2 : OOB);
     }
+    const int kw = c * KCH + (lane & 7) * 16;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = c * KCH + h * 64 + q4 * 16;
+    for (int v = 0; v < 2; ++v)
 #pragma unroll
       for (int ts = 0; ts < NT; ++ts)
-        b.w[ts][h] = load16_stream(rq, cok && k < K ? qrow + (uint32_t)(ts * 16 * K + k) : OOB);
-    }
+        b.w[ts][v] = load16_stream(rq, cok && kw < K ? qrow8 + (uint32_t)((ts * 16 + 8 * v) * K + kw) : OOB);
   };
 
   f32x4_t acc[MT][NT];
@@ -695,9 +699,11 @@ gemm_rows_kernel(KParams p) {
 #pragma unroll
     for (int ts = 0; ts < NT; ++ts) acc[mt][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4* const xw = xs + wk * XG;                   // this wave's X area
-  const int fw = ((cr & 3) << 2) | (cr >> 2);       // slot swizzle of the row this lane writes
-  const int fr = ((r16 & 3) << 2) | (r16 >> 2);     // ... and of the row it reads
+  uint4* const xw = xs + wk * XG;                   // this wave's X area: row r, granule g at
+  const int fr = r16;                               //   r*16 + (g ^ r), read by row r16
+  uint4* const ww = wsm + wk * NT * 128;            // this wave's weight area: row R, granule g
+  const int wr8 = lane >> 3;                        //   at R*8 + (g ^ (R/2 % 8))
+  const int wsw = (r16 >> 1) & 7;
   auto compute = [&](int j, const Buf& b) {
     const int cl = wk + j * NWK;                    // chunk index inside the workgroup
     // X chunk -> LDS (row-major, swizzled) -> MFMA fragments: lane (r16, q4) takes the k values
@@ -705,7 +711,10 @@ gemm_rows_kernel(KParams p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xw[mt * 256 + cr * 16 + ((4 * i + cp) ^ fw)] = b.x[mt][i];
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * (i & 1) + cr;
+        xw[mt * 256 + row * 16 + ((8 * (i >> 1) + cp) ^ row)] = b.x[mt][i];
+      }
     bf16x8_t xf[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -714,15 +723,26 @@ gemm_rows_kernel(KParams p) {
         const int gr = 8 * (f >> 1) + 2 * q4 + (f & 1);
         xf[mt][f] = __builtin_bit_cast(bf16x8_t, xw[mt * 256 + r16 * 16 + (gr ^ fr)]);
       }
+    // weights -> LDS (row-major, swizzled) -> the MFMA order: lane (r16, q4) takes granules q4
+    // and 4 + q4 of row r16
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const int R = 8 * v + wr8;
+        ww[(ts * 16 + R) * 8 + ((lane & 7) ^ ((R >> 1) & 7))] = b.w[ts][v];
+      }
 #pragma unroll
     for (int ts = 0; ts < NT; ++ts) {
       const int er = (n0 + ts * 16 + r16) / 32 - n0 / 32;
       const float sc0 = block_scale(e_lds[er * ECOLS + cl * 4 + (q4 >> 1)]);
       const float sc1 = block_scale(e_lds[er * ECOLS + cl * 4 + 2 + (q4 >> 1)]);
-      const bf16x8_t w0 = dequant8(b.w[ts][0].x, b.w[ts][0].y, sc0);
-      const bf16x8_t w1 = dequant8(b.w[ts][0].z, b.w[ts][0].w, sc0);
-      const bf16x8_t w2 = dequant8(b.w[ts][1].x, b.w[ts][1].y, sc1);
-      const bf16x8_t w3 = dequant8(b.w[ts][1].z, b.w[ts][1].w, sc1);
+      const uint4 wa = ww[(ts * 16 + r16) * 8 + (q4 ^ wsw)];
+      const uint4 wb = ww[(ts * 16 + r16) * 8 + ((4 + q4) ^ wsw)];
+      const bf16x8_t w0 = dequant8(wa.x, wa.y, sc0);
+      const bf16x8_t w1 = dequant8(wa.z, wa.w, sc0);
+      const bf16x8_t w2 = dequant8(wb.x, wb.y, sc1);
+      const bf16x8_t w3 = dequant8(wb.z, wb.w, sc1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x4_t c = acc[mt][ts];
@@ -1332,7 +1352,7 @@ const Config kConfigs[] = {
     RCFG(1, 2, 8, 4, 4),  // 30 rows: 16 x 32 tile
     RCFG(2, 2, 8, 4, 2),  // 31 rows: 32 x 32 tile, two chunks in flight per wave
     RCFG(3, 2, 8, 4, 2),  // 32 rows: 48 x 32 tile
-    RCFG(4, 2, 8, 4, 2),  // 33 rows: 64 x 32 tile
+    RCFG(4, 2, 4, 8, 2),  // 33 rows: 64 x 32 tile, 4 waves along K x 8 chunks
     RCFG(2, 2, 8, 4, 4),  // 34 rows: 32 x 32 tile, all four chunks in flight
     RCFG(2, 1, 8, 4, 4),  // 35 rows: 32 x 16 tile
     RCFG(3, 2, 8, 4, 3),  // 36 rows: 48 x 32 tile, three chunks in flight
@@ -1361,6 +1381,8 @@ const Config kConfigs[] = {
     ECFG(1, 1, 4, 2, 8),      // 59 decode: 16 weight rows, 4 waves along K x 2 chunks
     ECFG(1, 1, 8, 2, 8),      // 60 decode: 16 weight rows, 8 waves along K x 2 chunks
     ECFG(1, 1, 4, 4, 16),     // 61 decode: 16 rows of X, 4 waves along K x 4 chunks
+    RCFG(3, 2, 4, 8, 2),      // 62 rows: 48 x 32 tile, 4 waves along K x 8 chunks
+    RCFG(2, 2, 4, 8, 4),      // 63 rows: 32 x 32 tile, 4 waves along K x 8 chunks, 4 in flight
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1471,8 +1493,9 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
       cps = 32;
     }
   } else {
-    // rows kernel: 16 x 32 (M <= 64), 32 x 32 (<= 128), 48 x 32 (<= 192), 64 x 32 tiles
-    cfg = s.M <= 64 ? 30 : s.M <= 128 ? 31 : s.M <= 192 ? 32 : 33;
+    // rows kernel: 16 x 32 tiles, 8 waves along K (M <= 64); 32 x 32 (<= 128), 48 x 32 (<= 192)
+    // and 64 x 32 tiles, 4 waves along K x 8 chunks
+    cfg = s.M <= 64 ? 30 : s.M <= 128 ? 37 : s.M <= 192 ? 62 : 33;
     cps = kchunks < 32 ? kchunks : 32;
   }
   if (split_k > 0) cps = (kchunks + split_k - 1) / split_k;
