@@ -1499,7 +1499,11 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
     cps = kchunks < 32 ? kchunks : 32;
   }
   if (split_k > 0) cps = (kchunks + split_k - 1) / split_k;
-  return plan_with(s, cfg, cps, plan);
+  const int st = plan_with(s, cfg, cps, plan);
+  if (st != BSFP8_EINVAL) return st;
+  // The one-pass choice cannot take this many chunks per split (an explicit split_k with a long
+  // K): the staged kernel walks any K range in passes (16 rows of X, 4 waves along K).
+  return plan_with(s, 2, cps, plan);
 }
 
 int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,

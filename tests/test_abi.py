@@ -73,6 +73,33 @@ def test_workspace_and_plans(lib):
         assert info["BM"] % 8 == 0 and info["NB"] % 16 == 0 and info["threads"] % 64 == 0
 
 
+def test_plan_is_valid_for_every_shape_class(lib):
+    """The built-in plan picks a compiled configuration that accepts the shape for every row count
+    1..256, N and K multiples of 32 (ragged and whole 128-chunk K, narrow and wide weights), G in
+    1, 2, 4, with and without an explicit split, and every chunk is owned by exactly one split."""
+    Ks = [32, 96, 128, 576, 640, 800, 2048, 4096, 5120, 8192]
+    Ns = [32, 96, 128, 1024, 5120, 16384, 32768]
+    for M in list(range(1, 33)) + [48, 63, 64, 65, 96, 127, 128, 129, 160, 192, 193, 224, 256]:
+        for G in (1, 2, 4):
+            for N in Ns:
+                if G * N > 65536:
+                    continue
+                for K in Ks:
+                    for split_k in (0, 1, 3):
+                        p = B.bsfp8_plan_info(M, G, N, K, split_k=split_k)
+                        kch = (K + 127) // 128
+                        assert p["kchunks"] == kch
+                        assert (p["splits"] - 1) * p["cps"] < kch <= p["splits"] * p["cps"], (M, G, N, K, split_k, p)
+                        assert p["mblocks"] * p["BM"] >= M and N % p["NB"] == 0
+                        info = B.bsfp8_config_info(p["cfg"])
+                        if info["kind"] in (3, 4):
+                            assert K % 128 == 0
+                        if split_k:
+                            assert p["splits"] == -(-kch // -(-kch // split_k))
+                        ws = B.bsfp8_workspace_bytes(M, G, N, K, split_k)
+                        assert (ws == 0) == (p["splits"] == 1) or ws > 0
+
+
 def test_argument_checks_return_before_gpu_work(lib):
     null = ctypes.c_void_p(0)
     G = lib.bsfp8_gemm

@@ -62,6 +62,17 @@ def test_explicit_split_k(split_k):
     check_bf16(bf16_bits(y), x, G, N, K, q, e)
 
 
+@pytest.mark.parametrize("M,G,N,K", [(6, 1, 64, 5120), (40, 2, 64, 4608), (12, 1, 32, 8192)])
+def test_one_split_over_a_long_k(M, G, N, K):
+    """split_k=1 with more chunks than a one-pass kernel holds: the plan falls back to the staged
+    kernel, which walks the whole K range in passes."""
+    p = B.bsfp8_plan_info(M, G, N, K, split_k=1)
+    assert p["splits"] == 1 and B.bsfp8_config_info(p["cfg"])["kind"] == 0
+    x, q, e = _inputs(350 + M, M, G, N, K)
+    y = _run("bsfp8_gemm", x, q, e, G, K, split_k=1)
+    check_bf16(bf16_bits(y), x, G, N, K, q, e)
+
+
 def test_every_kernel_configuration():
     """Each compiled configuration, with a few chunks-per-split values, on a shape with several
     m-blocks (where the tile is smaller than M), a ragged K tail (the tile and decode kernels
