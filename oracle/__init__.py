@@ -4,6 +4,9 @@ TEST INFRASTRUCTURE ONLY. It may be imported by tests/, by __graft_entry__.smoke
 cpu_baseline leg of bench.py, and by nothing else. It shares no code, tables or constants with
 the HIP library under block_scaled_fp8_skinny_amd/, and imports nothing from it.
 
+Modules: formats (e4m3, bf16, fp32 rounding), ops (the bf16 hot path and its preparation), mx
+(MXFP8 activations and the fp8 x fp8 contraction, the next step after the hot path).
+
 Parity status: every function here is pinned by CPU tests (tests/test_oracle_*.py) to values
 fixed by the format definitions, closed forms, invariants and exact rational brute force.
 """
