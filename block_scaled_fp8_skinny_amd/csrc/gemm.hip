@@ -1282,6 +1282,236 @@ gemm_decode_kernel(KParams p) {
     if (live[i]) store_out(p, off[i], v[i]);
 }
 
+// Slab kernel for mid row counts on narrow weights: a BM x NB output tile per workgroup over its
+// whole K range, the X slab shared by all waves through LDS. What bounds these shapes is the rate
+// at which one CU can pull L2-resident data: a wave load that reads one contiguous kilobyte runs
+// at about 100 GB/s per CU, one spread over two to sixteen rows (the fragment-friendly shapes) at
+// about 60. So the K range is walked in slabs of four chunks (512 values, one kilobyte of each X
+// row), and every X load fetches one whole row piece:
+//  * a stage of the LDS ring holds the X slab (BM rows x 1 KB, row-major, granule g of row r at
+//    slot g ^ (r % 16), so that the fragment reads of 16 rows at one k hit 16 distinct bank groups)
+//    and the weight slab (NB rows x 512 bytes, two rows per load, granule g of row R at slot
+//    g ^ (R % 16)); each lane fetches the granule that belongs in its slot, so a load still covers
+//    exactly one contiguous kilobyte (X) or two 512-byte row pieces (weights);
+//  * S - 1 slabs are in flight while one is computed; each wave counts its own loads (every wave
+//    issues the same number per slab) and one barrier per slab publishes the stage and frees the
+//    one consumed before;
+//  * NWM x NWN x NWK waves: a wave owns a 16*MT x 16*NT sub-tile and the chunks
+//    wk*CPW .. wk*CPW + CPW - 1 of every slab (CPW = 4 / NWK), so each output's fp32 sum is
+//    NWK ascending chains, which are added through LDS in ascending wk order at the end;
+//  * with more than one split (whole slabs per split) the partials meet in the pairwise-exchange
+//    tree of the one-pass kernels.
+constexpr int SLAB_CH = 4;                          // chunks per slab
+
+template <int MT, int NT, int NWM, int NWN, int NWK, int S>
+__global__ void __launch_bounds__(WAVE * NWM * NWN * NWK)
+gemm_slab_kernel(KParams p) {
+  constexpr int NWAVE = NWM * NWN * NWK;
+  constexpr int BM = 16 * MT * NWM;
+  constexpr int NB = 16 * NT * NWN;
+  constexpr int CPW = SLAB_CH / NWK;                // chunks of a slab per wave
+  constexpr int XG = BM * 64;                       // 16-byte granules of an X slab
+  constexpr int WGR = NB * 32;                      // ... of a weight slab
+  constexpr int PCX = BM / NWAVE, PCW = NB / 2 / NWAVE;
+  constexpr int PC = PCX + PCW;                     // loads per wave per slab
+  constexpr int EROWS = NB / 32;
+  constexpr int ESTR = TILE_MAX_CPS * 4;
+  constexpr int TILES = MT * NT;
+  static_assert(SLAB_CH % NWK == 0, "waves along K split a slab evenly");
+  static_assert(BM % NWAVE == 0 && (NB / 2) % NWAVE == 0, "every wave issues the same loads");
+  static_assert(S >= 2 && (S - 2) * PC <= 63, "ring depth, counter range");
+  static_assert(NB % 32 == 0, "whole exponent block rows");
+  static_assert((NWK - 1) * NWM * NWN * TILES * WAVE * 16 <= S * (XG + WGR) * 16, "reduction fits the ring");
+  __shared__ uint4 ring[S][XG + WGR];
+  __shared__ uint8_t e_lds[EROWS * ESTR];
+
+  prefetch_args(p);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wk = wave / (NWM * NWN), wmn = wave % (NWM * NWN);
+  const int wm = wmn / NWN, wn = wmn % NWN;
+  const int q4 = lane >> 4, r16 = lane & 15;
+
+  int t = xcd_logical(blockIdx.x, p.nwg);
+  const int mb = t % p.mblocks;
+  t /= p.mblocks;
+  const int nb = t % p.nblocks;
+  t /= p.nblocks;
+  const int g = t % p.G;
+  const int s = t / p.G;
+
+  const int K = p.K, M = p.M, N = p.N, G = p.G;
+  const int n0 = nb * NB, m0 = mb * BM;
+  const int c_begin = s * p.cps;                    // a multiple of SLAB_CH
+  const int c_end = min(c_begin + p.cps, p.kchunks);
+  const int nch = c_end - c_begin;
+  const int nslab = (nch + SLAB_CH - 1) / SLAB_CH;
+  const int KB = K / 32;
+
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, (int)p.x_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.q, 0, (int)p.q_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((void*)p.e, 0, (int)p.e_bytes, RSRC_WORD3);
+
+  // exponent words of the split's range (one 4-byte word = one chunk of a block row)
+  for (int er = wave; er < EROWS; er += NWAVE) {
+    const int kb = (c_begin + lane) * 4;
+    const uint32_t off = (uint32_t)((g * (N / 32) + n0 / 32 + er) * KB + kb);
+    lds_load4(re, lds_addr(e_lds + er * ESTR), lane < nch && kb < KB ? off : OOB);
+  }
+
+  // X load u: tile row i = wave + u*NWAVE, the lane fetches granule lane ^ (i % 16) of the row's
+  // kilobyte. Weight load u: rows 2i, 2i + 1 (i = wave + u*NWAVE), the lane fetches granule
+  // (lane % 32) ^ (R % 16) of row R = 2i + lane/32.
+  uint32_t xoff[PCX];
+  bool xok[PCX];
+#pragma unroll
+  for (int u = 0; u < PCX; ++u) {
+    const int i = wave + u * NWAVE;
+    const int m = m0 + i;
+    xok[u] = m < M;
+    xoff[u] = xok[u] ? (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K + (lane ^ (i & 15)) * 8) * 2) : 0u;
+  }
+  uint32_t woff[PCW];
+#pragma unroll
+  for (int u = 0; u < PCW; ++u) {
+    const int i = wave + u * NWAVE;
+    const int R = 2 * i + (lane >> 5);
+    woff[u] = (uint32_t)(g * N + n0 + R) * (uint32_t)K + 16 * ((lane & 31) ^ (R & 15));
+  }
+  auto issue = [&](int j) {
+    const int c0 = c_begin + j * SLAB_CH;           // first chunk of slab j
+    const bool sok = j < nslab;
+    const uint4* st = ring[j % S];
+#pragma unroll
+    for (int u = 0; u < PCX; ++u) {
+      const int i = wave + u * NWAVE;
+      const uint32_t k2 = (uint32_t)(c0 * KCH * 2);
+      lds_load16(rx, lds_addr(st + i * 64), sok && xok[u] && c0 * KCH + 8 * lane < K ? xoff[u] + k2 : OOB);
+    }
+#pragma unroll
+    for (int u = 0; u < PCW; ++u) {
+      const int i = wave + u * NWAVE;
+      lds_load16_stream(rq, lds_addr(st + XG + i * 64), sok ? woff[u] + (uint32_t)(c0 * KCH) : OOB);
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) issue(j);
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) acc[mt][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int j = 0; j < nslab; ++j) {
+    wait_vmcnt_le<(S - 2) * PC>();                  // this wave's loads of slab j
+    lds_barrier();                                  // ... everyone's; slab j - 1 is consumed
+    issue(j + S - 1);
+    const uint4* st = ring[j % S];
+#pragma unroll
+    for (int cc = wk * CPW; cc < wk * CPW + CPW; ++cc) {
+      const int cl = j * SLAB_CH + cc;              // chunk index inside the split
+      if (cl >= nch) break;
+      bf16x8_t xf[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint4* xrow = st + (wm * 16 * MT + mt * 16 + r16) * 64;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          xf[mt][u] = __builtin_bit_cast(bf16x8_t, xrow[(cc * 16 + 2 * q4 + (u & 1) + 8 * (u >> 1)) ^ r16]);
+      }
+      const int e0 = cl * 4 + (q4 >> 1);
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) {
+        const int R = wn * 16 * NT + ts * 16 + r16;
+        const uint4* wrow = st + XG + R * 32;
+        const uint4 a = wrow[(cc * 8 + q4) ^ r16];
+        const uint4 b = wrow[(cc * 8 + 4 + q4) ^ r16];
+        const int er = R >> 5;
+        const float sc0 = block_scale(e_lds[er * ESTR + e0]);
+        const float sc1 = block_scale(e_lds[er * ESTR + e0 + 2]);
+        const bf16x8_t w0 = dequant8(a.x, a.y, sc0);
+        const bf16x8_t w1 = dequant8(a.z, a.w, sc0);
+        const bf16x8_t w2 = dequant8(b.x, b.y, sc1);
+        const bf16x8_t w3 = dequant8(b.z, b.w, sc1);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4_t c = acc[mt][ts];
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, xf[mt][0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, xf[mt][1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2, xf[mt][2], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w3, xf[mt][3], c, 0, 0, 0);
+          acc[mt][ts] = c;
+        }
+      }
+    }
+  }
+  wait_vmcnt_le<0>();                               // no load may still be writing LDS
+
+  // waves along K: ascending-order sum through LDS (aliasing the ring)
+  if constexpr (NWK > 1) {
+    lds_barrier();                                  // every wave is done with the ring
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(&ring[0][0]);
+    if (wk > 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ts = 0; ts < NT; ++ts)
+          red[(((wk - 1) * NWM * NWN + wmn) * TILES + mt * NT + ts) * WAVE + lane] = acc[mt][ts];
+    }
+    __syncthreads();
+    if (wk != 0) return;
+#pragma unroll
+    for (int w = 1; w < NWK; ++w)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ts = 0; ts < NT; ++ts)
+          acc[mt][ts] += red[(((w - 1) * NWM * NWN + wmn) * TILES + mt * NT + ts) * WAVE + lane];
+  }
+
+  if (p.splits == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = m0 + wm * 16 * MT + mt * 16 + r16;
+      if (m >= M) continue;
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) {
+        const size_t o = ((size_t)m * G + g) * N + n0 + wn * 16 * NT + ts * 16 + q4 * 4;
+        const f32x4_t v = acc[mt][ts];
+        if (p.out_f32) {
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + o) = v;
+        } else {
+          const uint2 w2 = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + o) = w2;
+        }
+      }
+    }
+    return;
+  }
+  constexpr int NV = TILES * 4;
+  float v[NV];
+  size_t off[NV];
+  bool live[NV];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = (mt * NT + ts) * 4 + r;
+        const int m = m0 + wm * 16 * MT + mt * 16 + r16;
+        v[i] = acc[mt][ts][r];
+        off[i] = ((size_t)m * G + g) * N + n0 + wn * 16 * NT + ts * 16 + q4 * 4 + r;
+        live[i] = m < M;
+      }
+  combine_splits<NV>(p, s, v, off, live);
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (live[i]) store_out(p, off[i], v[i]);
+}
+
 // Split-K reduction for the tile kernel: Y = sum over s = 0, 1, ..., S-1 of the partials, added
 // in that order in fp32, then rounded once to the output type. Four outputs per thread.
 __global__ void __launch_bounds__(256)
@@ -1304,10 +1534,11 @@ reduce_splits_kernel(const float* __restrict__ part, void* __restrict__ y, int64
 // ---------------------------------------------------------------------------------------------
 typedef void (*KernelFn)(KParams);
 
-enum Kind { STAGED = 0, DIRECT = 1, ROWS = 2, TILE = 3, DECODE = 4 };
+enum Kind { STAGED = 0, DIRECT = 1, ROWS = 2, TILE = 3, DECODE = 4, SLAB = 5 };
 
 struct Config {
-  int MT, NT, NWM, NWN, NWK, CW;         // TILE: CW = chunks in flight; DECODE: MT*16 = X rows
+  int MT, NT, NWM, NWN, NWK, CW;         // TILE: CW = chunks in flight; SLAB: CW = ring stages;
+                                         // DECODE: MT = X rows
   KernelFn fn;
   int kind;                              // DIRECT, ROWS and DECODE kernels make one pass
 };
@@ -1317,6 +1548,7 @@ struct Config {
 #define RCFG(MT, NT, NWK, CW, D) {MT, NT, 1, 1, NWK, CW, gemm_rows_kernel<MT, NT, NWK, CW, D>, ROWS}
 #define ECFG(NT, NWN, NWK, CW, XR) {XR, NT, 1, NWN, NWK, CW, gemm_decode_kernel<NT, NWN, NWK, CW, XR>, DECODE}
 #define TCFG(MT, NT, NWM, NWN, D, GI) {MT, NT, NWM, NWN, 1, D, gemm_tile_kernel<MT, NT, NWM, NWN, D, GI>, TILE}
+#define SCFG(MT, NT, NWM, NWN, NWK, S) {MT, NT, NWM, NWN, NWK, S, gemm_slab_kernel<MT, NT, NWM, NWN, NWK, S>, SLAB}
 
 const Config kConfigs[] = {
     CFG(1, 1, 4, 1, 4),   // 0  small: 64 rows, one wave per 16 rows, 4 chunks per wave
@@ -1383,6 +1615,18 @@ const Config kConfigs[] = {
     ECFG(1, 1, 4, 4, 16),     // 61 decode: 16 rows of X, 4 waves along K x 4 chunks
     RCFG(3, 2, 4, 8, 2),      // 62 rows: 48 x 32 tile, 4 waves along K x 8 chunks
     RCFG(2, 2, 4, 8, 4),      // 63 rows: 32 x 32 tile, 4 waves along K x 8 chunks, 4 in flight
+    TCFG(1, 1, 1, 2, 16, 4),  // 64 tile: 16 x 32, 2 waves of 16 x 16, 16 stages
+    TCFG(1, 1, 2, 2, 12, 4),  // 65 tile: 32 x 32, 4 waves of 16 x 16, 12 stages
+    TCFG(3, 1, 1, 2, 9, 4),   // 66 tile: 48 x 32, 2 waves of 48 x 16, 9 stages
+    TCFG(2, 1, 1, 2, 12, 4),  // 67 tile: 32 x 32, 2 waves of 32 x 16, 12 stages
+    TCFG(2, 1, 2, 2, 7, 4),   // 68 tile: 64 x 32, 4 waves of 32 x 16, 7 stages
+    SCFG(1, 1, 1, 2, 4, 4),   // 69 slab: 16 x 32, 8 waves (2 along N x 4 along K), 4 stages
+    SCFG(1, 1, 2, 2, 2, 3),   // 70 slab: 32 x 32, 8 waves (2 x 2 x 2 along K), 3 stages
+    SCFG(1, 2, 2, 1, 4, 3),   // 71 slab: 32 x 32, 8 waves (2 along M x 4 along K), 3 stages
+    SCFG(3, 1, 1, 2, 4, 2),   // 72 slab: 48 x 32, 8 waves (2 along N x 4 along K), 2 stages
+    SCFG(1, 1, 1, 4, 2, 3),   // 73 slab: 16 x 64, 8 waves (4 along N x 2 along K), 3 stages
+    SCFG(1, 1, 2, 2, 1, 3),   // 74 slab: 32 x 32, 4 waves (2 x 2), 3 stages
+    SCFG(1, 2, 1, 2, 4, 3),   // 75 slab: 16 x 64, 8 waves (2 along N x 4 along K), 3 stages
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1426,6 +1670,10 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
     return BSFP8_EINVAL;                                        // one pass
   if (c.kind == DECODE && s.K % KCH != 0) return BSFP8_EINVAL;  // whole exponent words per chunk
   if (c.kind == TILE && (p.cps > TILE_MAX_CPS || s.K % KCH != 0)) return BSFP8_EINVAL;
+  // slab kernel: K in whole chunks, splits begin on slab boundaries, one exponent word per lane
+  if (c.kind == SLAB &&
+      (s.K % KCH != 0 || p.cps > TILE_MAX_CPS || (p.cps < p.kchunks && p.cps % SLAB_CH != 0)))
+    return BSFP8_EINVAL;
   p.splits = (p.kchunks + p.cps - 1) / p.cps;
   if (p.splits > 64) return BSFP8_EINVAL;
   p.mblocks = (s.M + p.BM - 1) / p.BM;
@@ -1493,10 +1741,16 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
       cps = 32;
     }
   } else {
-    // rows kernel: 16 x 32 tiles, 8 waves along K (M <= 64); 32 x 32 (<= 128), 48 x 32 (<= 192)
-    // and 64 x 32 tiles, 4 waves along K x 8 chunks
-    cfg = s.M <= 64 ? 30 : s.M <= 128 ? 37 : s.M <= 192 ? 62 : 33;
-    cps = kchunks < 32 ? kchunks : 32;
+    // up to 64 rows with K in whole chunks: the slab kernel (16 x 32 tiles, X rows read a
+    // kilobyte at a time), one split. Otherwise the rows kernel: 16 x 32 tiles, 8 waves along K
+    // (M <= 64); 32 x 32 (<= 128), 48 x 32 (<= 192) and 64 x 32 tiles, 4 waves along K x 8 chunks
+    if (s.M <= 64 && s.K % KCH == 0 && kchunks <= TILE_MAX_CPS) {
+      cfg = 69;
+      cps = kchunks;
+    } else {
+      cfg = s.M <= 64 ? 30 : s.M <= 128 ? 37 : s.M <= 192 ? 62 : 33;
+      cps = kchunks < 32 ? kchunks : 32;
+    }
   }
   if (split_k > 0) cps = (kchunks + split_k - 1) / split_k;
   const int st = plan_with(s, cfg, cps, plan);

@@ -92,8 +92,10 @@ def test_plan_is_valid_for_every_shape_class(lib):
                         assert (p["splits"] - 1) * p["cps"] < kch <= p["splits"] * p["cps"], (M, G, N, K, split_k, p)
                         assert p["mblocks"] * p["BM"] >= M and N % p["NB"] == 0
                         info = B.bsfp8_config_info(p["cfg"])
-                        if info["kind"] in (3, 4):
+                        if info["kind"] in (3, 4, 5):
                             assert K % 128 == 0
+                        if info["kind"] == 5 and p["splits"] > 1:
+                            assert p["cps"] % 4 == 0
                         if split_k:
                             assert p["splits"] == -(-kch // -(-kch // split_k))
                         ws = B.bsfp8_workspace_bytes(M, G, N, K, split_k)

@@ -62,12 +62,16 @@ def test_explicit_split_k(split_k):
     check_bf16(bf16_bits(y), x, G, N, K, q, e)
 
 
-@pytest.mark.parametrize("M,G,N,K", [(6, 1, 64, 5120), (40, 2, 64, 4608), (12, 1, 32, 8192)])
+@pytest.mark.parametrize("M,G,N,K", [(6, 1, 64, 5120), (40, 2, 64, 4608), (12, 1, 32, 8192),
+                                     (40, 1, 32, 8320)])
 def test_one_split_over_a_long_k(M, G, N, K):
     """split_k=1 with more chunks than a one-pass kernel holds: the plan falls back to the staged
-    kernel, which walks the whole K range in passes."""
+    kernel, which walks the whole K range in passes, or (33..64 rows, K in whole chunks, at most
+    64 of them) keeps the slab kernel, which walks any K range in slabs."""
     p = B.bsfp8_plan_info(M, G, N, K, split_k=1)
-    assert p["splits"] == 1 and B.bsfp8_config_info(p["cfg"])["kind"] == 0
+    kind = B.bsfp8_config_info(p["cfg"])["kind"]
+    assert p["splits"] == 1 and kind in (0, 5)
+    assert (kind == 5) == (33 <= M <= 64 and K % 128 == 0 and K <= 8192)
     x, q, e = _inputs(350 + M, M, G, N, K)
     y = _run("bsfp8_gemm", x, q, e, G, K, split_k=1)
     check_bf16(bf16_bits(y), x, G, N, K, q, e)
@@ -80,12 +84,14 @@ def test_every_kernel_configuration():
     G, N = 2, 256
     for cfg in range(B.bsfp8_num_configs()):
         info = B.bsfp8_config_info(cfg)
-        K = 768 if info["kind"] in (3, 4) else 800
+        K = 768 if info["kind"] in (3, 4, 5) else 800
         M = min(2 * info["BM"] - 3, 256)
         x, q, e = _inputs(400 + cfg, M, G, N, K)
         exact = oracle.gemm_exact_f64(x, G, N, K, q, e)
         if info["kind"] in (1, 2, 4):       # one pass: chunks per split <= CW * NWK
             cps_list = sorted({1, 2, info["CW"] * info["NWK"]})
+        elif info["kind"] == 5:             # splits on 4-chunk slab boundaries, a partial last slab
+            cps_list = (4, (K + 127) // 128)
         else:                               # several splits, and one split over all the chunks
             cps_list = (1, 2, (K + 127) // 128)
         for cps in cps_list:
