@@ -41,6 +41,12 @@ _SIGS = {
     "bsfp8_plan_info": (_I, [_I64, _I64, _I64, _I64, _I, _I, ctypes.POINTER(_I)]),
     "bsfp8_workspace_bytes_config": (_SZ, [_I64, _I64, _I64, _I64, _I, _I]),
     "bsfp8_gemm_config": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _I, _P, _SZ, _P, _I, _P]),
+    "bsfp8_quantize_mx": (_I, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "bsfp8_gemm_mx": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _I, _P]),
+    "bsfp8_mx_num_configs": (_I, []),
+    "bsfp8_mx_config_info": (_I, [_I, ctypes.POINTER(_I)]),
+    "bsfp8_mx_plan": (_I, [_I64, _I64, _I64]),
+    "bsfp8_gemm_mx_config": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _P, _I, _P]),
 }
 
 _lib = None
@@ -279,4 +285,71 @@ def bsfp8_gemm_config(x, q, e, cfg, cps, ws=None, out=None, out_dtype="bf16"):
     wsb = ws.numel() if ws is not None else 0
     _check(lib().bsfp8_gemm_config(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), cfg, cps, _ptr(ws), wsb,
                                    _ptr(out), od, _stream(x)), "bsfp8_gemm_config")
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# MXFP8 activations and the fp8 x fp8 GEMM
+# ------------------------------------------------------------------------------------------------
+def bsfp8_quantize_mx(x, L=None, xq=None, xs=None):
+    """bf16 activations [M, >= L] -> (codes uint8 [M, L], scale bytes uint8 [M, L/32])."""
+    x, M, ldx = _x_view(x)
+    if x.dim() == 3:
+        raise ValueError("x must be [M, L]")
+    L = x.shape[1] if L is None else L
+    if xq is None:
+        xq = torch.empty((M, L), dtype=torch.uint8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M, L // 32), dtype=torch.uint8, device=x.device)
+    _need(xq, torch.uint8, "xq")
+    _need(xs, torch.uint8, "xs")
+    _check(lib().bsfp8_quantize_mx(_ptr(x), ldx, M, L, _ptr(xq), _ptr(xs), _stream(x)), "bsfp8_quantize_mx")
+    return xq, xs
+
+
+def _mx_args(xq, xs, q, e, out, out_dtype):
+    q = _codes(q)
+    _need(q, torch.uint8, "q")
+    _need(e, torch.uint8, "e")
+    xq = _codes(xq)
+    if xq.dtype != torch.uint8 or xq.dim() != 2 or xq.stride(1) != 1 or not xq.is_cuda:
+        raise ValueError("xq must be a uint8 GPU tensor [M, ldq] with unit column stride")
+    M = xq.shape[0]
+    ldq = xq.stride(0) if M > 1 else xq.shape[1]
+    if xs.dtype != torch.uint8 or xs.dim() != 2 or xs.stride(1) != 1 or (M > 1 and xs.stride(0) * 32 != ldq):
+        raise ValueError("xs must be uint8 [M, ldq/32] with rows aligned to the codes")
+    G, N, K = q.shape
+    od = OUT_F32 if out_dtype in ("f32", torch.float32, OUT_F32) else OUT_BF16
+    if out is None:
+        out = torch.empty((M, G, N), dtype=torch.float32 if od == OUT_F32 else torch.bfloat16, device=xq.device)
+    _need(out, torch.float32 if od == OUT_F32 else torch.bfloat16, "out")
+    return xq, q, M, ldq, G, N, K, od, out
+
+
+def bsfp8_gemm_mx(xq, xs, q, e, out=None, out_dtype="bf16"):
+    """Y [M, G, N] = per group Xmx[:, g*K:(g+1)*K] @ W_g^T on the block-scaled fp8 MFMA."""
+    xq, q, M, ldq, G, N, K, od, out = _mx_args(xq, xs, q, e, out, out_dtype)
+    _check(lib().bsfp8_gemm_mx(_ptr(xq), _ptr(xs), ldq, M, G, N, K, _ptr(q), _ptr(e), _ptr(out), od, _stream(xq)),
+           "bsfp8_gemm_mx")
+    return out
+
+
+def bsfp8_mx_num_configs():
+    return int(lib().bsfp8_mx_num_configs())
+
+
+def bsfp8_mx_config_info(cfg):
+    out = (_I * 6)()
+    _check(lib().bsfp8_mx_config_info(cfg, out), "bsfp8_mx_config_info")
+    return dict(BM=out[0], NB=out[1], threads=out[2], SC=out[3], stages=out[4], NWK=out[5])
+
+
+def bsfp8_mx_plan(M, G, N):
+    return _check(int(lib().bsfp8_mx_plan(M, G, N)), "bsfp8_mx_plan")
+
+
+def bsfp8_gemm_mx_config(xq, xs, q, e, cfg, out=None, out_dtype="bf16"):
+    xq, q, M, ldq, G, N, K, od, out = _mx_args(xq, xs, q, e, out, out_dtype)
+    _check(lib().bsfp8_gemm_mx_config(_ptr(xq), _ptr(xs), ldq, M, G, N, K, _ptr(q), _ptr(e), cfg, _ptr(out), od,
+                                      _stream(xq)), "bsfp8_gemm_mx_config")
     return out

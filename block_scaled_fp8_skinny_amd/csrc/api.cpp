@@ -74,6 +74,20 @@ struct Counter {
   }
 };
 
+// Size, alignment and stride checks of the fp8 x fp8 GEMM.
+int check_gemm_mx(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int64_t M, int64_t G, int64_t N,
+                  int64_t K, const uint8_t* q, const uint8_t* e, void* y, int out_dtype) {
+  if (out_dtype != BSFP8_OUT_BF16 && out_dtype != BSFP8_OUT_F32) return BSFP8_EINVAL;
+  if (M < 0 || M > 256 || G < 1 || N < 32 || K < 128 || N % 32 || K % 128) return BSFP8_ESHAPE;
+  if (K > 8192 || G > 4096 || N > (1 << 24) || G * N > (1 << 26)) return BSFP8_ESHAPE;
+  if (M > 0 && (!xq || !xs || !q || !e || !y)) return BSFP8_EINVAL;
+  if (ldq < G * K || ldq % 128) return BSFP8_ESTRIDE;
+  if (!aligned16(xq) || !aligned16(q) || !aligned16(y) || (reinterpret_cast<uintptr_t>(xs) & 3) ||
+      (reinterpret_cast<uintptr_t>(e) & 3))
+    return BSFP8_ESTRIDE;
+  return BSFP8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -242,6 +256,44 @@ int bsfp8_gemm_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int6
   if (st != BSFP8_OK) return st;
   if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned16(ws))) return BSFP8_EWORKSPACE;
   return launch_gemm(s, p, x, q, e, ws, y, out_dtype == BSFP8_OUT_F32, as_stream(stream));
+}
+
+int bsfp8_quantize_mx(const uint16_t* x, int64_t ldx, int64_t M, int64_t L, uint8_t* xq, uint8_t* xs,
+                      void* stream) {
+  if (M < 0 || L < 32 || L % 32 || M > (1 << 24) || L > (1 << 26)) return BSFP8_ESHAPE;
+  if (M == 0) return BSFP8_OK;
+  if (!x || !xq || !xs) return BSFP8_EINVAL;
+  if (ldx < L || ldx % 8 || !aligned16(x) || !aligned16(xq)) return BSFP8_ESTRIDE;
+  return launch_quantize_mx(x, ldx, M, L, xq, xs, as_stream(stream));
+}
+
+int bsfp8_gemm_mx(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int64_t M, int64_t G, int64_t N,
+                  int64_t K, const uint8_t* q, const uint8_t* e, void* y, int out_dtype, void* stream) {
+  const int st = check_gemm_mx(xq, xs, ldq, M, G, N, K, q, e, y, out_dtype);
+  if (st != BSFP8_OK || M == 0) return st;
+  return launch_gemm_mx(xq, xs, ldq, (int)M, (int)G, (int)N, (int)K, q, e, y, out_dtype == BSFP8_OUT_F32,
+                        mx_pick((int)M, (int)G, (int)N), as_stream(stream));
+}
+
+int bsfp8_mx_num_configs(void) { return num_mx_configs(); }
+
+int bsfp8_mx_config_info(int cfg, int* out) {
+  if (!out) return BSFP8_EINVAL;
+  return mx_config_info(cfg, out);
+}
+
+int bsfp8_mx_plan(int64_t M, int64_t G, int64_t N) {
+  if (M < 1 || M > 256 || G < 1 || N < 32 || N % 32) return BSFP8_ESHAPE;
+  return mx_pick((int)M, (int)G, (int)N);
+}
+
+int bsfp8_gemm_mx_config(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int64_t M, int64_t G,
+                         int64_t N, int64_t K, const uint8_t* q, const uint8_t* e, int cfg, void* y,
+                         int out_dtype, void* stream) {
+  const int st = check_gemm_mx(xq, xs, ldq, M, G, N, K, q, e, y, out_dtype);
+  if (st != BSFP8_OK || M == 0) return st;
+  return launch_gemm_mx(xq, xs, ldq, (int)M, (int)G, (int)N, (int)K, q, e, y, out_dtype == BSFP8_OUT_F32, cfg,
+                        as_stream(stream));
 }
 
 }  // extern "C"

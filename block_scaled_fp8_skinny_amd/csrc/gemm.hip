@@ -40,129 +40,11 @@
 
 #include <type_traits>
 
-#include "internal.h"
+#include "device.h"
 
 namespace bsfp8 {
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int KCH = 128;                 // K per chunk
-constexpr int WAVE = 64;
-constexpr int MAX_LEVELS = 7;            // splits <= 64 -> at most 6 tree levels
-constexpr uint32_t OOB = 0x80000000u;    // buffer offset beyond every descriptor's range
-constexpr int RSRC_WORD3 = 0x00020000;   // raw buffer descriptor word 3 for gfx9-class GPUs
-
-struct KParams {
-  const uint16_t* x;
-  const uint8_t* q;
-  const uint8_t* e;
-  void* y;
-  unsigned long long* slots;             // pairwise-combine slots (splits > 1)
-  int64_t ldx;
-  uint32_t x_bytes, q_bytes, e_bytes;    // extents of the three buffer descriptors
-  int M, G, N, K;
-  int kchunks, cps, splits, mblocks, nblocks, out_f32;
-  int nwg;                               // grid size (gridDim would be read from the dispatch packet)
-  int levels;
-  int level_base[MAX_LEVELS];            // first slot array of each tree level
-};
-
-__device__ __forceinline__ uint32_t bits_of(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
-
-// Eight e4m3 codes (two dwords, k order = byte order) times the block factor -> eight bf16.
-__device__ __forceinline__ bf16x8_t dequant8(uint32_t lo, uint32_t hi, float scale) {
-  u32x4_t r;
-  r[0] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false));
-  r[1] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true));
-  r[2] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false));
-  r[3] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true));
-  return __builtin_bit_cast(bf16x8_t, r);
-}
-
-// Block factor 2^(b-127) as the fp32 whose exponent field is b (the convert reads the exponent).
-__device__ __forceinline__ float block_scale(uint32_t b) { return __uint_as_float(b << 23); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  bf16x2_t v = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32: round half to even
-  return bits_of(v);
-}
-
-__device__ __forceinline__ uint16_t to_bf16(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
-
-__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// Weight stream: read once per call, so it is loaded non-temporally ("nt") and does not evict
-// the activation slab, which every workgroup of the call re-reads from L2.
-constexpr int CPOL_NT = 2;
-__device__ __forceinline__ uint4 load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CPOL_NT);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// Logical workgroup index such that each XCD (hardware slot blockIdx % 8) owns a contiguous
-// range of logical indices.
-// (Branch-free: XCDs below `rem` hold per + 1 workgroups, the others per.)
-__device__ __forceinline__ int xcd_logical(int i, int nwg) {
-  const int xcd = i & 7, idx = i >> 3, per = nwg >> 3, rem = nwg & 7;
-  return xcd * per + min(xcd, rem) + idx;
-}
-
-// Fetch every kernel argument at entry: an empty asm that reads the fields makes the compiler
-// issue all the scalar argument loads together (one round trip) instead of in dependent rounds.
-__device__ __forceinline__ void prefetch_args(const KParams& p) {
-  asm volatile("" ::"s"(p.x), "s"(p.q), "s"(p.e), "s"(p.y), "s"(p.slots), "s"(p.ldx));
-  asm volatile("" ::"s"(p.x_bytes), "s"(p.q_bytes), "s"(p.e_bytes), "s"(p.M), "s"(p.G), "s"(p.N),
-               "s"(p.K));
-  asm volatile("" ::"s"(p.kchunks), "s"(p.cps), "s"(p.splits), "s"(p.mblocks), "s"(p.nblocks),
-               "s"(p.out_f32), "s"(p.nwg));
-}
-
-// Pairwise-combine tree over the split index for up to NV outputs of one lane (see the header
-// comment). v[i] is this split's partial of output i, off[i] its element index, live[i] whether
-// the lane owns it. All exchanges of one tree level are issued before any result is used, so a
-// level costs one round trip to memory. On return live[i] says whether this lane finished output
-// i (its total is then in v[i]).
-template <int NV>
-__device__ __forceinline__ void combine_splits(const KParams& p, int s, float (&v)[NV],
-                                               const size_t (&off)[NV], bool (&live)[NV]) {
-  const size_t mgn = (size_t)p.M * p.G * p.N;
-  int idx = s, cnt = p.splits;
-  for (int lv = 0; lv < p.levels; ++lv) {
-    if ((idx ^ 1) < cnt) {
-      unsigned long long* base = p.slots + (size_t)(p.level_base[lv] + (idx >> 1)) * mgn;
-      unsigned long long old[NV];
-#pragma unroll
-      for (int i = 0; i < NV; ++i)
-        old[i] = live[i] ? atomicExch(base + off[i], (1ull << 32) | __float_as_uint(v[i])) : 0ull;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        if (!live[i]) continue;
-        if (old[i] == 0ull) {
-          live[i] = false;                          // the partner finishes this node
-        } else {
-          v[i] = __uint_as_float((uint32_t)old[i]) + v[i];
-          __hip_atomic_store(base + off[i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    }
-    idx >>= 1;
-    cnt = (cnt + 1) >> 1;
-  }
-}
-
-__device__ __forceinline__ void store_out(const KParams& p, size_t off, float v) {
-  if (p.out_f32)
-    reinterpret_cast<float*>(p.y)[off] = v;
-  else
-    reinterpret_cast<uint16_t*>(p.y)[off] = to_bf16(v);
-}
 
 template <int MT, int NT, int NWN, int NWK, int CW>
 __global__ void __launch_bounds__(WAVE * NWN * NWK)
@@ -863,47 +745,6 @@ gemm_rows_kernel(KParams p) {
 //  * The exponent bytes of the workgroup's K range are staged once.
 //  * With splits > 1 each workgroup stores its fp32 partial tile to the workspace [S][M][G][N]
 //    and a second kernel sums the partials in ascending split order.
-constexpr int TILE_MAX_CPS = 64;                    // exponent staging: at most 64 chunks per split
-
-// Workgroup barrier for the LDS ring: every LDS read of this wave has completed (lgkmcnt 0) and
-// no memory access moves across it, but - unlike __syncthreads(), whose fence would also wait for
-// the loads still streaming into the other stages - it does not wait for the vector memory
-// counter.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Buffer loads in LDS mode: lane l's bytes land at LDS address lds + l*size (lds is wave-uniform,
-// passed in M0; the compiler cannot prove that values derived from the wave index are uniform,
-// hence the readfirstlane). Written as inline assembly so that the compiler neither reorders them nor adds
-// waits of its own for them (it would wait for every load in flight before any LDS read); the
-// kernel counts them itself with wait_vmcnt_le.
-typedef uint32_t lds_addr_t;
-template <typename T>
-__device__ __forceinline__ lds_addr_t lds_addr(const T* p) {
-  return (lds_addr_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
-}
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_addr_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_load16_stream(__amdgpu_buffer_rsrc_t r, lds_addr_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, lds_addr_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory", "m0");
-}
-
-// Wait until at most N of this wave's vector memory loads are outstanding (loads complete in
-// order); no memory access of the kernel moves across it.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_le() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 template <int MT, int NT, int NWM, int NWN, int D, int GI>
 __global__ void __launch_bounds__(WAVE * NWM * NWN)
 gemm_tile_kernel(KParams p) {

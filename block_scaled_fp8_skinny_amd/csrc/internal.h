@@ -50,6 +50,15 @@ int launch_pad_k_input(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int
 int launch_dequant(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
                    uint16_t* w, hipStream_t stream);
 
+// MXFP8 activations and the fp8 x fp8 GEMM (mx.hip)
+int launch_quantize_mx(const uint16_t* x, int64_t ldx, int64_t M, int64_t L, uint8_t* xq, uint8_t* xs,
+                       hipStream_t stream);
+int launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int M, int G, int N, int K,
+                   const uint8_t* q, const uint8_t* e, void* y, int out_f32, int cfg, hipStream_t stream);
+int num_mx_configs();
+int mx_config_info(int cfg, int* out);
+int mx_pick(int M, int G, int N);
+
 inline int hip_status(hipError_t err) { return err == hipSuccess ? BSFP8_OK : BSFP8_EHIP; }
 
 }  // namespace bsfp8

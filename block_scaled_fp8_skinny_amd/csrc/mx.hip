@@ -1,0 +1,411 @@
+// MXFP8 activations and the fp8 x fp8 block-scaled GEMM for gfx950 (MI355X).
+//
+// The pages' comparison path is an MXFP8 W8A8 linear: the linear quantizes its bf16 input itself
+// into e4m3 elements with one power-of-two (E8M0) scale per 32 consecutive values of a row, and
+// multiplies it with the block-fp8 weight (page "recipes/docker-images/mia-tp4/adapter/
+// shared_pad_k.py", module docstring, DIAGNOSIS and LOSSLESS). The pages do not print the
+// quantizer; the rule here is the OCP Microscaling v1.0 one for MXFP8: scale exponent
+// floor(log2(amax)) - 8, elements rounded to nearest even and saturated at +-448.
+//
+// Design (gfx950, wave64):
+//  * quantize_mx_kernel: four lanes per 32-value block (eight values each), amax by two lane
+//    exchanges, the scale exponent read off the bf16 exponent field, each element scaled by an
+//    exact power of two and rounded with the integer e4m3 encoder shared with the twin encoder.
+//  * gemm_mx_kernel: v_mfma_scale_f32_16x16x128_f8f6f4 takes both operands as e4m3 codes with
+//    one E8M0 scale per 32 values of each row, so there is no dequantisation at all. Measured
+//    operand layout: a lane (r16, q) of a 128-wide chunk holds k = 16q + [0, 16) and
+//    64 + 16q + [0, 16) of its row (the bf16 kernels' weight pieces), and lane r + 16b supplies
+//    the scale of row r, block b. The weight is the A operand (16 weight rows), the activation
+//    codes the B operand. Each 128-wide chunk is one MFMA per 16 x 16 tile.
+//  * Both operands stream into an LDS ring with the buffer loads' LDS mode, SC chunks per stage;
+//    at SC = 8 every load is one contiguous kilobyte of one row (the fastest shape for a CU to
+//    pull), at SC = 1 eight rows x 128 bytes. Each lane fetches the granule that belongs in its
+//    slot (granule g of row r at slot g ^ (r % 16), or g ^ (r/2 % 8) for 128-byte rows), so the
+//    fragment reads of 16 rows at one k hit 16 distinct bank groups.
+//  * The weight exponents and the activation scales of the whole K range are staged once.
+//  * Waves split the tile (NWM x NWN) and the chunks of a stage (NWK); the NWK chains are added
+//    through LDS in ascending order, so every output's fp32 sum is fixed by the configuration.
+
+#include "device.h"
+
+namespace bsfp8 {
+namespace {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+constexpr int MX_BLOCK = 32;
+constexpr int MX_MAX_CH = 64;                       // chunks staged at once (K <= 8192)
+
+// ---------------------------------------------------------------------------------------------
+// quantizer: x bf16 [M][ldx] -> codes [M][L], scale bytes [M][L/32]
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) quantize_mx_kernel(const uint16_t* x, int64_t ldx, int64_t L,
+                                                          int64_t nblk, uint8_t* xq, uint8_t* xs) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t blk = t >> 2;                       // 32-value block; four lanes each
+  const int part = (int)(t & 3);
+  const bool live = blk < nblk;
+  const int64_t bpr = L / MX_BLOCK;
+  const int64_t m = live ? blk / bpr : 0, cb = live ? blk % bpr : 0;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (live) v = *reinterpret_cast<const uint4*>(x + m * ldx + cb * MX_BLOCK + part * 8);
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  uint32_t h[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[2 * i] = d[i] & 0xFFFF;
+    h[2 * i + 1] = d[i] >> 16;
+  }
+  uint32_t amax = 0, nonfinite = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t mag = h[i] & 0x7FFF;
+    nonfinite |= mag >= 0x7F80 ? 1u : 0u;
+    amax = mag > amax ? mag : amax;
+  }
+  // the four lanes of a block are adjacent in the wave
+#pragma unroll
+  for (int off = 1; off <= 2; off <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)amax, off);
+    amax = o > amax ? o : amax;
+    nonfinite |= (uint32_t)__shfl_xor((int)nonfinite, off);
+  }
+  // floor(log2(amax)) = E - 127 for a normal bf16 amax; zero and subnormal amax give the
+  // smallest scale. s = floor(log2(amax)) - 8, clamped to [-127, 127].
+  const int E = (int)(amax >> 7);
+  int s = E == 0 ? -127 : E - 135;
+  s = s < -127 ? -127 : (s > 127 ? 127 : s);
+  uint32_t codes[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (nonfinite) {
+      codes[i] = (h[i] & 0x8000) ? 0xFFu : 0x7Fu;
+    } else {
+      float sv = ldexpf(__uint_as_float(h[i] << 16), -s);   // exact: a power-of-two scaling
+      sv = fminf(fmaxf(sv, -448.f), 448.f);                   // saturating conversion
+      codes[i] = e4m3_rne(sv);
+    }
+  }
+  if (live) {
+    const uint2 o = make_uint2(codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24),
+                               codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24));
+    *reinterpret_cast<uint2*>(xq + m * L + cb * MX_BLOCK + part * 8) = o;
+    if (part == 0) xs[m * bpr + cb] = nonfinite ? (uint8_t)255 : (uint8_t)(s + 127);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp8 x fp8 GEMM
+// ---------------------------------------------------------------------------------------------
+struct MxParams {
+  const uint8_t* xq;                   // activation codes [M][ldq], group g at columns g*K
+  const uint8_t* xs;                   // activation scale bytes [M][ldq/32]
+  const uint8_t* q;                    // weight codes [G][N][K]
+  const uint8_t* e;                    // weight exponent bytes [G][N/32][K/32]
+  void* y;                             // [M][G][N] bf16 or fp32
+  int64_t ldq;                         // row stride of xq in bytes (a multiple of 128)
+  uint32_t xq_bytes, xs_bytes, q_bytes, e_bytes;
+  int M, G, N, K, kchunks, mblocks, nblocks, out_f32, nwg;
+};
+
+__device__ __forceinline__ void prefetch_mx_args(const MxParams& p) {
+  asm volatile("" ::"s"(p.xq), "s"(p.xs), "s"(p.q), "s"(p.e), "s"(p.y), "s"(p.ldq));
+  asm volatile("" ::"s"(p.xq_bytes), "s"(p.xs_bytes), "s"(p.q_bytes), "s"(p.e_bytes), "s"(p.M), "s"(p.G),
+               "s"(p.N), "s"(p.K));
+  asm volatile("" ::"s"(p.kchunks), "s"(p.mblocks), "s"(p.nblocks), "s"(p.out_f32), "s"(p.nwg));
+}
+
+// Slot swizzle of a row piece of P granules (16 bytes each): XOR with the row inside a 16-granule
+// window, or inside the piece itself for 128-byte pieces (two rows share one 256-byte bank cycle).
+template <int P>
+__device__ __forceinline__ int mx_swz(int row) {
+  return P >= 16 ? (row & 15) : ((row >> 1) & 7);
+}
+
+template <int MT, int NT, int NWM, int NWN, int NWK, int SC, int S>
+__global__ void __launch_bounds__(WAVE * NWM * NWN * NWK)
+gemm_mx_kernel(MxParams p) {
+  constexpr int NWAVE = NWM * NWN * NWK;
+  constexpr int BM = 16 * MT * NWM;
+  constexpr int NB = 16 * NT * NWN;
+  constexpr int P = 8 * SC;                         // granules of one row piece per stage
+  constexpr int RPL = 64 / P;                       // rows per load
+  constexpr int XG = BM * P, WGR = NB * P;          // granules of the X and weight parts of a stage
+  constexpr int XI = BM / RPL, WI = NB / RPL;       // loads per stage
+  constexpr int PCX = XI / NWAVE, PCW = WI / NWAVE;
+  constexpr int PC = PCX + PCW;
+  constexpr int CPW = SC / NWK;                     // chunks of a stage per wave
+  constexpr int EROWS = NB >= 32 ? NB / 32 : 1;
+  constexpr int TILES = MT * NT;
+  static_assert(SC == 1 || SC == 2 || SC == 4 || SC == 8, "stage width");
+  static_assert(SC % NWK == 0, "waves along K split a stage evenly");
+  static_assert(XI % NWAVE == 0 && WI % NWAVE == 0, "every wave issues the same loads");
+  static_assert(S >= 2 && (S - 2) * PC <= 63, "ring depth, counter range");
+  static_assert((NWK - 1) * NWM * NWN * TILES * WAVE <= S * (XG + WGR), "reduction fits the ring");
+  __shared__ uint4 ring[S][XG + WGR];
+  __shared__ uint32_t e_lds[EROWS * MX_MAX_CH];
+  __shared__ uint32_t xs_lds[BM * MX_MAX_CH];
+
+  prefetch_mx_args(p);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wk = wave / (NWM * NWN), wmn = wave % (NWM * NWN);
+  const int wm = wmn / NWN, wn = wmn % NWN;
+  const int q4 = lane >> 4, r16 = lane & 15;
+
+  int t = xcd_logical(blockIdx.x, p.nwg);
+  const int mb = t % p.mblocks;
+  t /= p.mblocks;
+  const int nb = t % p.nblocks;
+  const int g = t / p.nblocks;
+
+  const int K = p.K, M = p.M, N = p.N, G = p.G;
+  const int n0 = nb * NB, m0 = mb * BM;
+  const int nch = p.kchunks;
+  const int nst = (nch + SC - 1) / SC;
+  const int KB = K / 32;
+  const uint32_t ldsx = (uint32_t)(p.ldq / 32);    // row stride of the scale bytes
+
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)p.xq, 0, (int)p.xq_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)p.xs, 0, (int)p.xs_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.q, 0, (int)p.q_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((void*)p.e, 0, (int)p.e_bytes, RSRC_WORD3);
+
+  // (1) weight exponent words (one 4-byte word = the four blocks of one chunk of a block row)
+  for (int er = wave; er < EROWS; er += NWAVE) {
+    const uint32_t off = (uint32_t)((g * (N / 32) + n0 / 32 + er) * KB + lane * 4);
+    lds_load4(re, lds_addr(e_lds + er * MX_MAX_CH), lane < nch ? off : OOB);
+  }
+  // (2) activation scale words, dense [BM][nch]: word f is chunk f % nch of tile row f / nch
+  for (int i = wave; i * 64 < BM * nch; i += NWAVE) {
+    const int f = i * 64 + lane;
+    const int row = f / nch, c = f % nch;
+    const int m = m0 + row;
+    const uint32_t off = (uint32_t)m * ldsx + (uint32_t)(g * KB + c * 4);
+    lds_load4(rs, lds_addr(xs_lds + i * 64), f < BM * nch && m < M ? off : OOB);
+  }
+
+  // Load u of a stage: rows RPL*i .. RPL*i + RPL - 1 (i = wave + u*NWAVE) of the X or weight
+  // part; the lane fills slot lane % P of row RPL*i + lane / P with granule slot ^ swz(row).
+  const int lrow = lane / P, lslot = lane % P;
+  uint32_t xoff[PCX];
+  int xgran[PCX];
+  bool xok[PCX];
+#pragma unroll
+  for (int u = 0; u < PCX; ++u) {
+    const int row = RPL * (wave + u * NWAVE) + lrow;
+    const int m = m0 + row;
+    xgran[u] = lslot ^ mx_swz<P>(row);
+    xok[u] = m < M;
+    xoff[u] = xok[u] ? (uint32_t)((int64_t)m * p.ldq + (int64_t)g * K + 16 * xgran[u]) : 0u;
+  }
+  uint32_t woff[PCW];
+  int wgran[PCW];
+#pragma unroll
+  for (int u = 0; u < PCW; ++u) {
+    const int row = RPL * (wave + u * NWAVE) + lrow;
+    wgran[u] = lslot ^ mx_swz<P>(row);
+    woff[u] = (uint32_t)(g * N + n0 + row) * (uint32_t)K + 16 * wgran[u];
+  }
+  auto issue = [&](int j) {
+    const int c0 = j * SC;                          // first chunk of stage j
+    const uint4* st = ring[j % S];
+#pragma unroll
+    for (int u = 0; u < PCX; ++u) {
+      const int i = wave + u * NWAVE;
+      const bool ok = xok[u] && c0 + (xgran[u] >> 3) < nch;
+      lds_load16(rx, lds_addr(st + i * 64), ok ? xoff[u] + (uint32_t)(c0 * KCH) : OOB);
+    }
+#pragma unroll
+    for (int u = 0; u < PCW; ++u) {
+      const int i = wave + u * NWAVE;
+      const bool ok = c0 + (wgran[u] >> 3) < nch;
+      lds_load16_stream(rq, lds_addr(st + XG + i * 64), ok ? woff[u] + (uint32_t)(c0 * KCH) : OOB);
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) issue(j);
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) acc[mt][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint8_t* eb = reinterpret_cast<const uint8_t*>(e_lds);
+  const uint8_t* xsb = reinterpret_cast<const uint8_t*>(xs_lds);
+  const int sw = mx_swz<P>(r16);                    // rows of a fragment read start 16-aligned
+  for (int j = 0; j < nst; ++j) {
+    wait_vmcnt_le<(S - 2) * PC>();                  // this wave's loads of stage j
+    lds_barrier();                                  // ... everyone's; stage j - 1 is consumed
+    issue(j + S - 1);
+    const uint4* st = ring[j % S];
+#pragma unroll
+    for (int cc = wk * CPW; cc < wk * CPW + CPW; ++cc) {
+      const int cl = j * SC + cc;
+      if (cl >= nch) break;
+      v8i_t xf[MT];
+      int xsc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * 16 * MT + mt * 16 + r16;
+        const uint4* xr = st + row * P;
+        const uint4 a = xr[(cc * 8 + q4) ^ sw], b = xr[(cc * 8 + 4 + q4) ^ sw];
+        xf[mt] = v8i_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+        xsc[mt] = xsb[(row * nch + cl) * 4 + q4];
+      }
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) {
+        const int R = wn * 16 * NT + ts * 16 + r16;
+        const uint4* wr = st + XG + R * P;
+        const uint4 a = wr[(cc * 8 + q4) ^ sw], b = wr[(cc * 8 + 4 + q4) ^ sw];
+        const v8i_t wf = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+        const int er = (n0 + R) / 32 - n0 / 32;
+        const int wsc = eb[er * MX_MAX_CH * 4 + cl * 4 + q4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt][ts] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf[mt], acc[mt][ts], 0, 0, 0,
+                                                                        wsc, 0, xsc[mt]);
+      }
+    }
+  }
+  wait_vmcnt_le<0>();                               // no load may still be writing LDS
+
+  if constexpr (NWK > 1) {
+    lds_barrier();                                  // every wave is done with the ring
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(&ring[0][0]);
+    if (wk > 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ts = 0; ts < NT; ++ts)
+          red[(((wk - 1) * NWM * NWN + wmn) * TILES + mt * NT + ts) * WAVE + lane] = acc[mt][ts];
+    }
+    __syncthreads();
+    if (wk != 0) return;
+#pragma unroll
+    for (int w = 1; w < NWK; ++w)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ts = 0; ts < NT; ++ts)
+          acc[mt][ts] += red[(((w - 1) * NWM * NWN + wmn) * TILES + mt * NT + ts) * WAVE + lane];
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = m0 + wm * 16 * MT + mt * 16 + r16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) {
+      const size_t o = ((size_t)m * G + g) * N + n0 + wn * 16 * NT + ts * 16 + q4 * 4;
+      const f32x4_t v = acc[mt][ts];
+      if (p.out_f32) {
+        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + o) = v;
+      } else {
+        const uint2 w2 = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + o) = w2;
+      }
+    }
+  }
+}
+
+typedef void (*MxKernelFn)(MxParams);
+struct MxConfig {
+  int MT, NT, NWM, NWN, NWK, SC, S;
+  MxKernelFn fn;
+};
+#define XCFG(MT, NT, NWM, NWN, NWK, SC, S) \
+  {MT, NT, NWM, NWN, NWK, SC, S, gemm_mx_kernel<MT, NT, NWM, NWN, NWK, SC, S>}
+
+const MxConfig kMxConfigs[] = {
+    XCFG(1, 1, 1, 1, 4, 8, 4),   // 0  16 x 16, 4 waves along K, kilobyte rows, 4 stages
+    XCFG(1, 1, 1, 2, 4, 4, 5),   // 1  16 x 32, 8 waves (2 along N x 4 along K), 512-byte rows
+    XCFG(1, 1, 2, 2, 2, 4, 4),   // 2  32 x 32, 8 waves (2 x 2 x 2 along K), 512-byte rows
+    XCFG(3, 1, 1, 2, 4, 4, 3),   // 3  48 x 32, 8 waves (2 along N x 4 along K), 512-byte rows
+    XCFG(1, 1, 2, 2, 2, 8, 2),   // 4  32 x 32, 8 waves, kilobyte rows, 2 stages
+    XCFG(1, 2, 1, 4, 1, 2, 3),   // 5  16 x 128, 4 waves of 16 x 32, 256-byte rows
+    XCFG(2, 2, 2, 4, 1, 1, 4),   // 6  64 x 128, 8 waves of 32 x 32, 128-byte rows
+    XCFG(4, 2, 2, 4, 1, 1, 3),   // 7  128 x 128, 8 waves of 64 x 32, 128-byte rows
+    XCFG(1, 1, 1, 2, 4, 8, 3),   // 8  16 x 32, 8 waves (2 along N x 4 along K), kilobyte rows
+};
+constexpr int kNumMxConfigs = sizeof(kMxConfigs) / sizeof(kMxConfigs[0]);
+
+// Built-in choice: wide weights (an LM-head shard) take 128-wide weight tiles streamed once per
+// row tile; narrow weights take 16..48 x 16..32 tiles so that a few hundred workgroups fill the
+// chip.
+int mx_plan(int M, int G, int N) {
+  const long long tiles16 = (long long)G * N / 16;
+  if (tiles16 >= 1024 && N % 128 == 0) return M <= 16 ? 5 : M <= 64 ? 6 : 7;
+  if (M <= 16) return 0;
+  if (N % 32) return 0;
+  return M <= 64 ? 1 : M <= 128 ? 2 : 3;
+}
+
+}  // namespace
+
+int num_mx_configs() { return kNumMxConfigs; }
+
+int mx_config_info(int cfg, int* out) {
+  if (cfg < 0 || cfg >= kNumMxConfigs) return BSFP8_EINVAL;
+  const MxConfig& c = kMxConfigs[cfg];
+  out[0] = 16 * c.MT * c.NWM;
+  out[1] = 16 * c.NT * c.NWN;
+  out[2] = WAVE * c.NWM * c.NWN * c.NWK;
+  out[3] = c.SC;
+  out[4] = c.S;
+  out[5] = c.NWK;
+  return BSFP8_OK;
+}
+
+int mx_pick(int M, int G, int N) { return mx_plan(M, G, N); }
+
+int launch_quantize_mx(const uint16_t* x, int64_t ldx, int64_t M, int64_t L, uint8_t* xq, uint8_t* xs,
+                       hipStream_t stream) {
+  const int64_t nblk = M * (L / MX_BLOCK);
+  if (nblk == 0) return BSFP8_OK;
+  const int64_t threads = nblk * 4;
+  hipLaunchKernelGGL(quantize_mx_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, x, ldx,
+                     L, nblk, xq, xs);
+  return hip_status(hipGetLastError());
+}
+
+int launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int M, int G, int N, int K,
+                   const uint8_t* q, const uint8_t* e, void* y, int out_f32, int cfg, hipStream_t stream) {
+  if (cfg < 0 || cfg >= kNumMxConfigs) return BSFP8_EINVAL;
+  const MxConfig& c = kMxConfigs[cfg];
+  const int BM = 16 * c.MT * c.NWM, NB = 16 * c.NT * c.NWN;
+  if (N % NB) return BSFP8_ESHAPE;
+  MxParams k{};
+  k.xq = xq;
+  k.xs = xs;
+  k.q = q;
+  k.e = e;
+  k.y = y;
+  k.ldq = ldq;
+  const int64_t xb = (int64_t)(M - 1) * ldq + (int64_t)G * K;
+  const int64_t sb = (int64_t)(M - 1) * (ldq / 32) + (int64_t)G * K / 32;
+  const int64_t qb = (int64_t)G * N * K;
+  const int64_t ebytes = (int64_t)G * (N / 32) * (K / 32);
+  if (xb >= (int64_t)OOB || sb >= (int64_t)OOB || qb >= (int64_t)OOB || ebytes >= (int64_t)OOB)
+    return BSFP8_ESHAPE;
+  k.xq_bytes = (uint32_t)xb;
+  k.xs_bytes = (uint32_t)sb;
+  k.q_bytes = (uint32_t)qb;
+  k.e_bytes = (uint32_t)ebytes;
+  k.M = M;
+  k.G = G;
+  k.N = N;
+  k.K = K;
+  k.kchunks = K / KCH;
+  k.mblocks = (M + BM - 1) / BM;
+  k.nblocks = N / NB;
+  k.out_f32 = out_f32;
+  const long long nwg = (long long)k.mblocks * k.nblocks * G;
+  if (nwg <= 0 || nwg > 0x7fffffffLL) return BSFP8_ESHAPE;
+  k.nwg = (int)nwg;
+  hipLaunchKernelGGL(c.fn, dim3((unsigned)nwg), dim3(WAVE * c.NWM * c.NWN * c.NWK), 0, stream, k);
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace bsfp8

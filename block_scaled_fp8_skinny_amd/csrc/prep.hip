@@ -1,14 +1,10 @@
 // Preparation kernels of the block-scaled fp8 weight path for gfx950: scale ingestion, the
 // exact-twin encoder, K padding and standalone dequantisation.
 
-#include "internal.h"
+#include "device.h"
 
 namespace bsfp8 {
 namespace {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t bits_of(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
 // ---------------------------------------------------------------------------------------------
 // fp32 block scales -> exponent bytes (page "shared_pad_k.py", _pad_weight: positive powers of
@@ -37,35 +33,6 @@ __device__ __forceinline__ int block_exp(uint32_t amax_bits) {
   const int E = (int)(amax_bits >> 7), f = (int)(amax_bits & 0x7F);
   int e = (E == 0) ? -134 : (f <= 96 ? E - 135 : E - 134);
   return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
-// e4m3 code of an fp32 value with |v| <= 448, round half to even (including the e4m3
-// subnormals, quantum 2^-9); magnitudes below 2^-10 give a signed zero.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80;
-  const uint32_t a = u & 0x7FFFFFFF;
-  const uint32_t E = a >> 23;
-  uint32_t code;
-  if (E >= 121) {                                   // >= 2^-6: e4m3 normal range
-    const uint32_t keep = ((E - 120) << 3) | ((a >> 20) & 7);
-    const uint32_t rest = a & 0xFFFFF;
-    code = keep + ((rest > 0x80000u || (rest == 0x80000u && (keep & 1))) ? 1 : 0);
-  } else if (E == 0) {
-    code = 0;                                       // fp32 zero/subnormal: far below 2^-10
-  } else {
-    const uint32_t full = (a & 0x7FFFFF) | 0x800000; // value = full * 2^(E - 150)
-    const uint32_t sh = 141 - E;                     // quantum 2^-9 = 2^(E-150) * 2^sh
-    if (sh > 24) {
-      code = 0;
-    } else {
-      const uint32_t keep = full >> sh;
-      const uint32_t rest = full & ((1u << sh) - 1);
-      const uint32_t half = 1u << (sh - 1);
-      code = keep + ((rest > half || (rest == half && (keep & 1))) ? 1 : 0);
-    }
-  }
-  return sign | code;
 }
 
 __global__ void __launch_bounds__(256) make_twin_kernel(const uint16_t* w, int64_t nblk_r,

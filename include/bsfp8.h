@@ -154,6 +154,45 @@ BSFP8_API int bsfp8_gemm(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, i
                const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes,
                void* y, int out_dtype, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * MXFP8 activations and the fp8 x fp8 GEMM (W8A8; per call, asynchronous, no allocation)
+ *
+ * Page "recipes/docker-images/mia-tp4/adapter/shared_pad_k.py" (module docstring, DIAGNOSIS and
+ * LOSSLESS): the pages' MXFP8 linear quantizes its bf16 input itself into e4m3 values with one
+ * power-of-two (E8M0) scale per 32 consecutive values of a row and multiplies that with the
+ * block-fp8 weight. The pages do not print the quantizer; the rule here is OCP Microscaling (MX)
+ * v1.0 for MXFP8: per 32-value block, s = floor(log2(max |v|)) - 8 clamped to [-127, 127]
+ * (an all-zero block gets -127), each element e4m3(v * 2^-s) rounded to nearest even and
+ * saturated at +-448; a block holding inf or NaN gets scale byte 255 and e4m3 NaN codes
+ * (0x7F, or 0xFF for a negative sign). Unlike the bf16 path this is lossy: it is the pages'
+ * comparison path, not the exact twin GEMM.
+ * ------------------------------------------------------------------------------------------ */
+
+/* bf16 activations -> MXFP8 codes and scale bytes.
+ *   x  : uint16_t bf16 [M][ldx] (device, 16-byte aligned), ldx >= L, ldx % 8 == 0.
+ *   xq : uint8_t e4m3 codes [M][L] (device, contiguous, 16-byte aligned).
+ *   xs : uint8_t scale bytes [M][L/32] (device, contiguous), byte = s + 127 (2^(byte-127)).
+ * L % 32 == 0. Deterministic and exact (every decision is an integer one). */
+BSFP8_API int bsfp8_quantize_mx(const uint16_t* x, int64_t ldx, int64_t M, int64_t L, uint8_t* xq,
+                                uint8_t* xs, void* stream);
+
+/* Y[m][g][n] = sum_k Xmx[m][g*K + k] * W[g][n][k], with Xmx = e4m3(xq) * 2^(xs - 127) per
+ * 32-value row block and W = e4m3(q) * 2^(e - 127) per 32x32 weight block (the weight's block
+ * exponent serves as the MX scale of each row's 32-value piece).
+ *   xq, xs : codes [M][ldq] (16-byte aligned) and scale bytes [M][ldq/32] (4-byte aligned), group g
+ *            at columns [g*K, (g+1)*K) (e.g. the output of bsfp8_quantize_mx with L = G*K);
+ *            ldq >= G*K and ldq % 128 == 0.
+ *   q, e   : the weight twin as for bsfp8_gemm (q 16-byte aligned, e 4-byte aligned).
+ *   y      : [M][G][N] bf16 (RNE) or fp32 per out_dtype (16-byte aligned).
+ * 1 <= M <= 256 (M == 0 is a no-op), N % 32 == 0, K % 128 == 0 and K <= 8192. The products run
+ * on the block-scaled fp8 MFMA with fp32 accumulation across 128-wide chunks; the hardware sums
+ * each group of eight adjacent products inside the instruction with a precision of about 2^-14
+ * of the group's largest product (measured), so results are not those of an exact sum rounded
+ * once. The summation order is fixed by the built-in configuration: bitwise reproducible. */
+BSFP8_API int bsfp8_gemm_mx(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int64_t M, int64_t G,
+                            int64_t N, int64_t K, const uint8_t* q, const uint8_t* e, void* y,
+                            int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,9 @@ BSFP8_API int bsfp8_num_configs(void);
  * workgroup), 2 = one-pass with both operands in registers, 3 = tile kernel (X shared through
  * LDS; out[3] = chunks in flight; with more than one split each workgroup writes an fp32 partial
  * tile and a second kernel adds the partials in ascending split order), 4 = one-pass decode
- * kernel (X, exponents and weights streamed into LDS; out[0] rows of X per workgroup). For kinds
+ * kernel (X, exponents and weights streamed into LDS; out[0] rows of X per workgroup), 5 = slab
+ * kernel (X shared through an LDS ring of 512-wide K slabs; out[3] = ring stages; splits begin
+ * on slab boundaries). For kinds
  * 1, 2 and 4 the chunks per split must be at most out[3] * out[5]; for kind 3 at most 64. Kinds 3
  * and 4 take K in whole 128-wide chunks (K % 128 == 0).
  * Returns BSFP8_EINVAL for an unknown cfg. `out` is host memory of 7 ints. */
@@ -47,6 +49,18 @@ BSFP8_API size_t bsfp8_workspace_bytes_config(int64_t M, int64_t G, int64_t N, i
 BSFP8_API int bsfp8_gemm_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
                       const uint8_t* q, const uint8_t* e, int cfg, int cps, void* ws,
                       size_t ws_bytes, void* y, int out_dtype, void* stream);
+
+/* fp8 x fp8 GEMM (bsfp8_gemm_mx) configurations. out (host, 6 ints) of bsfp8_mx_config_info:
+ * rows of X per workgroup, weight rows per workgroup, threads, chunks per ring stage, ring stages,
+ * waves along K. bsfp8_mx_plan returns the configuration bsfp8_gemm_mx picks (or a negative
+ * status). bsfp8_gemm_mx_config runs an explicit configuration; arguments and errors otherwise as
+ * bsfp8_gemm_mx (BSFP8_ESHAPE when N is not a multiple of the configuration's weight rows). */
+BSFP8_API int bsfp8_mx_num_configs(void);
+BSFP8_API int bsfp8_mx_config_info(int cfg, int* out);
+BSFP8_API int bsfp8_mx_plan(int64_t M, int64_t G, int64_t N);
+BSFP8_API int bsfp8_gemm_mx_config(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int64_t M, int64_t G,
+                                   int64_t N, int64_t K, const uint8_t* q, const uint8_t* e, int cfg,
+                                   void* y, int out_dtype, void* stream);
 
 #ifdef __cplusplus
 }
