@@ -92,7 +92,33 @@ def make_copies(torch, B, G, N, K, elo, ehi, n_copies, seed):
     return qs, es
 
 
-def time_workload(name, M, steps, warmup, split_k=0):
+def graph_us(torch, fn, steps):
+    """Average time per call of `steps` calls of fn(i) captured in one HIP graph and replayed
+    between HIP events on the replay stream (the first replay uploads the graph, untimed)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(steps):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    del graph
+    return 1e3 * t0.elapsed_time(t1) / steps
+
+
+def time_workload(name, M, steps, warmup, split_k=0, path="bf16"):
+    """path "bf16": the exact twin GEMM (bsfp8_gemm). path "mx": the fp8 x fp8 GEMM
+    (bsfp8_gemm_mx) on activations quantized once before the timed region; the quantizer is timed
+    on its own and reported as quantize_us."""
     import torch
     import block_scaled_fp8_skinny_amd as B
     import synthetic as S
@@ -100,16 +126,30 @@ def time_workload(name, M, steps, warmup, split_k=0):
     G, N, K, _, (elo, ehi), out, desc = WORKLOADS[name]
     out_bytes = 4 if out == "f32" else 2
     w_b, e_b, x_b, y_b = algorithmic_bytes(M, G, N, K, out_bytes)
+    if path == "mx":
+        x_b = M * G * K + M * G * K // 32             # e4m3 codes + scale bytes
     copy_bytes = w_b + e_b
     n_copies = max(4, min(steps, math.ceil(COLD_BYTES / copy_bytes)))
     qs, es = make_copies(torch, B, G, N, K, elo, ehi, n_copies, seed=7000 + M)
     x = torch.from_numpy(S.bf16_normal(S.rng(7100 + M), (M, G * K)).view("int16")).view(torch.bfloat16).cuda()
-    ws = B.workspace(M, G, N, K, split_k)
+    ws = B.workspace(M, G, N, K, split_k) if path == "bf16" else None
     y = torch.empty((M, G, N), dtype=torch.float32 if out == "f32" else torch.bfloat16, device="cuda")
-    plan = B.bsfp8_plan_info(M, G, N, K, split_k)
+    quant_us = None
+    if path == "mx":
+        xq, xs = B.bsfp8_quantize_mx(x)
+        plan = {"mx_cfg": B.bsfp8_mx_plan(M, G, N), **B.bsfp8_mx_config_info(B.bsfp8_mx_plan(M, G, N))}
 
-    def call(i):
-        B.bsfp8_gemm(x, qs[i % n_copies], es[i % n_copies], split_k=split_k, ws=ws, out=y, out_dtype=out)
+        def call(i):
+            B.bsfp8_gemm_mx(xq, xs, qs[i % n_copies], es[i % n_copies], out=y, out_dtype=out)
+
+        for i in range(20):
+            B.bsfp8_quantize_mx(x, xq=xq, xs=xs)
+        quant_us = graph_us(torch, lambda i: B.bsfp8_quantize_mx(x, xq=xq, xs=xs), min(steps, 1000))
+    else:
+        plan = B.bsfp8_plan_info(M, G, N, K, split_k)
+
+        def call(i):
+            B.bsfp8_gemm(x, qs[i % n_copies], es[i % n_copies], split_k=split_k, ws=ws, out=y, out_dtype=out)
 
     for i in range(warmup):
         call(i)
@@ -129,32 +169,14 @@ def time_workload(name, M, steps, warmup, split_k=0):
     kern_us_median = 1e3 * kern_ms[n_ev // 2]
 
     # (2) wall time per call: all `steps` calls captured in one graph, replayed once
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(graph, stream=side):
-            for i in range(steps):
-                call(i)
-    torch.cuda.current_stream().wait_stream(side)
-    graph.replay()                     # untimed replay (first replay uploads the graph)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    graph.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    wall_ms = t0.elapsed_time(t1)
-    wall_us = 1e3 * wall_ms / steps
-    del graph
-    res = dict(workload=name, desc=desc, M=M, G=G, N=N, K=K, out=out, plan=plan, copies=n_copies,
+    wall_us = graph_us(torch, call, steps)
+    wall_ms = wall_us * steps / 1e3
+    res = dict(workload=name, path=path, desc=desc, M=M, G=G, N=N, K=K, out=out, plan=plan, copies=n_copies,
                copy_bytes=copy_bytes, wall_us_per_call=wall_us, kernel_us_mean=kern_us_mean,
                kernel_us_median=kern_us_median, weight_stream_gbs_wall=copy_bytes / (wall_us * 1e3),
                algorithmic_bytes=w_b + e_b + x_b + y_b, flops=2 * M * G * N * K,
                algorithmic_gbs=(w_b + e_b + x_b + y_b) / (wall_us * 1e3),
-               tflops=2 * M * G * N * K / (wall_us * 1e6), wall_ms_total=wall_ms)
+               tflops=2 * M * G * N * K / (wall_us * 1e6), wall_ms_total=wall_ms, quantize_us=quant_us)
     del qs, es
     torch.cuda.empty_cache()
     return res
@@ -191,17 +213,24 @@ def cpu_baseline(name, M, seconds):
                       f"BLAS threads={threads}, os.cpu_count()={os.cpu_count()}"}
 
 
+def gemm_source_sha256():
+    """Hash of the sources the bf16 GEMM kernels are built from (gemm.hip and device.h)."""
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "device.h"):
+        with open(os.path.join(ROOT, "block_scaled_fp8_skinny_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(name, M):
     """HBM bytes per launch from the committed rocprofv3 counter summary, when it was taken on
     the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{name}_m{M}.json")
-    src = os.path.join(ROOT, "block_scaled_fp8_skinny_amd", "csrc", "gemm.hip")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = gemm_source_sha256()
     if rec.get("gemm_source_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -265,6 +294,13 @@ def main():
             for m in ms:
                 st = 400 if name == "lm_head" else 2000
                 rr = time_workload(name, m, st, 50)
+                rows.append(rr)
+                print(json.dumps(rr), file=sys.stderr, flush=True)
+        # the fp8 x fp8 path (MXFP8 activations) on the same weights
+        for name, ms in (("wo_a", [6]), ("wo_a_mid", [16, 64, 128, 192]), ("lm_head", [16, 64, 128])):
+            for m in ms:
+                st = 400 if name == "lm_head" else 2000
+                rr = time_workload(name, m, st, 50, path="mx")
                 rows.append(rr)
                 print(json.dumps(rr), file=sys.stderr, flush=True)
         with open(args.all, "w") as f:

@@ -22,7 +22,11 @@
 //    pull), at SC = 1 eight rows x 128 bytes. Each lane fetches the granule that belongs in its
 //    slot (granule g of row r at slot g ^ (r % 16), or g ^ (r/2 % 8) for 128-byte rows), so the
 //    fragment reads of 16 rows at one k hit 16 distinct bank groups.
-//  * The weight exponents and the activation scales of the whole K range are staged once.
+//  * The weight exponents of the whole K range are staged once. The activation scales (one
+//    4-byte word = the four blocks of one chunk of a row) travel with each stage when a stage
+//    holds at least four chunks of a row (16 contiguous bytes per row); with narrower stages a
+//    per-stage load would touch one cache line per row for 4 bytes, so the scales of the whole
+//    K range are staged once instead, row by row.
 //  * Waves split the tile (NWM x NWN) and the chunks of a stage (NWK); the NWK chains are added
 //    through LDS in ascending order, so every output's fp32 sum is fixed by the configuration.
 
@@ -133,7 +137,11 @@ gemm_mx_kernel(MxParams p) {
   constexpr int XG = BM * P, WGR = NB * P;          // granules of the X and weight parts of a stage
   constexpr int XI = BM / RPL, WI = NB / RPL;       // loads per stage
   constexpr int PCX = XI / NWAVE, PCW = WI / NWAVE;
-  constexpr int PC = PCX + PCW;
+  constexpr bool XS_STAGED = SC >= 4;               // activation scales travel with the stage
+  constexpr int XSI = (BM * SC + 63) / 64;          // scale-word loads per stage (64 words each)
+  constexpr int PCS = XS_STAGED ? (XSI + NWAVE - 1) / NWAVE : 0;   // per wave (surplus: dummies)
+  constexpr int XSG = PCS * NWAVE * 16;             // granules of the scale part (a 256-byte slot per load)
+  constexpr int PC = PCX + PCW + PCS;
   constexpr int CPW = SC / NWK;                     // chunks of a stage per wave
   constexpr int EROWS = NB >= 32 ? NB / 32 : 1;
   constexpr int TILES = MT * NT;
@@ -141,10 +149,10 @@ gemm_mx_kernel(MxParams p) {
   static_assert(SC % NWK == 0, "waves along K split a stage evenly");
   static_assert(XI % NWAVE == 0 && WI % NWAVE == 0, "every wave issues the same loads");
   static_assert(S >= 2 && (S - 2) * PC <= 63, "ring depth, counter range");
-  static_assert((NWK - 1) * NWM * NWN * TILES * WAVE <= S * (XG + WGR), "reduction fits the ring");
-  __shared__ uint4 ring[S][XG + WGR];
+  static_assert((NWK - 1) * NWM * NWN * TILES * WAVE <= S * (XG + WGR + XSG), "reduction fits the ring");
+  __shared__ uint4 ring[S][XG + WGR + XSG];
   __shared__ uint32_t e_lds[EROWS * MX_MAX_CH];
-  __shared__ uint32_t xs_lds[BM * MX_MAX_CH];
+  __shared__ uint32_t xs_lds[XS_STAGED ? 1 : BM * MX_MAX_CH];
 
   prefetch_mx_args(p);
   const int tid = threadIdx.x;
@@ -176,13 +184,16 @@ gemm_mx_kernel(MxParams p) {
     const uint32_t off = (uint32_t)((g * (N / 32) + n0 / 32 + er) * KB + lane * 4);
     lds_load4(re, lds_addr(e_lds + er * MX_MAX_CH), lane < nch ? off : OOB);
   }
-  // (2) activation scale words, dense [BM][nch]: word f is chunk f % nch of tile row f / nch
-  for (int i = wave; i * 64 < BM * nch; i += NWAVE) {
-    const int f = i * 64 + lane;
-    const int row = f / nch, c = f % nch;
-    const int m = m0 + row;
-    const uint32_t off = (uint32_t)m * ldsx + (uint32_t)(g * KB + c * 4);
-    lds_load4(rs, lds_addr(xs_lds + i * 64), f < BM * nch && m < M ? off : OOB);
+  // (2) unless they travel with the stages: the activation scale words of the whole range, dense
+  //     [BM][nch] (word f is chunk f % nch of tile row f / nch)
+  if constexpr (!XS_STAGED) {
+    for (int i = wave; i * 64 < BM * nch; i += NWAVE) {
+      const int f = i * 64 + lane;
+      const int row = f / nch, c = f % nch;
+      const int m = m0 + row;
+      const uint32_t off = (uint32_t)m * ldsx + (uint32_t)(g * KB + c * 4);
+      lds_load4(rs, lds_addr(xs_lds + i * 64), f < BM * nch && m < M ? off : OOB);
+    }
   }
 
   // Load u of a stage: rows RPL*i .. RPL*i + RPL - 1 (i = wave + u*NWAVE) of the X or weight
@@ -207,9 +218,28 @@ gemm_mx_kernel(MxParams p) {
     wgran[u] = lslot ^ mx_swz<P>(row);
     woff[u] = (uint32_t)(g * N + n0 + row) * (uint32_t)K + 16 * wgran[u];
   }
+  // Scale load u of a stage: words i*64 .. i*64 + 63 (i = wave + u*NWAVE) of the stage's dense
+  // [BM][SC] array (row f / SC, chunk f % SC); loads with i >= XSI fill their slot with zeros.
+  uint32_t soff[PCS > 0 ? PCS : 1];
+  int schunk[PCS > 0 ? PCS : 1];
+  bool sok[PCS > 0 ? PCS : 1];
+#pragma unroll
+  for (int u = 0; u < PCS; ++u) {
+    const int f = (wave + u * NWAVE) * 64 + lane;
+    const int row = f / SC, m = m0 + row;
+    schunk[u] = f % SC;
+    sok[u] = f < BM * SC && m < M;
+    soff[u] = sok[u] ? (uint32_t)m * ldsx + (uint32_t)(g * KB + schunk[u] * 4) : 0u;
+  }
   auto issue = [&](int j) {
     const int c0 = j * SC;                          // first chunk of stage j
     const uint4* st = ring[j % S];
+#pragma unroll
+    for (int u = 0; u < PCS; ++u) {
+      const bool ok = sok[u] && c0 + schunk[u] < nch;
+      lds_load4(rs, lds_addr(st + XG + WGR + (wave + u * NWAVE) * 16), ok ? soff[u] + (uint32_t)(c0 * 4) : OOB);
+      (void)XSI;
+    }
 #pragma unroll
     for (int u = 0; u < PCX; ++u) {
       const int i = wave + u * NWAVE;
@@ -234,13 +264,16 @@ gemm_mx_kernel(MxParams p) {
     for (int ts = 0; ts < NT; ++ts) acc[mt][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const uint8_t* eb = reinterpret_cast<const uint8_t*>(e_lds);
-  const uint8_t* xsb = reinterpret_cast<const uint8_t*>(xs_lds);
   const int sw = mx_swz<P>(r16);                    // rows of a fragment read start 16-aligned
   for (int j = 0; j < nst; ++j) {
     wait_vmcnt_le<(S - 2) * PC>();                  // this wave's loads of stage j
     lds_barrier();                                  // ... everyone's; stage j - 1 is consumed
     issue(j + S - 1);
     const uint4* st = ring[j % S];
+    const uint8_t* xsb = XS_STAGED ? reinterpret_cast<const uint8_t*>(st + XG + WGR)
+                                   : reinterpret_cast<const uint8_t*>(xs_lds);
+    const int xrow_words = XS_STAGED ? SC : nch;    // words per row in the scale array read here
+    const int xcol = XS_STAGED ? 0 : j * SC;        // word of chunk cc of this stage
 #pragma unroll
     for (int cc = wk * CPW; cc < wk * CPW + CPW; ++cc) {
       const int cl = j * SC + cc;
@@ -253,7 +286,7 @@ gemm_mx_kernel(MxParams p) {
         const uint4* xr = st + row * P;
         const uint4 a = xr[(cc * 8 + q4) ^ sw], b = xr[(cc * 8 + 4 + q4) ^ sw];
         xf[mt] = v8i_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-        xsc[mt] = xsb[(row * nch + cl) * 4 + q4];
+        xsc[mt] = xsb[(row * xrow_words + xcol + cc) * 4 + q4];
       }
 #pragma unroll
       for (int ts = 0; ts < NT; ++ts) {
@@ -328,6 +361,9 @@ const MxConfig kMxConfigs[] = {
     XCFG(2, 2, 2, 4, 1, 1, 4),   // 6  64 x 128, 8 waves of 32 x 32, 128-byte rows
     XCFG(4, 2, 2, 4, 1, 1, 3),   // 7  128 x 128, 8 waves of 64 x 32, 128-byte rows
     XCFG(1, 1, 1, 2, 4, 8, 3),   // 8  16 x 32, 8 waves (2 along N x 4 along K), kilobyte rows
+    XCFG(2, 2, 2, 4, 1, 1, 5),   // 9  64 x 128, 8 waves of 32 x 32, 128-byte rows, 5 stages
+    XCFG(1, 2, 1, 4, 1, 2, 4),   // 10 16 x 128, 4 waves of 16 x 32, 256-byte rows, 4 stages
+    XCFG(1, 4, 1, 2, 2, 4, 2),   // 11 16 x 128, 4 waves (2 along N x 2 along K), 512-byte rows
 };
 constexpr int kNumMxConfigs = sizeof(kMxConfigs) / sizeof(kMxConfigs[0]);
 

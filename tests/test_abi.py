@@ -125,3 +125,31 @@ def test_argument_checks_return_before_gpu_work(lib):
     assert lib.bsfp8_pad_k_input(null, 10, 1, 1, 32, 64, null, null) == B.ESTRIDE
     assert lib.bsfp8_dequant(null, null, 1, 32, 40, null, null) == B.ESHAPE
     assert lib.bsfp8_scales_from_f32(null, -1, 2, null, ctypes.byref(bad), null) == B.ESHAPE
+
+
+def test_mx_argument_checks_and_plans(lib):
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(4096)
+    Q, X = lib.bsfp8_quantize_mx, lib.bsfp8_gemm_mx
+    assert Q(null, 64, 0, 64, null, null, null) == B.OK                     # empty: no-op
+    assert Q(null, 64, 2, 48, null, null, null) == B.ESHAPE                 # L not a multiple of 32
+    assert Q(fake, 32, 2, 64, fake, fake, null) == B.ESTRIDE                # ldx < L
+    assert Q(ctypes.c_void_p(4104), 64, 2, 64, fake, fake, null) == B.ESTRIDE   # x not 16-byte aligned
+    assert Q(null, 64, 2, 64, null, null, null) == B.EINVAL
+    # gemm_mx(xq, xs, ldq, M, G, N, K, q, e, y, out, stream)
+    assert X(null, null, 256, 0, 1, 64, 256, null, null, null, 0, null) == B.OK     # empty: no-op
+    assert X(null, null, 256, 1, 1, 64, 256, null, null, null, 9, null) == B.EINVAL  # out dtype
+    assert X(fake, fake, 192, 1, 1, 64, 192, fake, fake, fake, 0, null) == B.ESHAPE  # K % 128
+    assert X(fake, fake, 256, 257, 1, 64, 256, fake, fake, fake, 0, null) == B.ESHAPE  # M > 256
+    assert X(fake, fake, 8320, 1, 1, 64, 8320, fake, fake, fake, 0, null) == B.ESHAPE  # K > 8192
+    assert X(fake, fake, 320, 1, 1, 64, 256, fake, fake, fake, 0, null) == B.ESTRIDE   # ldq % 128
+    assert X(fake, fake, 128, 1, 1, 64, 256, fake, fake, fake, 0, null) == B.ESTRIDE   # ldq < G*K
+    assert X(fake, ctypes.c_void_p(4098), 256, 1, 1, 64, 256, fake, fake, fake, 0, null) == B.ESTRIDE
+    assert X(null, fake, 256, 1, 1, 64, 256, fake, fake, fake, 0, null) == B.EINVAL
+    # the plan picks a compiled configuration whose weight tile divides N, for every row count
+    n = B.bsfp8_mx_num_configs()
+    for M in range(1, 257):
+        for G, N in ((2, 1024), (1, 32768), (1, 5120), (4, 1024), (1, 96), (1, 32)):
+            cfg = B.bsfp8_mx_plan(M, G, N)
+            assert 0 <= cfg < n and N % B.bsfp8_mx_config_info(cfg)["NB"] == 0, (M, G, N, cfg)
+    assert lib.bsfp8_mx_plan(0, 1, 64) == B.ESHAPE
