@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--workload", default="wo_a", choices=sorted(WORKLOADS))
     p.add_argument("--m", type=int, default=None)
     p.add_argument("--split-k", type=int, default=0)
+    p.add_argument("--path", default="bf16", choices=["bf16", "mx"],
+                   help="bf16: the exact twin GEMM (default); mx: the fp8 x fp8 GEMM on MXFP8 activations")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--all", default=None, help="also time every workload and row count; write JSON lines here")
@@ -257,7 +259,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 20}), flush=True)
         return
     M = args.m or WORKLOADS[args.workload][3]
-    r = time_workload(args.workload, M, args.steps, args.warmup, args.split_k)
+    r = time_workload(args.workload, M, args.steps, args.warmup, args.split_k, path=args.path)
     G, N, K = r["G"], r["N"], r["K"]
     line = {
         "metric": METRIC,
@@ -269,18 +271,21 @@ def main():
         "ms_per_step": r["wall_us_per_call"] / 1e3,
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(r["weight_stream_gbs_wall"] / PAGES_GBS, 2) if args.workload == "wo_a" and M == 6 else None,
-        "dtype": "bf16",
+        "vs_baseline": (round(r["weight_stream_gbs_wall"] / PAGES_GBS, 2)
+                        if args.workload == "wo_a" and M == 6 and args.path == "bf16" else None),
+        "dtype": "bf16" if args.path == "bf16" else "fp8",
         "data": "synthetic",
-        "config": {"workload": r["desc"] + f"; M={M}", "M": M, "G": G, "N": N, "K": K,
+        "config": {"workload": r["desc"] + f"; M={M}" + ("; fp8 x fp8 path (MXFP8 activations)" if args.path == "mx" else ""),
+                   "path": args.path, "M": M, "G": G, "N": N, "K": K,
                    "weight_copies": r["copies"], "copy_bytes": r["copy_bytes"], "plan": r["plan"]},
         "us_per_call": round(r["wall_us_per_call"], 3),
+        "quantize_us_per_call": round(r["quantize_us"], 3) if r["quantize_us"] is not None else None,
         "pct_hbm_peak": round(100 * r["weight_stream_gbs_wall"] / HBM_PEAK_GBS, 1),
         "eager_event_us_per_call_mean": round(r["kernel_us_mean"], 3),
         "eager_event_us_per_call_median": round(r["kernel_us_median"], 3),
         "roofline": {"bound": "hbm", "achieved": round(r["algorithmic_gbs"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(r["algorithmic_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(args.workload, M),
+                     "traffic": traffic_from_profile(args.workload, M) if args.path == "bf16" else None,
                      "algorithmic_bytes_per_launch": r["algorithmic_bytes"]},
         "baseline_ref": "pages (GB10, other hardware): twin path 2.20 ms / 43 layers = 51.2 us/call at M=6",
     }
