@@ -50,7 +50,11 @@ WORKLOADS = {
                         "shared-expert down_proj, K zero-padded 576->640"),
     "lm_head": (1, 32768, 5120, 128, (118, 122), "f32",
                 "draft LM head: X bf16 [M, 5120], W e4m3 [32768, 5120] + u8 exponents [1024, 160], fp32 logits"),
+    "main_proj": (1, 1280, 5120, 16, (115, 125), "bf16",
+                  "draft main_proj shard (row-scale twin): X bf16 [M, 5120], W e4m3 [1280, 5120] + u8 exponents "
+                  "per row and 32 columns [1280, 160]"),
 }
+ROW_SCALE_WORKLOADS = {"main_proj"}
 
 
 def parse():
@@ -71,15 +75,16 @@ def parse():
     return p.parse_args()
 
 
-def algorithmic_bytes(M, G, N, K, out_bytes):
+def algorithmic_bytes(M, G, N, K, out_bytes, row_scales=False):
     w = G * N * K
-    e = G * (N // 32) * (K // 32)
+    e = G * N * (K // 32) if row_scales else G * (N // 32) * (K // 32)
     return w, e, M * G * K * 2, M * G * N * out_bytes
 
 
-def make_copies(torch, B, G, N, K, elo, ehi, n_copies, seed):
+def make_copies(torch, B, G, N, K, elo, ehi, n_copies, seed, row_scales=False):
     """Seeded synthetic weight copies on the device: e4m3 codes uniform over the finite codes,
-    exponent bytes uniform in [elo, ehi]."""
+    exponent bytes uniform in [elo, ehi] (one per 32x32 block, or per row and 32 columns)."""
+    erows = N if row_scales else N // 32
     import synthetic as S
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed)
@@ -88,7 +93,7 @@ def make_copies(torch, B, G, N, K, elo, ehi, n_copies, seed):
     for i in range(n_copies):
         idx = torch.randint(0, table.numel(), (G, N, K), generator=gen, device="cuda", dtype=torch.int32)
         qs.append(table[idx])
-        es.append(torch.randint(elo, ehi + 1, (G, N // 32, K // 32), generator=gen, device="cuda",
+        es.append(torch.randint(elo, ehi + 1, (G, erows, K // 32), generator=gen, device="cuda",
                                 dtype=torch.int32).to(torch.uint8))
         del idx
     return qs, es
@@ -126,15 +131,19 @@ def time_workload(name, M, steps, warmup, split_k=0, path="bf16"):
     import synthetic as S
 
     G, N, K, _, (elo, ehi), out, desc = WORKLOADS[name]
+    row_scales = name in ROW_SCALE_WORKLOADS
     out_bytes = 4 if out == "f32" else 2
-    w_b, e_b, x_b, y_b = algorithmic_bytes(M, G, N, K, out_bytes)
+    w_b, e_b, x_b, y_b = algorithmic_bytes(M, G, N, K, out_bytes, row_scales)
     if path == "mx":
         x_b = M * G * K + M * G * K // 32             # e4m3 codes + scale bytes
     copy_bytes = w_b + e_b
     n_copies = max(4, min(steps, math.ceil(COLD_BYTES / copy_bytes)))
-    qs, es = make_copies(torch, B, G, N, K, elo, ehi, n_copies, seed=7000 + M)
+    qs, es = make_copies(torch, B, G, N, K, elo, ehi, n_copies, seed=7000 + M, row_scales=row_scales)
     x = torch.from_numpy(S.bf16_normal(S.rng(7100 + M), (M, G * K)).view("int16")).view(torch.bfloat16).cuda()
-    ws = B.workspace(M, G, N, K, split_k) if path == "bf16" else None
+    if row_scales:
+        ws = B.workspace_row32(M, G, N, K, split_k)
+    else:
+        ws = B.workspace(M, G, N, K, split_k) if path == "bf16" else None
     y = torch.empty((M, G, N), dtype=torch.float32 if out == "f32" else torch.bfloat16, device="cuda")
     quant_us = None
     if path == "mx":
@@ -147,6 +156,11 @@ def time_workload(name, M, steps, warmup, split_k=0, path="bf16"):
         for i in range(20):
             B.bsfp8_quantize_mx(x, xq=xq, xs=xs)
         quant_us = graph_us(torch, lambda i: B.bsfp8_quantize_mx(x, xq=xq, xs=xs), min(steps, 1000))
+    elif row_scales:
+        plan = {"row_scale_twin": True}
+
+        def call(i):
+            B.bsfp8_gemm_row32(x, qs[i % n_copies], es[i % n_copies], split_k=split_k, ws=ws, out=y, out_dtype=out)
     else:
         plan = B.bsfp8_plan_info(M, G, N, K, split_k)
 
@@ -301,6 +315,11 @@ def main():
                 rr = time_workload(name, m, st, 50)
                 rows.append(rr)
                 print(json.dumps(rr), file=sys.stderr, flush=True)
+        # the row-scale twin (one exponent per row and 32 columns) at its page's shape
+        for m in (1, 6, 16):
+            rr = time_workload("main_proj", m, 2000, 50)
+            rows.append(rr)
+            print(json.dumps(rr), file=sys.stderr, flush=True)
         # the fp8 x fp8 path (MXFP8 activations) on the same weights
         for name, ms in (("wo_a", [6]), ("wo_a_mid", [16, 64, 128, 192]), ("lm_head", [16, 64, 128])):
             for m in ms:

@@ -41,6 +41,10 @@ _SIGS = {
     "bsfp8_plan_info": (_I, [_I64, _I64, _I64, _I64, _I, _I, ctypes.POINTER(_I)]),
     "bsfp8_workspace_bytes_config": (_SZ, [_I64, _I64, _I64, _I64, _I, _I]),
     "bsfp8_gemm_config": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _I, _P, _SZ, _P, _I, _P]),
+    "bsfp8_make_twin_row32": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, ctypes.POINTER(_I64), _P]),
+    "bsfp8_workspace_bytes_row32": (_SZ, [_I64, _I64, _I64, _I64, _I]),
+    "bsfp8_gemm_row32": (_I, _GEMM_ARGS),
+    "bsfp8_gemm_row32_config": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _I, _P, _SZ, _P, _I, _P]),
     "bsfp8_quantize_mx": (_I, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "bsfp8_gemm_mx": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _I, _P]),
     "bsfp8_mx_num_configs": (_I, []),
@@ -256,9 +260,10 @@ def bsfp8_num_configs():
 
 
 def bsfp8_config_info(cfg):
-    out = (_I * 7)()
+    out = (_I * 8)()
     _check(lib().bsfp8_config_info(cfg, out), "bsfp8_config_info")
-    return dict(BM=out[0], NB=out[1], threads=out[2], CW=out[3], NWN=out[4], NWK=out[5], direct=out[6] in (1, 2, 4), kind=out[6])
+    return dict(BM=out[0], NB=out[1], threads=out[2], CW=out[3], NWN=out[4], NWK=out[5], direct=out[6] in (1, 2, 4),
+                kind=out[6], row_scales=out[7])
 
 
 def bsfp8_plan_info(M, G, N, K, split_k=0, path=2):
@@ -352,4 +357,69 @@ def bsfp8_gemm_mx_config(xq, xs, q, e, cfg, out=None, out_dtype="bf16"):
     xq, q, M, ldq, G, N, K, od, out = _mx_args(xq, xs, q, e, out, out_dtype)
     _check(lib().bsfp8_gemm_mx_config(_ptr(xq), _ptr(xs), ldq, M, G, N, K, _ptr(q), _ptr(e), cfg, _ptr(out), od,
                                       _stream(xq)), "bsfp8_gemm_mx_config")
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# twins with one exponent per row and 32 columns
+# ------------------------------------------------------------------------------------------------
+def bsfp8_make_twin_row32(w):
+    """bf16 weight [G, N, K] -> Twin(accepted, q [G,N,K] uint8, e [G,N,K/32] uint8,
+    ok [G,N,K/32] uint8, n_bad)."""
+    _need(w, torch.bfloat16, "w")
+    if w.dim() != 3:
+        raise ValueError("w must be [G, N, K]")
+    G, N, K = w.shape
+    q = torch.empty((G, N, K), dtype=torch.uint8, device=w.device)
+    e = torch.empty((G, N, K // 32), dtype=torch.uint8, device=w.device)
+    ok = torch.empty((G, N, K // 32), dtype=torch.uint8, device=w.device)
+    bad = _I64(0)
+    st = _check(lib().bsfp8_make_twin_row32(_ptr(w), G, N, K, _ptr(q), _ptr(e), _ptr(ok), ctypes.byref(bad),
+                                            _stream(w)), "bsfp8_make_twin_row32")
+    return Twin(st == OK, q, e, ok, bad.value)
+
+
+def bsfp8_workspace_bytes_row32(M, G, N, K, split_k=0):
+    return int(lib().bsfp8_workspace_bytes_row32(M, G, N, K, split_k))
+
+
+def workspace_row32(M, G, N, K, split_k=0, device="cuda"):
+    n = bsfp8_workspace_bytes_row32(M, G, N, K, split_k)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def bsfp8_gemm_row32(x, q, e, split_k=0, ws=None, out=None, out_dtype="bf16"):
+    """Y [M, G, N] = per group X[:, g*K:(g+1)*K] @ W_g^T with W rebuilt from a row-scale twin
+    (e [G, N, K/32]); up to 16 rows."""
+    q = _codes(q)
+    _need(q, torch.uint8, "q")
+    _need(e, torch.uint8, "e")
+    G, N, K = q.shape
+    x, M, ldx = _x_view(x)
+    od = OUT_F32 if out_dtype in ("f32", torch.float32, OUT_F32) else OUT_BF16
+    if out is None:
+        out = torch.empty((M, G, N), dtype=torch.float32 if od == OUT_F32 else torch.bfloat16, device=x.device)
+    _need(out, torch.float32 if od == OUT_F32 else torch.bfloat16, "out")
+    if ws is None:
+        n = bsfp8_workspace_bytes_row32(max(M, 1), G, N, K, split_k)
+        ws = torch.zeros(n, dtype=torch.uint8, device=x.device) if n else None
+    wsb = ws.numel() if ws is not None else 0
+    _check(lib().bsfp8_gemm_row32(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), split_k, _ptr(ws), wsb, _ptr(out), od,
+                                  _stream(x)), "bsfp8_gemm_row32")
+    return out
+
+
+def bsfp8_gemm_row32_config(x, q, e, cfg, cps, ws=None, out=None, out_dtype="bf16"):
+    q = _codes(q)
+    G, N, K = q.shape
+    x, M, ldx = _x_view(x)
+    od = OUT_F32 if out_dtype in ("f32", torch.float32, OUT_F32) else OUT_BF16
+    if out is None:
+        out = torch.empty((M, G, N), dtype=torch.float32 if od == OUT_F32 else torch.bfloat16, device=x.device)
+    if ws is None:
+        n = bsfp8_workspace_bytes_config(max(M, 1), G, N, K, cfg, cps)
+        ws = torch.zeros(n, dtype=torch.uint8, device=x.device) if n else None
+    wsb = ws.numel() if ws is not None else 0
+    _check(lib().bsfp8_gemm_row32_config(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), cfg, cps, _ptr(ws), wsb,
+                                         _ptr(out), od, _stream(x)), "bsfp8_gemm_row32_config")
     return out

@@ -148,6 +148,26 @@ int bsfp8_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t*
   return bad ? BSFP8_NOT_EXACT : BSFP8_OK;
 }
 
+int bsfp8_make_twin_row32(const uint16_t* w, int64_t G, int64_t N, int64_t K, uint8_t* q_out, uint8_t* e_out,
+                          uint8_t* block_ok, int64_t* n_bad_out, void* stream) {
+  if (G < 0 || N < 0 || K < 0 || K % 32) return BSFP8_ESHAPE;
+  if (n_bad_out) *n_bad_out = 0;
+  if (G * N * K == 0) return BSFP8_OK;
+  if (!w || !q_out || !e_out) return BSFP8_EINVAL;
+  if (!aligned16(w) || !aligned16(q_out)) return BSFP8_ESTRIDE;
+  hipStream_t s = as_stream(stream);
+  Counter c;
+  int st = c.init(s);
+  if (st != BSFP8_OK) return st;
+  st = launch_make_twin_row32(w, G, N, K, q_out, e_out, block_ok, c.dev, s);
+  if (st != BSFP8_OK) return st;
+  unsigned long long bad = 0;
+  st = c.read(s, &bad);
+  if (st != BSFP8_OK) return st;
+  if (n_bad_out) *n_bad_out = (int64_t)bad;
+  return bad ? BSFP8_NOT_EXACT : BSFP8_OK;
+}
+
 int bsfp8_pad_k_weight(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
                        int64_t K_pad, uint8_t* q_pad, uint8_t* e_pad, void* stream) {
   if (G < 0 || N < 0 || K < 0 || N % 32 || K % 32 || K_pad % 32 || K_pad < K) return BSFP8_ESHAPE;
@@ -207,6 +227,41 @@ int bsfp8_gemm(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, 
   return run_gemm(path, 256, x, ldx, M, G, N, K, q, e, split_k, ws, ws_bytes, y, out_dtype, stream);
 }
 
+size_t bsfp8_workspace_bytes_row32(int64_t M, int64_t G, int64_t N, int64_t K, int split_k) {
+  if (M <= 0 || M > 16 || G < 1 || N < 32 || K < 128 || N % 32 || K % 128 || split_k < 0 || split_k > 64) return 0;
+  if (G > 4096 || N > (1 << 24) || K > (1 << 24)) return 0;
+  GemmShape s{G * K, (int)M, (int)G, (int)N, (int)K};
+  GemmPlan p;
+  return plan_gemm_row32(s, split_k, &p) == BSFP8_OK ? p.ws_bytes : 0;
+}
+
+int bsfp8_gemm_row32(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                     const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes, void* y,
+                     int out_dtype, void* stream) {
+  GemmShape s;
+  int st = check_gemm(x, ldx, M, G, N, K, q, e, y, out_dtype, split_k, 16, &s);
+  if (st != BSFP8_OK || M == 0) return st;
+  GemmPlan p;
+  st = plan_gemm_row32(s, split_k, &p);
+  if (st != BSFP8_OK) return st;
+  if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned16(ws))) return BSFP8_EWORKSPACE;
+  return launch_gemm(s, p, x, q, e, ws, y, out_dtype == BSFP8_OUT_F32, as_stream(stream));
+}
+
+int bsfp8_gemm_row32_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                            const uint8_t* q, const uint8_t* e, int cfg, int cps, void* ws, size_t ws_bytes,
+                            void* y, int out_dtype, void* stream) {
+  if (!gemm_config_row_scales(cfg)) return BSFP8_EINVAL;
+  GemmShape s;
+  int st = check_gemm(x, ldx, M, G, N, K, q, e, y, out_dtype, 0, 256, &s);
+  if (st != BSFP8_OK || M == 0) return st;
+  GemmPlan p;
+  st = plan_with(s, cfg, cps, &p);
+  if (st != BSFP8_OK) return st;
+  if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned16(ws))) return BSFP8_EWORKSPACE;
+  return launch_gemm(s, p, x, q, e, ws, y, out_dtype == BSFP8_OUT_F32, as_stream(stream));
+}
+
 int bsfp8_num_configs(void) { return num_gemm_configs(); }
 
 int bsfp8_config_info(int cfg, int* out) {
@@ -248,6 +303,7 @@ size_t bsfp8_workspace_bytes_config(int64_t M, int64_t G, int64_t N, int64_t K, 
 int bsfp8_gemm_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
                       const uint8_t* q, const uint8_t* e, int cfg, int cps, void* ws,
                       size_t ws_bytes, void* y, int out_dtype, void* stream) {
+  if (gemm_config_row_scales(cfg)) return BSFP8_EINVAL;       // those read [G][N][K/32] exponents
   GemmShape s;
   int st = check_gemm(x, ldx, M, G, N, K, q, e, y, out_dtype, 0, 256, &s);
   if (st != BSFP8_OK || M == 0) return st;

@@ -946,23 +946,31 @@ gemm_tile_kernel(KParams p) {
 // at or beyond M (not loaded at all) feed only output columns that are not stored. Waves along K
 // are summed through LDS in ascending order, as in the other one-pass kernels, so an output's fp32
 // sum is the same chain of chunks as in gemm_direct_kernel with the same NWK and chunks per split.
-template <int NT, int NWN, int NWK, int CW, int XR>
+// RS = 1 takes one exponent byte per weight row and 32 columns (e [G][N][K/32]; page
+// "recipes/docker-images/mia-tp4/docs/tp4-adapters.md", row draft_main_proj) instead of one per
+// 32x32 block: the exponent words are then staged per weight row, nothing else changes.
+// TR = real weight rows per 16-row MFMA tile: with TR = 8 a workgroup holds half as many weight
+// rows, so a long K range still fits its LDS in one pass; the MFMA's rows 8..15 then repeat rows
+// 0..7 and their outputs are not stored.
+template <int NT, int NWN, int NWK, int CW, int XR, int RS, int TR>
 __global__ void __launch_bounds__(WAVE * NWN * NWK)
 gemm_decode_kernel(KParams p) {
   constexpr int NWAVE = NWN * NWK;
-  constexpr int NB = 16 * NT * NWN;
+  constexpr int NB = TR * NT * NWN;
+  constexpr int TG = TR * 8;                        // granules of one tile's chunk in LDS
   constexpr int PCH = NWK * CW;                     // chunks of the workgroup
   constexpr int ROWG = PCH * 16 + 1;                // granules per LDS X row (one of padding)
   constexpr int XI = XR * PCH / 4;                  // X loads: 1 KB = 4 chunks of one row
   constexpr int XPW = XI / NWAVE;
-  constexpr int WPW = CW * NT * 2;                  // weight loads per wave
-  constexpr int EROWS = NB >= 32 ? NB / 32 : 1;
+  constexpr int WPW = CW * NT * (TR / 8);           // weight loads per wave
+  constexpr int EROWS = RS ? NB : (NB >= 32 ? NB / 32 : 1);   // exponent rows staged
   static_assert(XI % NWAVE == 0 && XPW >= 1, "every wave issues the same X loads");
-  static_assert(PCH <= 64 && EROWS <= NWAVE, "one exponent load per block row");
+  static_assert(PCH <= 64, "one exponent word per lane and chunk");
   static_assert((XR & (XR - 1)) == 0 && XR <= 16, "X rows: a power of two up to 16");
   static_assert(XPW + WPW + 1 <= 63, "vector memory counter range");
+  static_assert(TR == 8 || TR == 16, "tile rows");
   __shared__ uint4 x_lds[XR * ROWG];
-  __shared__ uint4 w_lds[NWAVE * CW * NT * 128];
+  __shared__ uint4 w_lds[NWAVE * CW * NT * TG];
   __shared__ uint32_t e_lds[EROWS * 64];
   __shared__ f32x4_t red[NWK > 1 ? (NWK - 1) * NWN * NT * WAVE : 1];
 
@@ -990,11 +998,14 @@ gemm_decode_kernel(KParams p) {
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.q, 0, (int)p.q_bytes, RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((void*)p.e, 0, (int)p.e_bytes, RSRC_WORD3);
 
-  // (1) exponent words: wave er loads block row er, lane l the word of chunk c_begin + l
-  if (wave < EROWS) {
+  // (1) exponent words: wave w loads exponent rows w, w + NWAVE, ... (block rows, or weight rows
+  //     with RS), lane l the word of chunk c_begin + l. The count may differ between waves: these
+  //     loads come first, and the waits below count only the weight loads issued after them.
+  for (int er = wave; er < EROWS; er += NWAVE) {
     const int c = c_begin + lane;
-    const uint32_t off = (uint32_t)((g * (N / 32) + n0 / 32 + wave) * KB + c * 4);
-    lds_load4(re, lds_addr(e_lds + wave * 64), c < c_end ? off : OOB);
+    const int erow = RS ? g * N + n0 + er : g * (N / 32) + n0 / 32 + er;
+    const uint32_t off = (uint32_t)(erow * KB + c * 4);
+    lds_load4(re, lds_addr(e_lds + er * 64), c < c_end ? off : OOB);
   }
   // (2) X rows m0 .. m0+XR-1 over the workgroup's chunks: load i covers row i / (PCH/4), granules
   //     64*(i % (PCH/4)) .. +63 of the row's range. Rows at or beyond M are not loaded (the waits
@@ -1008,23 +1019,23 @@ gemm_decode_kernel(KParams p) {
     const uint32_t off = (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K + k) * 2);
     if (m < M) lds_load16(rx, lds_addr(x_lds + row * ROWG + pc * 64), k < c_end * KCH ? off : OOB);
   }
-  // (3) this wave's weight chunks: load (j, ts, v) covers rows 8v .. 8v+7 of its 16-row tile ts,
-  //     the lane fills row R = 8v + lane/8, slot lane%8 with granule (lane%8) ^ (R/2 % 8)
-  uint4* const wbase = w_lds + wave * CW * NT * 128;
+  // (3) this wave's weight chunks: load (j, ts, v) covers rows 8v .. 8v+7 of its tile ts (TR
+  //     rows), the lane fills row R = 8v + lane/8, slot lane%8 with granule (lane%8) ^ (R/2 % 8)
+  uint4* const wbase = w_lds + wave * CW * NT * TG;
   {
     const int R0 = lane >> 3;
-    const uint32_t qrow = (uint32_t)(g * N + n0 + wn * 16 * NT + R0) * (uint32_t)K;
+    const uint32_t qrow = (uint32_t)(g * N + n0 + wn * TR * NT + R0) * (uint32_t)K;
 #pragma unroll
     for (int j = 0; j < CW; ++j) {
       const int c = c_begin + wk + j * NWK;
 #pragma unroll
       for (int ts = 0; ts < NT; ++ts)
 #pragma unroll
-        for (int v = 0; v < 2; ++v) {
+        for (int v = 0; v < TR / 8; ++v) {
           const int R = 8 * v + R0;
           const int gsrc = (lane & 7) ^ ((R >> 1) & 7);
-          const uint32_t off = qrow + (uint32_t)((ts * 16 + 8 * v) * K + c * KCH + gsrc * 16);
-          lds_load16_stream(rq, lds_addr(wbase + (j * NT + ts) * 128 + v * 64), c < c_end ? off : OOB);
+          const uint32_t off = qrow + (uint32_t)((ts * TR + 8 * v) * K + c * KCH + gsrc * 16);
+          lds_load16_stream(rq, lds_addr(wbase + (j * NT + ts) * TG + v * 64), c < c_end ? off : OOB);
         }
     }
   }
@@ -1037,7 +1048,8 @@ gemm_decode_kernel(KParams p) {
   for (int ts = 0; ts < NT; ++ts) acc[ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint4* xrow = x_lds + (r16 & (XR - 1)) * ROWG;   // rows beyond XR feed unused columns
   const uint8_t* eb = reinterpret_cast<const uint8_t*>(e_lds);
-  const int wsw = (r16 >> 1) & 7;
+  const int wr = r16 & (TR - 1);                   // the weight row this lane reads (rows TR..15
+  const int wsw = (wr >> 1) & 7;                    // of a half tile repeat rows 0..7)
   auto chunk = [&](int j) {
     const int cl = wk + j * NWK;                    // chunk index inside the workgroup
     // (a chunk past the range was not loaded: its LDS holds nothing defined)
@@ -1048,10 +1060,10 @@ gemm_decode_kernel(KParams p) {
     const bf16x8_t x3 = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 9 + 2 * q4]);
 #pragma unroll
     for (int ts = 0; ts < NT; ++ts) {
-      const int er = (n0 + wn * 16 * NT + ts * 16 + r16) / 32 - n0 / 32;
+      const int er = RS ? wn * TR * NT + ts * TR + wr : (n0 + wn * TR * NT + ts * TR + wr) / 32 - n0 / 32;
       const float sc0 = block_scale(eb[er * 256 + cl * 4 + (q4 >> 1)]);
       const float sc1 = block_scale(eb[er * 256 + cl * 4 + 2 + (q4 >> 1)]);
-      const uint4* wt = wbase + (j * NT + ts) * 128 + r16 * 8;
+      const uint4* wt = wbase + (j * NT + ts) * TG + wr * 8;
       const uint4 a = wt[q4 ^ wsw], b = wt[(4 + q4) ^ wsw];
       f32x4_t c = acc[ts];
       c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(a.x, a.y, sc0), x0, c, 0, 0, 0);
@@ -1061,15 +1073,16 @@ gemm_decode_kernel(KParams p) {
       acc[ts] = c;
     }
   };
-  wait_vmcnt_le<(CW - 1) * NT * 2>();
+  constexpr int WPC = NT * (TR / 8);                // weight loads per chunk
+  wait_vmcnt_le<(CW - 1) * WPC>();
   chunk(0);
-  if constexpr (CW > 1) { wait_vmcnt_le<(CW - 2 >= 0 ? CW - 2 : 0) * NT * 2>(); chunk(1); }
-  if constexpr (CW > 2) { wait_vmcnt_le<(CW - 3 >= 0 ? CW - 3 : 0) * NT * 2>(); chunk(2); }
-  if constexpr (CW > 3) { wait_vmcnt_le<(CW - 4 >= 0 ? CW - 4 : 0) * NT * 2>(); chunk(3); }
-  if constexpr (CW > 4) { wait_vmcnt_le<(CW - 5 >= 0 ? CW - 5 : 0) * NT * 2>(); chunk(4); }
-  if constexpr (CW > 5) { wait_vmcnt_le<(CW - 6 >= 0 ? CW - 6 : 0) * NT * 2>(); chunk(5); }
-  if constexpr (CW > 6) { wait_vmcnt_le<(CW - 7 >= 0 ? CW - 7 : 0) * NT * 2>(); chunk(6); }
-  if constexpr (CW > 7) { wait_vmcnt_le<(CW - 8 >= 0 ? CW - 8 : 0) * NT * 2>(); chunk(7); }
+  if constexpr (CW > 1) { wait_vmcnt_le<(CW - 2 >= 0 ? CW - 2 : 0) * WPC>(); chunk(1); }
+  if constexpr (CW > 2) { wait_vmcnt_le<(CW - 3 >= 0 ? CW - 3 : 0) * WPC>(); chunk(2); }
+  if constexpr (CW > 3) { wait_vmcnt_le<(CW - 4 >= 0 ? CW - 4 : 0) * WPC>(); chunk(3); }
+  if constexpr (CW > 4) { wait_vmcnt_le<(CW - 5 >= 0 ? CW - 5 : 0) * WPC>(); chunk(4); }
+  if constexpr (CW > 5) { wait_vmcnt_le<(CW - 6 >= 0 ? CW - 6 : 0) * WPC>(); chunk(5); }
+  if constexpr (CW > 6) { wait_vmcnt_le<(CW - 7 >= 0 ? CW - 7 : 0) * WPC>(); chunk(6); }
+  if constexpr (CW > 7) { wait_vmcnt_le<(CW - 8 >= 0 ? CW - 8 : 0) * WPC>(); chunk(7); }
   static_assert(CW <= 8, "chunks per wave");
 
   // (5) waves along K: ascending-order sum through LDS
@@ -1087,12 +1100,12 @@ gemm_decode_kernel(KParams p) {
   }
   // (6) output
   const int m = m0 + r16;
-  const bool mrow = r16 < XR && m < M;
+  const bool mrow = r16 < XR && m < M && q4 * 4 < TR;   // a real X row and a real weight row
   if (p.splits == 1) {
     if (mrow) {
 #pragma unroll
       for (int ts = 0; ts < NT; ++ts) {
-        const int n = n0 + wn * 16 * NT + ts * 16 + q4 * 4;
+        const int n = n0 + wn * TR * NT + ts * TR + q4 * 4;
         const size_t o = ((size_t)m * G + g) * N + n;
         const f32x4_t v = acc[ts];
         if (p.out_f32) {
@@ -1114,7 +1127,7 @@ gemm_decode_kernel(KParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       v[ts * 4 + r] = acc[ts][r];
-      off[ts * 4 + r] = ((size_t)m * G + g) * N + n0 + wn * 16 * NT + ts * 16 + q4 * 4 + r;
+      off[ts * 4 + r] = ((size_t)m * G + g) * N + n0 + wn * TR * NT + ts * TR + q4 * 4 + r;
       live[ts * 4 + r] = mrow;
     }
   combine_splits<NV>(p, s, v, off, live);
@@ -1382,12 +1395,15 @@ struct Config {
                                          // DECODE: MT = X rows
   KernelFn fn;
   int kind;                              // DIRECT, ROWS and DECODE kernels make one pass
+  int row_scales = 0;                    // 1: exponents per weight row and 32 columns
+  int TR = 16;                           // DECODE: real weight rows per 16-row MFMA tile (8 or 16)
 };
 
 #define CFG(MT, NT, NWN, NWK, CW) {MT, NT, 1, NWN, NWK, CW, gemm_kernel<MT, NT, NWN, NWK, CW>, STAGED}
 #define DCFG(NT, NWN, NWK, CW) {1, NT, 1, NWN, NWK, CW, gemm_direct_kernel<NT, NWN, NWK, CW>, DIRECT}
 #define RCFG(MT, NT, NWK, CW, D) {MT, NT, 1, 1, NWK, CW, gemm_rows_kernel<MT, NT, NWK, CW, D>, ROWS}
-#define ECFG(NT, NWN, NWK, CW, XR) {XR, NT, 1, NWN, NWK, CW, gemm_decode_kernel<NT, NWN, NWK, CW, XR>, DECODE}
+#define ECFG(NT, NWN, NWK, CW, XR) {XR, NT, 1, NWN, NWK, CW, gemm_decode_kernel<NT, NWN, NWK, CW, XR, 0, 16>, DECODE, 0, 16}
+#define ERCFG(NT, NWN, NWK, CW, XR, TR) {XR, NT, 1, NWN, NWK, CW, gemm_decode_kernel<NT, NWN, NWK, CW, XR, 1, TR>, DECODE, 1, TR}
 #define TCFG(MT, NT, NWM, NWN, D, GI) {MT, NT, NWM, NWN, 1, D, gemm_tile_kernel<MT, NT, NWM, NWN, D, GI>, TILE}
 #define SCFG(MT, NT, NWM, NWN, NWK, S) {MT, NT, NWM, NWN, NWK, S, gemm_slab_kernel<MT, NT, NWM, NWN, NWK, S>, SLAB}
 
@@ -1468,6 +1484,12 @@ const Config kConfigs[] = {
     SCFG(1, 1, 1, 4, 2, 3),   // 73 slab: 16 x 64, 8 waves (4 along N x 2 along K), 3 stages
     SCFG(1, 1, 2, 2, 1, 3),   // 74 slab: 32 x 32, 4 waves (2 x 2), 3 stages
     SCFG(1, 2, 1, 2, 4, 3),   // 75 slab: 16 x 64, 8 waves (2 along N x 4 along K), 3 stages
+    // exponents per weight row and 32 columns (row-scale twins)
+    ERCFG(1, 1, 8, 4, 8, 16),   // 76 decode: 8 rows of X x 16 weight rows, 8 waves along K x 4 chunks
+    ERCFG(1, 1, 4, 2, 8, 16),   // 77 decode: 4 waves along K x 2 chunks
+    ERCFG(1, 1, 4, 4, 16, 16),  // 78 decode: 16 rows of X, 4 waves along K x 4 chunks
+    ERCFG(1, 1, 8, 2, 16, 16),  // 79 decode: 16 rows of X, 8 waves along K x 2 chunks
+    ERCFG(1, 1, 8, 5, 8, 8),    // 80 decode: 8 weight rows, 8 waves along K x 5 chunks (40 in one pass)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1485,13 +1507,18 @@ int gemm_config_info(int cfg, int* out) {
   if (cfg < 0 || cfg >= kNumConfigs) return BSFP8_EINVAL;
   const Config& c = kConfigs[cfg];
   out[0] = c.kind == DECODE ? c.MT : 16 * c.MT * c.NWM;
-  out[1] = 16 * c.NT * c.NWN;
+  out[1] = c.TR * c.NT * c.NWN;
   out[2] = WAVE * c.NWM * c.NWN * c.NWK;
   out[3] = c.CW;
   out[4] = c.NWN;
   out[5] = c.NWK;
   out[6] = c.kind;
+  out[7] = c.row_scales;
   return BSFP8_OK;
+}
+
+int gemm_config_row_scales(int cfg) {
+  return cfg >= 0 && cfg < kNumConfigs ? kConfigs[cfg].row_scales : 0;
 }
 
 // Plan for an explicit configuration and chunks-per-split.
@@ -1501,7 +1528,7 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   GemmPlan p{};
   p.cfg = cfg;
   p.BM = c.kind == DECODE ? c.MT : 16 * c.MT * c.NWM;
-  p.NB = 16 * c.NT * c.NWN;
+  p.NB = c.TR * c.NT * c.NWN;
   if (s.N % p.NB) return BSFP8_ESHAPE;
   p.kchunks = (s.K + KCH - 1) / KCH;
   if (p.kchunks == 0) p.kchunks = 1;
@@ -1601,6 +1628,24 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
   return plan_with(s, 2, cps, plan);
 }
 
+// Built-in choice for weights with one exponent per row and 32 columns (a GEMV for up to 16
+// rows, page "recipes/docker-images/mia-tp4/docs/tp4-adapters.md", row draft_main_proj): the
+// decode kernel with row exponents and 8 rows of X per workgroup, with the waves and chunks the
+// 32x32 plan uses for decode rows (so replicated block exponents give bitwise its results) up to
+// 32 chunks; 33..40 chunks (K = 5120, the page's shape) run in one pass on half tiles; longer K
+// is split over workgroups (the pairwise exchange combines the splits).
+int plan_gemm_row32(const GemmShape& s, int split_k, GemmPlan* plan) {
+  if (s.K % KCH != 0 || s.M > 16) return BSFP8_ESHAPE;
+  const int kchunks = s.K / KCH;
+  // 4 waves x 2 chunks, or 8 waves x 4 chunks; from 33 to 40 chunks, 8 waves x 5 chunks on
+  // half tiles (8 weight rows per workgroup), which keeps the whole range in one pass
+  const int cfg = kchunks <= 8 ? 77 : kchunks <= 32 ? 76 : kchunks <= 40 ? 80 : 76;
+  const int cap = kchunks <= 8 ? 8 : kchunks <= 32 ? 32 : kchunks <= 40 ? 40 : 32;
+  int cps = kchunks < cap ? kchunks : cap;
+  if (split_k > 0) cps = (kchunks + split_k - 1) / split_k;
+  return plan_with(s, cfg, cps, plan);
+}
+
 int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,
                 const uint8_t* e, void* ws, void* y, int out_f32, hipStream_t stream) {
   KParams k{};
@@ -1612,7 +1657,8 @@ int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const 
   k.ldx = s.ldx;
   const int64_t xb = ((int64_t)(s.M - 1) * s.ldx + (int64_t)s.G * s.K) * 2;
   const int64_t qb = (int64_t)s.G * s.N * s.K;
-  const int64_t eb = (int64_t)s.G * (s.N / 32) * (s.K / 32);
+  const int64_t eb = kConfigs[p.cfg].row_scales ? (int64_t)s.G * s.N * (s.K / 32)
+                                                 : (int64_t)s.G * (s.N / 32) * (s.K / 32);
   if (xb >= (int64_t)OOB || qb >= (int64_t)OOB || eb >= (int64_t)OOB) return BSFP8_ESHAPE;
   k.x_bytes = (uint32_t)xb;
   k.q_bytes = (uint32_t)qb;

@@ -33,6 +33,10 @@ enum Path { PATH_SMALL = 0, PATH_MID = 1 };
 int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan);
 // Plan for an explicit configuration index and chunks per split.
 int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan);
+// Plan for weights with one exponent per row and 32 columns (M <= 16, K % 128 == 0).
+int plan_gemm_row32(const GemmShape& s, int split_k, GemmPlan* plan);
+// 1 when configuration `cfg` reads exponents per row and 32 columns.
+int gemm_config_row_scales(int cfg);
 int num_gemm_configs();
 // BM, NB, threads, chunks per wave per pass of a configuration.
 int gemm_config_info(int cfg, int* out);
@@ -43,6 +47,8 @@ int launch_scales_from_f32(const float* s, int64_t n, uint8_t* out, unsigned lon
                            hipStream_t stream);
 int launch_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t* q, uint8_t* e,
                      uint8_t* ok, unsigned long long* bad, hipStream_t stream);
+int launch_make_twin_row32(const uint16_t* w, int64_t G, int64_t N, int64_t K, uint8_t* q, uint8_t* e,
+                           uint8_t* ok, unsigned long long* bad, hipStream_t stream);
 int launch_pad_k_weight(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
                         int64_t K_pad, uint8_t* q_pad, uint8_t* e_pad, hipStream_t stream);
 int launch_pad_k_input(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t K,

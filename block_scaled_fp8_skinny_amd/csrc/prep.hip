@@ -108,6 +108,74 @@ __global__ void __launch_bounds__(256) make_twin_kernel(const uint16_t* w, int64
 }
 
 // ---------------------------------------------------------------------------------------------
+// Twin encoder with one exponent per row and 32 columns (page "recipes/docker-images/mia-tp4/
+// docs/tp4-adapters.md", row draft_main_proj: e4m3 with per-(row, 32-column) power-of-two
+// scales, checked to reproduce the weight exactly). The per-block rule is the 32x32 encoder's.
+// Two lanes per 1x32 block, sixteen values each; a block's 64 bytes are contiguous, so lane t
+// reads values 16t .. 16t + 15 of the flat weight.
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) make_twin_row32_kernel(const uint16_t* w, int64_t nblocks, uint8_t* q,
+                                                              uint8_t* e, uint8_t* okv, unsigned long long* bad) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t blk = t >> 1;
+  const bool live = blk < nblocks;
+  uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+  if (live) {
+    const uint4* src = reinterpret_cast<const uint4*>(w + t * 16);
+    v0 = src[0];
+    v1 = src[1];
+  }
+  const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t h[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[2 * i] = d[i] & 0xFFFF;
+    h[2 * i + 1] = d[i] >> 16;
+  }
+  uint32_t amax = 0, nonfinite = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t m = h[i] & 0x7FFF;
+    nonfinite |= m >= 0x7F80 ? 1u : 0u;
+    amax = m > amax ? m : amax;
+  }
+  // the two lanes of a block are adjacent in the wave
+  const uint32_t o = (uint32_t)__shfl_xor((int)amax, 1);
+  amax = o > amax ? o : amax;
+  nonfinite |= (uint32_t)__shfl_xor((int)nonfinite, 1);
+  const int eb = block_exp(amax);
+  const uint32_t eb_byte = (uint32_t)(eb + 127);
+  const float back_scale = __uint_as_float(eb_byte << 23);   // factor 2^e for the rebuild
+  uint32_t codes[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) codes[i] = e4m3_rne(ldexpf(__uint_as_float(h[i] << 16), -eb));
+  uint32_t same = 1;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[i] | (codes[i + 1] << 8),
+                                                                back_scale, false);
+    const uint32_t rb2 = bits_of(r);
+    same &= ((rb2 & 0xFFFF) == h[i]) && ((rb2 >> 16) == h[i + 1]) ? 1u : 0u;
+  }
+  same &= (uint32_t)__shfl_xor((int)same, 1);
+  const bool ok = same && !nonfinite;
+  uint32_t packed[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    packed[i] = codes[4 * i] | (codes[4 * i + 1] << 8) | (codes[4 * i + 2] << 16) | (codes[4 * i + 3] << 24);
+  uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  if (nonfinite) out = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  if (live) {
+    *reinterpret_cast<uint4*>(q + t * 16) = out;
+    if ((t & 1) == 0) {
+      e[blk] = nonfinite ? (uint8_t)255 : (uint8_t)eb_byte;
+      if (okv) okv[blk] = ok ? 1 : 0;
+      if (!ok) atomicAdd(bad, 1ull);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // K padding of a twin (page "shared_pad_k.py", _pad_weight): zero codes, unit exponents.
 // One thread per 16 codes of the padded weight; one thread per padded exponent byte.
 // ---------------------------------------------------------------------------------------------
@@ -197,6 +265,16 @@ int launch_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t
   if (nblocks == 0) return BSFP8_OK;
   hipLaunchKernelGGL(make_twin_kernel, dim3(grid_for(nblocks, 4)), dim3(256), 0, stream, w, R / 32,
                      D / 32, D, nblocks, q, e, ok, bad);
+  return hip_status(hipGetLastError());
+}
+
+int launch_make_twin_row32(const uint16_t* w, int64_t G, int64_t N, int64_t K, uint8_t* q, uint8_t* e,
+                           uint8_t* ok, unsigned long long* bad, hipStream_t stream) {
+  const int64_t nblocks = G * N * (K / 32);
+  if (nblocks == 0) return BSFP8_OK;
+  const int64_t threads = nblocks * 2;
+  hipLaunchKernelGGL(make_twin_row32_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, w,
+                     nblocks, q, e, ok, bad);
   return hip_status(hipGetLastError());
 }
 

@@ -96,6 +96,21 @@ BSFP8_API int bsfp8_scales_from_f32(const float* scales, int64_t rows, int64_t c
 BSFP8_API int bsfp8_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t* q_out,
                     uint8_t* e_out, uint8_t* block_ok, int64_t* n_bad_out, void* stream);
 
+/* bf16 weight -> e4m3 twin with one exponent per row and 32 columns, accepted only when it rebuilds
+ * the weight bit for bit. Page "recipes/docker-images/mia-tp4/docs/tp4-adapters.md", row
+ * draft_main_proj: each rank keeps its output columns as e4m3 with per-(row, 32-column)
+ * power-of-two scales, checked to reproduce the weight exactly. The per-block rule is the one of
+ * bsfp8_make_twin, applied to 1x32 blocks.
+ *   w        : uint16_t bf16 [G][N][K] (device, 16-byte aligned), K a multiple of 32.
+ *   q_out    : uint8_t [G][N][K] (device, 16-byte aligned).
+ *   e_out    : uint8_t [G][N][K/32] (device), byte = e + 127 (255 for a block holding inf or NaN).
+ *   block_ok : uint8_t [G][N][K/32] (device, nullable): 1 exact, 0 not.
+ *   n_bad_out: host, nullable: number of blocks that are not exact.
+ * Returns BSFP8_OK when every block is exact, BSFP8_NOT_EXACT otherwise; outputs are written in
+ * both cases. */
+BSFP8_API int bsfp8_make_twin_row32(const uint16_t* w, int64_t G, int64_t N, int64_t K, uint8_t* q_out,
+                                    uint8_t* e_out, uint8_t* block_ok, int64_t* n_bad_out, void* stream);
+
 /* Pad the contraction dimension of a twin: codes [G][N][K] -> [G][N][K_pad] with zero codes,
  * exponents [G][N/32][K/32] -> [G][N/32][K_pad/32] with byte 127 (factor 1.0).
  * Page "shared_pad_k.py", module docstring (WHAT THE PATCH DOES, item 1) and _pad_weight: the
@@ -153,6 +168,17 @@ BSFP8_API int bsfp8_gemm_mid(const uint16_t* x, int64_t ldx, int64_t M, int64_t 
 BSFP8_API int bsfp8_gemm(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
                const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes,
                void* y, int out_dtype, void* stream);
+
+/* The GEMM on a twin with one exponent per row and 32 columns (bsfp8_make_twin_row32): the GEMV
+ * of page "recipes/docker-images/mia-tp4/docs/tp4-adapters.md", row draft_main_proj, for up to
+ * 16 rows. W[g][n][k] = bf16(e4m3(q[g][n][k]) * 2^(e[g][n][k/32] - 127)); otherwise arguments,
+ * layouts, summation order and errors as bsfp8_gemm, with 1 <= M <= 16 (0 is a no-op) and
+ * K % 128 == 0. The workspace (exchange slots when K is split over workgroups) is sized by
+ * bsfp8_workspace_bytes_row32 and must be zero-filled once after allocation. */
+BSFP8_API size_t bsfp8_workspace_bytes_row32(int64_t M, int64_t G, int64_t N, int64_t K, int split_k);
+BSFP8_API int bsfp8_gemm_row32(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                               const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes,
+                               void* y, int out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * MXFP8 activations and the fp8 x fp8 GEMM (W8A8; per call, asynchronous, no allocation)

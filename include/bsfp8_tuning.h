@@ -32,7 +32,9 @@ BSFP8_API int bsfp8_num_configs(void);
  * on slab boundaries). For kinds
  * 1, 2 and 4 the chunks per split must be at most out[3] * out[5]; for kind 3 at most 64. Kinds 3
  * and 4 take K in whole 128-wide chunks (K % 128 == 0).
- * Returns BSFP8_EINVAL for an unknown cfg. `out` is host memory of 7 ints. */
+ * out[7] = 1 when the configuration reads one exponent per weight row and 32 columns (it then
+ * runs only through bsfp8_gemm_row32_config). Returns BSFP8_EINVAL for an unknown cfg. `out` is
+ * host memory of 8 ints. */
 BSFP8_API int bsfp8_config_info(int cfg, int* out);
 
 /* Plan the built-in table picks. path: 0 = small, 1 = mid, 2 = what bsfp8_gemm picks.
@@ -45,10 +47,17 @@ BSFP8_API size_t bsfp8_workspace_bytes_config(int64_t M, int64_t G, int64_t N, i
 
 /* The GEMM with an explicit configuration `cfg` and `cps` 128-wide K chunks per split (the
  * number of splits is ceil(ceil(K/128) / cps)). Arguments and errors otherwise as bsfp8_gemm;
- * 1 <= M <= 256. N must be a multiple of the configuration's NB (else BSFP8_ESHAPE). */
+ * 1 <= M <= 256. N must be a multiple of the configuration's NB (else BSFP8_ESHAPE).
+ * Row-scale configurations (out[7] of bsfp8_config_info) give BSFP8_EINVAL. */
 BSFP8_API int bsfp8_gemm_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
                       const uint8_t* q, const uint8_t* e, int cfg, int cps, void* ws,
                       size_t ws_bytes, void* y, int out_dtype, void* stream);
+
+/* The same for a row-scale configuration, on a twin with one exponent per row and 32 columns
+ * (e [G][N][K/32], as bsfp8_gemm_row32); other configurations give BSFP8_EINVAL. */
+BSFP8_API int bsfp8_gemm_row32_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N,
+                                      int64_t K, const uint8_t* q, const uint8_t* e, int cfg, int cps, void* ws,
+                                      size_t ws_bytes, void* y, int out_dtype, void* stream);
 
 /* fp8 x fp8 GEMM (bsfp8_gemm_mx) configurations. out (host, 6 ints) of bsfp8_mx_config_info:
  * rows of X per workgroup, weight rows per workgroup, threads, chunks per ring stage, ring stages,

@@ -41,13 +41,19 @@ def check_bf16(y_bits, x, G, N, K, q, e, exact=None, splits=64):
     AssertionError on an element that fails both."""
     if exact is None:
         exact = oracle.gemm_exact_f64(x, G, N, K, q, e)
+    return check_bf16_exact(y_bits, exact, lambda: oracle.abs_products_sum(x, G, N, K, q, e), K, splits)
+
+
+def check_bf16_exact(y_bits, exact, absum_fn, K, splits=64):
+    """check_bf16 for a given float64 sum; absum_fn() returns sum|x*w| (computed only when an
+    element is more than one ulp away)."""
     ref = oracle.f64_to_bf16_bits(exact)
     y_bits = np.asarray(y_bits, dtype=np.uint16).reshape(ref.shape)
     dist = np.abs(ordinal(y_bits) - ordinal(ref))
     far = dist > 1
     n_clause = 0
     if far.any():
-        absum = oracle.abs_products_sum(x, G, N, K, q, e)
+        absum = absum_fn()
         yv = oracle.bf16_bits_to_f64(y_bits)
         # half an ulp of the stored bf16 value
         half_ulp = np.where(yv == 0, 2.0 ** -134,

@@ -70,7 +70,9 @@ def test_workspace_and_plans(lib):
     assert len(maps) == 1
     for cfg in range(B.bsfp8_num_configs()):
         info = B.bsfp8_config_info(cfg)
-        assert info["BM"] % 8 == 0 and info["NB"] % 16 == 0 and info["threads"] % 64 == 0
+        # weight tiles are whole 16-row MFMA tiles, or half tiles (8 rows) for row-scale twins
+        assert info["BM"] % 8 == 0 and info["threads"] % 64 == 0
+        assert info["NB"] % 16 == 0 or (info["row_scales"] and info["NB"] % 8 == 0)
 
 
 def test_plan_is_valid_for_every_shape_class(lib):
@@ -153,3 +155,24 @@ def test_mx_argument_checks_and_plans(lib):
             cfg = B.bsfp8_mx_plan(M, G, N)
             assert 0 <= cfg < n and N % B.bsfp8_mx_config_info(cfg)["NB"] == 0, (M, G, N, cfg)
     assert lib.bsfp8_mx_plan(0, 1, 64) == B.ESHAPE
+
+
+def test_row32_plans_and_checks(lib):
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(4096)
+    X = lib.bsfp8_gemm_row32
+    assert X(null, 128, 0, 1, 64, 128, null, null, 0, null, 0, null, 0, null) == B.OK          # empty
+    assert X(fake, 256, 17, 1, 64, 256, fake, fake, 0, null, 0, fake, 0, null) == B.ESHAPE     # M > 16
+    assert X(fake, 192, 2, 1, 64, 192, fake, fake, 0, null, 0, fake, 0, null) == B.ESHAPE     # K % 128
+    bad = ctypes.c_int64(0)
+    assert lib.bsfp8_make_twin_row32(null, 1, 2, 48, null, null, null, ctypes.byref(bad), null) == B.ESHAPE
+    # the page's shape (K = 5120, 40 chunks) runs in one pass: no workspace
+    for M in (1, 6, 16):
+        assert B.bsfp8_workspace_bytes_row32(M, 1, 1280, 5120) == 0
+    # a longer K is split over workgroups and needs exchange slots
+    assert B.bsfp8_workspace_bytes_row32(6, 1, 1280, 8192) > 0
+    # 32x32 configurations are refused on the row-scale entry and vice versa
+    rs = [c for c in range(B.bsfp8_num_configs()) if B.bsfp8_config_info(c)["row_scales"]]
+    assert rs
+    assert lib.bsfp8_gemm_row32_config(fake, 256, 2, 1, 64, 256, fake, fake, 54, 2, null, 0, fake, 0, null) == B.EINVAL
+    assert lib.bsfp8_gemm_config(fake, 256, 2, 1, 64, 256, fake, fake, rs[0], 2, null, 0, fake, 0, null) == B.EINVAL

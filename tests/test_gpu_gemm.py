@@ -84,6 +84,8 @@ def test_every_kernel_configuration():
     G, N = 2, 256
     for cfg in range(B.bsfp8_num_configs()):
         info = B.bsfp8_config_info(cfg)
+        if info["row_scales"]:              # these read [G][N][K/32] exponents: test_gpu_row32.py
+            continue
         K = 768 if info["kind"] in (3, 4, 5) else 800
         M = min(2 * info["BM"] - 3, 256)
         x, q, e = _inputs(400 + cfg, M, G, N, K)
