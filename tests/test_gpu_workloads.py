@@ -101,3 +101,78 @@ def test_lm_head_sampled_rows_and_batch_invariance():
     check_f32(y128, d["x"], 1, rows.size, K, q_s, e_s)
     # and the bf16 rounding of those logits under the bf16 rule
     check_bf16(oracle.f64_to_bf16_bits(y128.astype(np.float64)), d["x"], 1, rows.size, K, q_s, e_s)
+
+
+# ---- the fp8 x fp8 path and the row-scale twin at their full sizes -------------------------------
+def test_mx_path_full_sizes_and_graph_replay():
+    """The fp8 x fp8 path at the wo_a mid shape (M = 192, every output) and the LM head (M = 128,
+    sampled vocabulary blocks), in the plans the benchmark times, plus a captured graph of
+    quantizer + GEMM replayed against the eager result."""
+    import oracle.mx as MX
+    from parity import check_mx_bf16, check_mx_f32
+    # wo_a mid, 192 rows: quantizer bitwise, every output under the fp8 rule
+    d = S.wo_a(8600, 192)
+    xt = to_gpu_bf16(d["x"])
+    xq, xs = B.bsfp8_quantize_mx(xt)
+    rq, rs = MX.quantize_mx(d["x"])
+    assert np.array_equal(xq.cpu().numpy(), rq) and np.array_equal(xs.cpu().numpy(), rs)
+    qt, et = to_gpu_u8(d["q"]), to_gpu_u8(d["e"])
+    y = B.bsfp8_gemm_mx(xq, xs, qt, et)
+    exact = MX.gemm_mx_exact_f64(rq, rs, 2, 1024, 4096, d["q"], d["e"])
+    absum = MX.abs_products_sum_mx(rq, rs, 2, 1024, 4096, d["q"], d["e"])
+    print("mx wo_a_mid M=192", check_mx_bf16(bf16_bits(y), exact, absum, 4096), flush=True)
+    # graph replays of quantize + GEMM equal the eager result
+    out = torch.empty_like(y)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.bsfp8_quantize_mx(xt, xq=xq, xs=xs)
+        B.bsfp8_gemm_mx(xq, xs, qt, et, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.bsfp8_quantize_mx(xt, xq=xq, xs=xs)
+        B.bsfp8_gemm_mx(xq, xs, qt, et, out=out)
+    for i in range(4):
+        out.fill_(0)
+        xq.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), y.view(torch.int16)), i
+        B.bsfp8_gemm_mx(xq, xs, qt, et)                  # eager work between replays
+        torch.cuda.synchronize()
+    # LM head, 128 rows, fp32 logits on sampled 32-row vocabulary blocks
+    N, K = 32768, 5120
+    d = S.lm_head(8700, 128)
+    xq, xs = B.bsfp8_quantize_mx(to_gpu_bf16(d["x"]))
+    rq, rs = MX.quantize_mx(d["x"])
+    assert np.array_equal(xq.cpu().numpy(), rq) and np.array_equal(xs.cpu().numpy(), rs)
+    y = B.bsfp8_gemm_mx(xq, xs, to_gpu_u8(d["q"]), to_gpu_u8(d["e"]), out_dtype="f32").cpu().numpy()
+    blocks = [0, 5, 400, 1023]
+    rows = np.concatenate([np.arange(b * 32, b * 32 + 32) for b in blocks])
+    q_s, e_s = d["q"][:, rows], d["e"][:, blocks]
+    exact = MX.gemm_mx_exact_f64(rq, rs, 1, rows.size, K, q_s, e_s)
+    absum = MX.abs_products_sum_mx(rq, rs, 1, rows.size, K, q_s, e_s)
+    rel = check_mx_f32(y[:, :, rows], exact, absum, K)
+    print(f"mx lm_head M=128 sampled: max |err|/sum|xw| = {rel:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("M", [1, 6, 16])
+def test_row32_main_proj_full_size(M):
+    """The row-scale twin at the draft main_proj shard: a 1280 x 5120 weight built exact, encoded
+    by the GPU encoder (bitwise vs the oracle), then the GEMV at 1, 6 and 16 rows."""
+    import oracle.row32 as R
+    from parity import check_bf16_exact
+    r = S.rng(8800)
+    q = S.e4m3_codes(r, (1, 1280, 5120))
+    e = S.exponent_bytes(r, (1, 1280, 160), 115, 125)
+    w = R.dequant_bf16_row32(q, e)
+    t = B.bsfp8_make_twin_row32(to_gpu_bf16(w))
+    ref = R.make_twin_row32(w)
+    assert t.accepted and ref.accepted
+    assert np.array_equal(t.q.cpu().numpy(), ref.q) and np.array_equal(t.e.cpu().numpy(), ref.e)
+    x = S.bf16_normal(S.rng(8801 + M), (M, 5120))
+    y = B.bsfp8_gemm_row32(to_gpu_bf16(x), t.q, t.e)
+    exact = R.gemm_exact_f64_row32(x, 1, 1280, 5120, ref.q, ref.e)
+    st = check_bf16_exact(bf16_bits(y), exact, lambda: R.abs_products_sum_row32(x, 1, 1280, 5120, ref.q, ref.e), 5120)
+    print(f"main_proj M={M}: {st}", flush=True)
