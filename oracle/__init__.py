@@ -6,7 +6,8 @@ the HIP library under block_scaled_fp8_skinny_amd/, and imports nothing from it.
 
 Modules: formats (e4m3, bf16, fp32 rounding), ops (the bf16 hot path and its preparation), mx
 (MXFP8 activations and the fp8 x fp8 contraction, the next step after the hot path), row32 (the
-per-(row, 32-column) scale twin and its GEMM, another next step).
+per-(row, 32-column) scale twin and its GEMM, another next step), epilogue (the fixed-order sum of
+fp32 split partials and MXFP8 quantisation of the output).
 
 Parity status: every function here is pinned by CPU tests (tests/test_oracle_*.py) to values
 fixed by the format definitions, closed forms, invariants and exact rational brute force.
@@ -18,3 +19,4 @@ from .ops import (PAD_EXPONENT, ScaleError, Twin, abs_products_sum, block_expone
                   dequant_values, gemm, gemm_exact_f64, make_twin, pad_k_input, pad_k_weight,
                   scales_from_f32)
 from . import row32
+from . import epilogue

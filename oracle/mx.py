@@ -51,14 +51,15 @@ def mx_scale_exponent(amax):
     return np.clip(s, -127, 127)
 
 
-def quantize_mx(x_bits, L=None):
-    """bf16 bits [M, >= L] -> (codes uint8 [M, L], scale bytes uint8 [M, L/32])."""
-    x_bits = np.asarray(x_bits, dtype=np.uint16)
-    M = x_bits.shape[0]
-    L = x_bits.shape[1] if L is None else L
+def quantize_mx_values(v):
+    """float64 values [M, L] (L a multiple of 32; inf and NaN allowed) -> (codes uint8 [M, L],
+    scale bytes uint8 [M, L/32]). The values must be exact copies of the inputs (bf16 or fp32
+    values are exact in float64), so that every decision below is taken on the input itself."""
+    v = np.asarray(v, dtype=np.float64)
+    M, L = v.shape
     if L % MX_BLOCK:
         raise ValueError("L must be a multiple of 32")
-    v = F.bf16_bits_to_f64(x_bits[:, :L]).reshape(M, L // MX_BLOCK, MX_BLOCK)
+    v = v.reshape(M, L // MX_BLOCK, MX_BLOCK)
     finite = np.isfinite(v).all(axis=2)
     amax = np.where(finite, np.abs(np.where(np.isfinite(v), v, 0.0)).max(axis=2), 0.0)
     s = mx_scale_exponent(amax)                                   # [M, L/32]
@@ -70,6 +71,15 @@ def quantize_mx(x_bits, L=None):
     codes = np.where(finite[:, :, None], codes, nan_code)
     scales = np.where(finite, s + 127, SCALE_NAN).astype(np.uint8)
     return codes.reshape(M, L).astype(np.uint8), scales
+
+
+def quantize_mx(x_bits, L=None):
+    """bf16 bits [M, >= L] -> (codes uint8 [M, L], scale bytes uint8 [M, L/32])."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    L = x_bits.shape[1] if L is None else L
+    if L % MX_BLOCK:
+        raise ValueError("L must be a multiple of 32")
+    return quantize_mx_values(F.bf16_bits_to_f64(x_bits[:, :L]))
 
 
 def dequant_mx(codes, scales):

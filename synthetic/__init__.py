@@ -31,6 +31,11 @@ def bf16_normal(r, shape, scale=1.0):
     return u.astype(np.uint16)
 
 
+def f32_normal(r, shape, scale=1.0):
+    """fp32 N(0, scale^2) draws (float32 array)."""
+    return (r.standard_normal(shape, dtype=np.float32) * np.float32(scale)).astype(np.float32)
+
+
 def e4m3_codes(r, shape):
     """Uniform over the finite e4m3 codes."""
     return FINITE_E4M3_CODES[r.integers(0, FINITE_E4M3_CODES.size, size=shape)]
