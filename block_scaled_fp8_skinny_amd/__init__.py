@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libbsfp8.so")
 OK, NOT_EXACT = 0, 1
 EINVAL, ESHAPE, ESCALE, ESTRIDE, EWORKSPACE, EHIP = -1, -2, -3, -4, -5, -6
 OUT_BF16, OUT_F32 = 0, 1
+SUM_ASCENDING, SUM_PAIRWISE = 0, 1
 
 # name -> (restype, argtypes)
 _P, _I64, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -51,6 +52,11 @@ _SIGS = {
     "bsfp8_mx_config_info": (_I, [_I, ctypes.POINTER(_I)]),
     "bsfp8_mx_plan": (_I, [_I64, _I64, _I64]),
     "bsfp8_gemm_mx_config": (_I, [_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _P, _I, _P]),
+    "bsfp8_reduce_quantize_mx": (_I, [_P, _I64, _I64, _I64, _I, _P, _P, _P]),
+    "bsfp8_workspace_bytes_mxfp8": (_SZ, [_I64, _I64, _I64, _I64, _I]),
+    "bsfp8_gemm_mxfp8": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _P, _SZ, _P, _P, _P]),
+    "bsfp8_workspace_bytes_mxfp8_config": (_SZ, [_I64, _I64, _I64, _I64, _I, _I]),
+    "bsfp8_gemm_mxfp8_config": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _I, _P, _SZ, _P, _P, _P]),
 }
 
 _lib = None
@@ -423,3 +429,75 @@ def bsfp8_gemm_row32_config(x, q, e, cfg, cps, ws=None, out=None, out_dtype="bf1
     _check(lib().bsfp8_gemm_row32_config(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), cfg, cps, _ptr(ws), wsb,
                                          _ptr(out), od, _stream(x)), "bsfp8_gemm_row32_config")
     return out
+
+
+# ------------------------------------------------------------------------------------------------
+# MXFP8 output epilogue
+# ------------------------------------------------------------------------------------------------
+def _mx_out(M, L, device, yq, ys):
+    if yq is None:
+        yq = torch.empty((M, L), dtype=torch.uint8, device=device)
+    if ys is None:
+        ys = torch.empty((M, L // 32), dtype=torch.uint8, device=device)
+    _need(yq, torch.uint8, "yq")
+    _need(ys, torch.uint8, "ys")
+    if yq.numel() < M * L or ys.numel() < M * (L // 32):
+        raise ValueError("yq or ys too small")
+    return yq, ys
+
+
+def bsfp8_reduce_quantize_mx(part, order=SUM_PAIRWISE, yq=None, ys=None):
+    """fp32 partials [S, M, L] -> (codes uint8 [M, L], scale bytes uint8 [M, L/32]): the fixed-order
+    fp32 sum of the S partials, quantised to MXFP8 along L."""
+    _need(part, torch.float32, "part")
+    if part.dim() != 3:
+        raise ValueError("part must be [S, M, L]")
+    S, M, L = part.shape
+    yq, ys = _mx_out(M, L, part.device, yq, ys)
+    _check(lib().bsfp8_reduce_quantize_mx(_ptr(part), S, M, L, int(order), _ptr(yq), _ptr(ys), _stream(part)),
+           "bsfp8_reduce_quantize_mx")
+    return yq, ys
+
+
+def bsfp8_workspace_bytes_mxfp8(M, G, N, K, split_k=0):
+    return int(lib().bsfp8_workspace_bytes_mxfp8(M, G, N, K, split_k))
+
+
+def workspace_mxfp8(M, G, N, K, split_k=0, device="cuda"):
+    """A workspace tensor for bsfp8_gemm_mxfp8 (its contents need no clearing)."""
+    return torch.empty(bsfp8_workspace_bytes_mxfp8(M, G, N, K, split_k), dtype=torch.uint8, device=device)
+
+
+def bsfp8_gemm_mxfp8(x, q, e, split_k=0, ws=None, yq=None, ys=None):
+    """The GEMM of bsfp8_gemm with the MXFP8 epilogue -> (codes uint8 [M, G*N], scale bytes uint8
+    [M, G*N/32])."""
+    q = _codes(q)
+    _need(q, torch.uint8, "q")
+    _need(e, torch.uint8, "e")
+    G, N, K = q.shape
+    x, M, ldx = _x_view(x)
+    yq, ys = _mx_out(M, G * N, x.device, yq, ys)
+    if ws is None and M > 0:
+        ws = workspace_mxfp8(M, G, N, K, split_k, device=x.device)
+    wsb = ws.numel() if ws is not None else 0
+    _check(lib().bsfp8_gemm_mxfp8(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), split_k, _ptr(ws), wsb,
+                                  _ptr(yq), _ptr(ys), _stream(x)), "bsfp8_gemm_mxfp8")
+    return yq, ys
+
+
+def bsfp8_workspace_bytes_mxfp8_config(M, G, N, K, cfg, cps):
+    return int(lib().bsfp8_workspace_bytes_mxfp8_config(M, G, N, K, cfg, cps))
+
+
+def bsfp8_gemm_mxfp8_config(x, q, e, cfg, cps, ws=None, yq=None, ys=None):
+    q = _codes(q)
+    G, N, K = q.shape
+    x, M, ldx = _x_view(x)
+    yq, ys = _mx_out(M, G * N, x.device, yq, ys)
+    if ws is None and M > 0:
+        ws = torch.empty(bsfp8_workspace_bytes_mxfp8_config(M, G, N, K, cfg, cps), dtype=torch.uint8,
+                         device=x.device)
+    wsb = ws.numel() if ws is not None else 0
+    _check(lib().bsfp8_gemm_mxfp8_config(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), cfg, cps, _ptr(ws), wsb,
+                                         _ptr(yq), _ptr(ys), _stream(x)), "bsfp8_gemm_mxfp8_config")
+    return yq, ys

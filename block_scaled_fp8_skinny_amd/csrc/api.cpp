@@ -88,6 +88,16 @@ int check_gemm_mx(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int64_t M, 
   return BSFP8_OK;
 }
 
+// The GEMM into the workspace (fp32 results or split partials), then the MXFP8 epilogue.
+int run_gemm_mxfp8(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,
+                   const uint8_t* e, void* ws, size_t ws_bytes, uint8_t* yq, uint8_t* ys, hipStream_t stream) {
+  if (!ws || ws_bytes < gemm_partials_bytes(s, p) || !aligned16(ws)) return BSFP8_EWORKSPACE;
+  int st = launch_gemm(s, p, x, q, e, ws, nullptr, 1, stream, /*partials=*/1);
+  if (st != BSFP8_OK) return st;
+  return launch_reduce_quantize_mx(reinterpret_cast<const float*>(ws), p.splits, s.M, (int64_t)s.G * s.N,
+                                   gemm_partials_order(p), yq, ys, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -271,15 +281,15 @@ int bsfp8_config_info(int cfg, int* out) {
 
 int bsfp8_plan_info(int64_t M, int64_t G, int64_t N, int64_t K, int split_k, int path, int* out) {
   if (!out) return BSFP8_EINVAL;
-  if (path < 0 || path > 2) return BSFP8_EINVAL;
-  const int p_eff = path == 2 ? (M <= 8 ? PATH_SMALL : PATH_MID) : path;
+  if (path < 0 || path > 3) return BSFP8_EINVAL;
+  const int p_eff = path >= 2 ? (M <= 8 ? PATH_SMALL : PATH_MID) : path;
   const int64_t max_m = p_eff == PATH_SMALL && path != 2 ? 16 : 256;
   GemmShape s;
   int st = check_dims(M, G, N, K, split_k, max_m, &s);
   if (st != BSFP8_OK) return st;
   if (M == 0) return BSFP8_ESHAPE;
   GemmPlan p;
-  st = plan_gemm(s, p_eff, split_k, &p);
+  st = path == 3 ? plan_gemm_mxfp8(s, split_k, &p) : plan_gemm(s, p_eff, split_k, &p);
   if (st != BSFP8_OK) return st;
   out[0] = p.cfg;
   out[1] = p.BM;
@@ -350,6 +360,59 @@ int bsfp8_gemm_mx_config(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int6
   if (st != BSFP8_OK || M == 0) return st;
   return launch_gemm_mx(xq, xs, ldq, (int)M, (int)G, (int)N, (int)K, q, e, y, out_dtype == BSFP8_OUT_F32, cfg,
                         as_stream(stream));
+}
+
+int bsfp8_reduce_quantize_mx(const float* part, int64_t S, int64_t M, int64_t L, int order, uint8_t* yq,
+                             uint8_t* ys, void* stream) {
+  if (order != BSFP8_SUM_ASCENDING && order != BSFP8_SUM_PAIRWISE) return BSFP8_EINVAL;
+  if (S < 1 || S > 64) return BSFP8_EINVAL;
+  if (M < 0 || L < 32 || L % 32 || M > (1 << 24) || L > (1 << 26)) return BSFP8_ESHAPE;
+  if (M == 0) return BSFP8_OK;
+  if (S * M * L > ((int64_t)1 << 40)) return BSFP8_ESHAPE;
+  if (!part || !yq || !ys) return BSFP8_EINVAL;
+  if (!aligned16(part) || !aligned16(yq)) return BSFP8_ESTRIDE;
+  return launch_reduce_quantize_mx(part, (int)S, M, L, order, yq, ys, as_stream(stream));
+}
+
+size_t bsfp8_workspace_bytes_mxfp8(int64_t M, int64_t G, int64_t N, int64_t K, int split_k) {
+  GemmShape s;
+  if (M <= 0 || check_dims(M, G, N, K, split_k, 256, &s) != BSFP8_OK) return 0;
+  GemmPlan p;
+  return plan_gemm_mxfp8(s, split_k, &p) == BSFP8_OK ? gemm_partials_bytes(s, p) : 0;
+}
+
+int bsfp8_gemm_mxfp8(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                     const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes, uint8_t* yq,
+                     uint8_t* ys, void* stream) {
+  GemmShape s;
+  int st = check_gemm(x, ldx, M, G, N, K, q, e, yq, BSFP8_OUT_F32, split_k, 256, &s);
+  if (st != BSFP8_OK || M == 0) return st;
+  if (!ys) return BSFP8_EINVAL;
+  GemmPlan p;
+  st = plan_gemm_mxfp8(s, split_k, &p);
+  if (st != BSFP8_OK) return st;
+  return run_gemm_mxfp8(s, p, x, q, e, ws, ws_bytes, yq, ys, as_stream(stream));
+}
+
+size_t bsfp8_workspace_bytes_mxfp8_config(int64_t M, int64_t G, int64_t N, int64_t K, int cfg, int cps) {
+  GemmShape s;
+  if (M <= 0 || check_dims(M, G, N, K, 0, 256, &s) != BSFP8_OK || gemm_config_row_scales(cfg)) return 0;
+  GemmPlan p;
+  return plan_with(s, cfg, cps, &p) == BSFP8_OK ? gemm_partials_bytes(s, p) : 0;
+}
+
+int bsfp8_gemm_mxfp8_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                            const uint8_t* q, const uint8_t* e, int cfg, int cps, void* ws, size_t ws_bytes,
+                            uint8_t* yq, uint8_t* ys, void* stream) {
+  if (gemm_config_row_scales(cfg)) return BSFP8_EINVAL;
+  GemmShape s;
+  int st = check_gemm(x, ldx, M, G, N, K, q, e, yq, BSFP8_OUT_F32, 0, 256, &s);
+  if (st != BSFP8_OK || M == 0) return st;
+  if (!ys) return BSFP8_EINVAL;
+  GemmPlan p;
+  st = plan_with(s, cfg, cps, &p);
+  if (st != BSFP8_OK) return st;
+  return run_gemm_mxfp8(s, p, x, q, e, ws, ws_bytes, yq, ys, as_stream(stream));
 }
 
 }  // extern "C"

@@ -26,6 +26,8 @@ struct KParams {
   const uint8_t* e;
   void* y;
   unsigned long long* slots;             // pairwise-combine slots (splits > 1)
+  float* part;                           // non-null: each split stores its fp32 partial here,
+                                         // [splits][M][G][N], for a later kernel to sum
   int64_t ldx;
   uint32_t x_bytes, q_bytes, e_bytes;    // extents of the three buffer descriptors
   int M, G, N, K;
@@ -92,11 +94,20 @@ __device__ __forceinline__ void prefetch_args(const KParams& p) {
 // comment). v[i] is this split's partial of output i, off[i] its element index, live[i] whether
 // the lane owns it. All exchanges of one tree level are issued before any result is used, so a
 // level costs one round trip to memory. On return live[i] says whether this lane finished output
-// i (its total is then in v[i]).
+// i (its total is then in v[i]). With p.part set the tree is left to a later kernel: split s
+// stores its partials and finishes nothing.
 template <int NV>
 __device__ __forceinline__ void combine_splits(const KParams& p, int s, float (&v)[NV],
                                                const size_t (&off)[NV], bool (&live)[NV]) {
   const size_t mgn = (size_t)p.M * p.G * p.N;
+  if (p.part) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (live[i]) p.part[(size_t)s * mgn + off[i]] = v[i];
+      live[i] = false;
+    }
+    return;
+  }
   int idx = s, cnt = p.splits;
   for (int lv = 0; lv < p.levels; ++lv) {
     if ((idx ^ 1) < cnt) {

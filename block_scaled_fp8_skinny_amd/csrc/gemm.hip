@@ -1521,6 +1521,14 @@ int gemm_config_row_scales(int cfg) {
   return cfg >= 0 && cfg < kNumConfigs ? kConfigs[cfg].row_scales : 0;
 }
 
+int gemm_partials_order(const GemmPlan& p) {
+  return kConfigs[p.cfg].kind == TILE ? BSFP8_SUM_ASCENDING : BSFP8_SUM_PAIRWISE;
+}
+
+size_t gemm_partials_bytes(const GemmShape& s, const GemmPlan& p) {
+  return (size_t)p.splits * s.M * s.G * s.N * 4;
+}
+
 // Plan for an explicit configuration and chunks-per-split.
 int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   if (cfg < 0 || cfg >= kNumConfigs) return BSFP8_EINVAL;
@@ -1634,6 +1642,12 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
 // 32x32 plan uses for decode rows (so replicated block exponents give bitwise its results) up to
 // 32 chunks; 33..40 chunks (K = 5120, the page's shape) run in one pass on half tiles; longer K
 // is split over workgroups (the pairwise exchange combines the splits).
+// The MXFP8-epilogue GEMM runs the plan bsfp8_gemm would pick for the same arguments, so its
+// codes quantise exactly the fp32 outputs of that call.
+int plan_gemm_mxfp8(const GemmShape& s, int split_k, GemmPlan* plan) {
+  return plan_gemm(s, s.M <= 8 ? PATH_SMALL : PATH_MID, split_k, plan);
+}
+
 int plan_gemm_row32(const GemmShape& s, int split_k, GemmPlan* plan) {
   if (s.K % KCH != 0 || s.M > 16) return BSFP8_ESHAPE;
   const int kchunks = s.K / KCH;
@@ -1647,7 +1661,14 @@ int plan_gemm_row32(const GemmShape& s, int split_k, GemmPlan* plan) {
 }
 
 int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,
-                const uint8_t* e, void* ws, void* y, int out_f32, hipStream_t stream) {
+                const uint8_t* e, void* ws, void* y, int out_f32, hipStream_t stream, int partials) {
+  if (partials) {
+    // fp32 results for a later kernel: the sum itself with one split, else every split's partial
+    if (p.splits == 1) {
+      y = ws;
+      out_f32 = 1;
+    }
+  }
   KParams k{};
   k.x = x;
   k.q = q;
@@ -1673,6 +1694,7 @@ int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const 
   k.mblocks = p.mblocks;
   k.nblocks = p.nblocks;
   k.out_f32 = out_f32;
+  if (partials && p.splits > 1 && kConfigs[p.cfg].kind != TILE) k.part = reinterpret_cast<float*>(ws);
   k.levels = tree_levels(p.splits);
   int base = 0, lv = 0;
   for (int c2 = p.splits; c2 > 1; c2 = (c2 + 1) >> 1) {
@@ -1684,7 +1706,7 @@ int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const 
   if (nwg <= 0 || nwg > 0x7fffffffLL) return BSFP8_ESHAPE;
   k.nwg = (int)nwg;
   hipLaunchKernelGGL(c.fn, dim3((unsigned)nwg), dim3(WAVE * c.NWM * c.NWN * c.NWK), 0, stream, k);
-  if (c.kind == TILE && p.splits > 1) {
+  if (c.kind == TILE && p.splits > 1 && !partials) {
     const int64_t n4 = (int64_t)s.M * s.G * s.N / 4;
     hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
                        reinterpret_cast<const float*>(ws), y, n4, p.splits, out_f32);

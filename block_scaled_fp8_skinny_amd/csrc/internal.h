@@ -33,6 +33,8 @@ enum Path { PATH_SMALL = 0, PATH_MID = 1 };
 int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan);
 // Plan for an explicit configuration index and chunks per split.
 int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan);
+// Plan of the MXFP8-epilogue GEMM (bsfp8_gemm_mxfp8).
+int plan_gemm_mxfp8(const GemmShape& s, int split_k, GemmPlan* plan);
 // Plan for weights with one exponent per row and 32 columns (M <= 16, K % 128 == 0).
 int plan_gemm_row32(const GemmShape& s, int split_k, GemmPlan* plan);
 // 1 when configuration `cfg` reads exponents per row and 32 columns.
@@ -40,8 +42,21 @@ int gemm_config_row_scales(int cfg);
 int num_gemm_configs();
 // BM, NB, threads, chunks per wave per pass of a configuration.
 int gemm_config_info(int cfg, int* out);
+// partials != 0: leave fp32 results in ws for a later kernel instead of writing y: the result
+// itself when the plan has one split, else the partial of every split ([splits][M][G][N]), in
+// the order gemm_partials_order names.
 int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,
-                const uint8_t* e, void* ws, void* y, int out_f32, hipStream_t stream);
+                const uint8_t* e, void* ws, void* y, int out_f32, hipStream_t stream, int partials = 0);
+// Order in which a plan's own combine adds its split partials: BSFP8_SUM_ASCENDING (tile kernel
+// and its reduce kernel) or BSFP8_SUM_PAIRWISE (the one-pass kernels' exchange tree).
+int gemm_partials_order(const GemmPlan& p);
+// Workspace of launch_gemm with partials: splits * M * G * N fp32 values.
+size_t gemm_partials_bytes(const GemmShape& s, const GemmPlan& p);
+
+// The MXFP8 epilogue (epilogue.hip): fixed-order sum of S fp32 partials [S][M][L], then MXFP8
+// quantisation along L (codes [M][L], scale bytes [M][L/32]).
+int launch_reduce_quantize_mx(const float* part, int S, int64_t M, int64_t L, int order, uint8_t* yq,
+                              uint8_t* ys, hipStream_t stream);
 
 int launch_scales_from_f32(const float* s, int64_t n, uint8_t* out, unsigned long long* bad,
                            hipStream_t stream);

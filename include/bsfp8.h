@@ -219,6 +219,58 @@ BSFP8_API int bsfp8_gemm_mx(const uint8_t* xq, const uint8_t* xs, int64_t ldq, i
                             int64_t N, int64_t K, const uint8_t* q, const uint8_t* e, void* y,
                             int out_dtype, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * MXFP8 output epilogue (per call, asynchronous, no allocation)
+ *
+ * Page "recipes/docker-images/mia-tp4/adapter/wo_a_w8.py": its module docstring reports the
+ * MXFP8-epilogue path (what production runs), and in `install` the dropped-weight path and
+ * small_mx hand the fp32 split partials [S][M][G][N] of _partial_w8 to a kernel that sums them
+ * and quantises the sum to MXFP8 in one pass, where the plain path sums them with _wo_a_reduce and
+ * rounds to bf16. Neither the quantiser nor the order of that sum is printed. Here:
+ *   - the partials are added in fp32 in a fixed order (bsfp8_sum_order);
+ *   - the sum, viewed as [M][L] (L = G*N for the GEMM), is quantised per 32 consecutive values of
+ *     a row with the rule of bsfp8_quantize_mx (OCP MX v1.0: s = floor(log2 amax) - 8 clamped to
+ *     [-127, 127], e4m3 RNE with saturation at 448, scale byte s + 127; byte 255 and e4m3 NaN
+ *     codes for a block holding inf or NaN);
+ *   - codes are [M][L] and scale bytes [M][L/32], both row-major (the pages' consumer wants its
+ *     scales in a swizzled layout of its own, which is not reproduced).
+ * ------------------------------------------------------------------------------------------ */
+
+typedef enum bsfp8_sum_order {
+  BSFP8_SUM_ASCENDING = 0,  /* ((p0 + p1) + p2) + ... : the order of the page's _wo_a_reduce */
+  BSFP8_SUM_PAIRWISE = 1    /* pairwise tree over the split index: p2i + p2i+1, an unpaired last
+                               partial carried up unchanged, repeated until one value is left */
+} bsfp8_sum_order;
+
+/* Fixed-order sum of S fp32 partials and MXFP8 quantisation of the sum.
+ *   part  : float [S][M][L] (device, contiguous, 16-byte aligned).
+ *   S     : 1..64 partials (S = 1 quantises part itself).
+ *   order : a bsfp8_sum_order.
+ *   yq    : uint8_t e4m3 codes [M][L] (device, contiguous, 16-byte aligned).
+ *   ys    : uint8_t scale bytes [M][L/32] (device, contiguous).
+ * L % 32 == 0 and L >= 32; M == 0 is a no-op. Every addition is an IEEE fp32 addition and every
+ * quantisation decision an integer one, so the result is bit-exact and deterministic. */
+BSFP8_API int bsfp8_reduce_quantize_mx(const float* part, int64_t S, int64_t M, int64_t L, int order,
+                                       uint8_t* yq, uint8_t* ys, void* stream);
+
+/* Workspace bytes of bsfp8_gemm_mxfp8 for this shape and split_k (never 0 for a valid shape:
+ * the fp32 results, one copy per split, pass through it). Nothing in it needs clearing. */
+BSFP8_API size_t bsfp8_workspace_bytes_mxfp8(int64_t M, int64_t G, int64_t N, int64_t K, int split_k);
+
+/* The GEMM of bsfp8_gemm with the MXFP8 epilogue: the fp32 results of the GEMM's plan for
+ * (M, G, N, K, split_k) - the sum itself with one split, else each split's partial - go to ws,
+ * and the epilogue adds the partials in the order of that plan's own combine (pairwise for the
+ * one-pass kernels, ascending for the tile kernel), so the quantised values are exactly the fp32
+ * outputs bsfp8_gemm returns for the same arguments with out_dtype = BSFP8_OUT_F32.
+ *   x, ldx, M, G, N, K, q, e, split_k : as bsfp8_gemm (1 <= M <= 256).
+ *   ws    : >= bsfp8_workspace_bytes_mxfp8(M, G, N, K, split_k) bytes (device, 16-byte aligned).
+ *   yq    : uint8_t e4m3 codes [M][G*N] (device, contiguous, 16-byte aligned).
+ *   ys    : uint8_t scale bytes [M][G*N/32] (device, contiguous).
+ * Two kernels on `stream`: the GEMM, then the epilogue. */
+BSFP8_API int bsfp8_gemm_mxfp8(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                               const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes,
+                               uint8_t* yq, uint8_t* ys, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,8 @@ BSFP8_API int bsfp8_num_configs(void);
  * host memory of 8 ints. */
 BSFP8_API int bsfp8_config_info(int cfg, int* out);
 
-/* Plan the built-in table picks. path: 0 = small, 1 = mid, 2 = what bsfp8_gemm picks.
+/* Plan the built-in table picks. path: 0 = small, 1 = mid, 2 = what bsfp8_gemm picks, 3 = what
+ * bsfp8_gemm_mxfp8 picks.
  * out (host, 8 ints): cfg, BM, NB, kchunks, chunks per split, splits, m-blocks, workgroups.
  * Returns a status as the GEMM calls would for this shape. */
 BSFP8_API int bsfp8_plan_info(int64_t M, int64_t G, int64_t N, int64_t K, int split_k, int path, int* out);
@@ -52,6 +53,15 @@ BSFP8_API size_t bsfp8_workspace_bytes_config(int64_t M, int64_t G, int64_t N, i
 BSFP8_API int bsfp8_gemm_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
                       const uint8_t* q, const uint8_t* e, int cfg, int cps, void* ws,
                       size_t ws_bytes, void* y, int out_dtype, void* stream);
+
+/* bsfp8_gemm_mxfp8 with an explicit configuration and chunks per split, and its workspace bytes
+ * (splits * M * G * N * 4). Arguments and errors otherwise as bsfp8_gemm_mxfp8 and
+ * bsfp8_gemm_config; the epilogue adds the partials in the order of the configuration's own
+ * combine, so the codes quantise exactly the fp32 output of bsfp8_gemm_config(cfg, cps). */
+BSFP8_API size_t bsfp8_workspace_bytes_mxfp8_config(int64_t M, int64_t G, int64_t N, int64_t K, int cfg, int cps);
+BSFP8_API int bsfp8_gemm_mxfp8_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N,
+                                      int64_t K, const uint8_t* q, const uint8_t* e, int cfg, int cps,
+                                      void* ws, size_t ws_bytes, uint8_t* yq, uint8_t* ys, void* stream);
 
 /* The same for a row-scale configuration, on a twin with one exponent per row and 32 columns
  * (e [G][N][K/32], as bsfp8_gemm_row32); other configurations give BSFP8_EINVAL. */

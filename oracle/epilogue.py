@@ -44,6 +44,11 @@ def sum_partials_f32(part, order):
     S = part.shape[0]
     if S < 1:
         raise ValueError("at least one partial")
+    with np.errstate(invalid="ignore", over="ignore"):     # IEEE inf and NaN results are wanted
+        return _sum(part, S, order)
+
+
+def _sum(part, S, order):
     if order == ORDER_ASCENDING:
         acc = part[0].copy()
         for s in range(1, S):

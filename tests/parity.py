@@ -131,3 +131,55 @@ def check_mx_f32(y, exact, absum, K):
         raise AssertionError(f"{int(bad.sum())} fp32 outputs beyond the fp8 bound, e.g. {idx.tolist()}")
     rel = err / np.maximum(absum, 1e-300)
     return float(rel.max()) if rel.size else 0.0
+
+
+# MXFP8 epilogue (fixed-order fp32 sum + MXFP8 quantisation of the output). The GPU quantises its
+# own fp32 sums, which differ from RNE_fp32(Y_exact) by at most B = budget * 2^-24 * sum|x*w| per
+# output; a code (and a block's scale) may therefore differ from the oracle's ideal epilogue only
+# where a value within B of the exact one lies on the other side of a rounding (or binade)
+# boundary. Both decisions are monotone in the value, so the check is an interval check.
+def _e4m3_sat_codes(t):
+    """float64 scaled values -> e4m3 codes: RNE, saturated at +-448 (the quantiser's rule)."""
+    F = oracle.formats
+    r = F.round_to_binary(t, F.E4M3_FRAC, F.E4M3_EMIN, F.E4M3_EMAX, overflow="inf")
+    return F.encode_e4m3(np.clip(r, -F.E4M3_MAX, F.E4M3_MAX))
+
+
+def e4m3_ordinal(c):
+    c = np.asarray(c).astype(np.int64)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def check_mxfp8(yq, ys, exact, absum, K, splits=64):
+    """yq [M, L], ys [M, L/32] from the GPU; exact and absum [M, L] float64. Returns stats."""
+    import oracle.epilogue as EP
+    import oracle.mx as MX
+    M, L = exact.shape
+    yq = np.asarray(yq, dtype=np.uint8).reshape(M, L)
+    ys = np.asarray(ys, dtype=np.uint8).reshape(M, L // 32)
+    iq, iscale = EP.quantize_mx_f32(oracle.f64_to_fp32(exact))
+    B = rounding_budget(K, splits) * U * absum
+    nb = L // 32
+    amax = np.abs(exact).reshape(M, nb, 32).max(axis=2)
+    bmax = B.reshape(M, nb, 32).max(axis=2)
+    s_lo = MX.mx_scale_exponent(np.maximum(amax - bmax, 0.0))
+    s_hi = MX.mx_scale_exponent(amax + bmax)
+    sg = ys.astype(np.int64) - 127
+    scale_ok = (ys == iscale) | ((sg >= s_lo) & (sg <= s_hi) & (ys != 255))
+    if not scale_ok.all():
+        idx = np.argwhere(~scale_ok)[:5]
+        raise AssertionError(f"{int((~scale_ok).sum())} block scales out of range, e.g. {idx.tolist()}: "
+                             f"gpu {[int(ys[tuple(i)]) for i in idx]} ideal {[int(iscale[tuple(i)]) for i in idx]}")
+    sgk = np.repeat(sg, 32, axis=1)
+    same = (yq == iq) & np.repeat(ys == iscale, 32, axis=1)
+    lo = e4m3_ordinal(_e4m3_sat_codes(np.ldexp(exact - B, -sgk)))
+    hi = e4m3_ordinal(_e4m3_sat_codes(np.ldexp(exact + B, -sgk)))
+    o = e4m3_ordinal(yq)
+    ok = same | ((o >= lo) & (o <= hi))
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        raise AssertionError(f"{int((~ok).sum())} codes fail the epilogue rule, e.g. {idx.tolist()}: "
+                             f"gpu {[hex(int(yq[tuple(i)])) for i in idx]} ideal {[hex(int(iq[tuple(i)])) for i in idx]}")
+    return dict(n=int(yq.size), same=int(same.sum()), by_clause=int((~same).sum()),
+                blocks=int(ys.size), scale_differs=int((ys != iscale).sum()))

@@ -176,3 +176,38 @@ def test_row32_plans_and_checks(lib):
     assert rs
     assert lib.bsfp8_gemm_row32_config(fake, 256, 2, 1, 64, 256, fake, fake, 54, 2, null, 0, fake, 0, null) == B.EINVAL
     assert lib.bsfp8_gemm_config(fake, 256, 2, 1, 64, 256, fake, fake, rs[0], 2, null, 0, fake, 0, null) == B.EINVAL
+
+
+def test_mxfp8_epilogue_checks_and_plans(lib):
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(4096)
+    R = lib.bsfp8_reduce_quantize_mx
+    # (part, S, M, L, order, yq, ys, stream)
+    assert R(fake, 1, 2, 64, 2, fake, fake, null) == B.EINVAL                   # order
+    assert R(fake, 0, 2, 64, 0, fake, fake, null) == B.EINVAL                   # S < 1
+    assert R(fake, 65, 2, 64, 0, fake, fake, null) == B.EINVAL                  # S > 64
+    assert R(fake, 1, 2, 48, 0, fake, fake, null) == B.ESHAPE                   # L % 32
+    assert R(fake, 1, 2, 0, 0, fake, fake, null) == B.ESHAPE
+    assert R(null, 1, 0, 64, 1, null, null, null) == B.OK                       # empty: no-op
+    assert R(null, 1, 2, 64, 1, fake, fake, null) == B.EINVAL
+    assert R(ctypes.c_void_p(4100), 1, 2, 64, 1, fake, fake, null) == B.ESTRIDE
+    assert R(fake, 1, 2, 64, 1, ctypes.c_void_p(4100), fake, null) == B.ESTRIDE
+    # the epilogue GEMM runs bsfp8_gemm's plan; its workspace holds one fp32 copy per split
+    for M, G, N, K, sk in ((6, 2, 1024, 4096, 0), (6, 2, 1024, 4096, 4), (64, 2, 1024, 4096, 0),
+                           (16, 1, 32768, 5120, 0), (16, 1, 32768, 5120, 2), (6, 1, 5120, 576, 0)):
+        p3 = B.bsfp8_plan_info(M, G, N, K, split_k=sk, path=3)
+        assert p3 == B.bsfp8_plan_info(M, G, N, K, split_k=sk, path=2)
+        assert B.bsfp8_workspace_bytes_mxfp8(M, G, N, K, sk) == p3["splits"] * M * G * N * 4
+        assert B.bsfp8_workspace_bytes_mxfp8_config(M, G, N, K, p3["cfg"], p3["cps"]) == p3["splits"] * M * G * N * 4
+    assert B.bsfp8_workspace_bytes_mxfp8(0, 2, 1024, 4096, 0) == 0
+    X = lib.bsfp8_gemm_mxfp8
+    # (x, ldx, M, G, N, K, q, e, split_k, ws, ws_bytes, yq, ys, stream)
+    assert X(null, 64, 0, 1, 64, 64, null, null, 0, null, 0, null, null, null) == B.OK
+    assert X(fake, 64, 1, 1, 64, 64, fake, fake, 0, fake, 1 << 20, fake, null, null) == B.EINVAL   # ys
+    assert X(fake, 64, 1, 1, 64, 64, fake, fake, 0, fake, 16, fake, fake, null) == B.EWORKSPACE    # ws small
+    assert X(fake, 64, 1, 1, 64, 64, fake, fake, 0, null, 0, fake, fake, null) == B.EWORKSPACE
+    assert X(fake, 64, 1, 1, 64, 64, fake, fake, 0, fake, 1 << 20, ctypes.c_void_p(4097), fake, null) == B.ESTRIDE
+    assert X(fake, 64, 1, 1, 64, 40, fake, fake, 0, fake, 1 << 20, fake, fake, null) == B.ESHAPE
+    rs = [c for c in range(B.bsfp8_num_configs()) if B.bsfp8_config_info(c)["row_scales"]]
+    assert lib.bsfp8_gemm_mxfp8_config(fake, 256, 2, 1, 64, 256, fake, fake, rs[0], 2, fake, 1 << 20, fake, fake,
+                                       null) == B.EINVAL

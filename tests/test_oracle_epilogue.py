@@ -244,3 +244,37 @@ def test_ideal_epilogue_is_exact_on_integer_sums():
     assert np.array_equal(Y, np.round(Y)) and np.abs(Y).max() < 2 ** 24
     c2, s2 = EP.quantize_mx_f32(Y.reshape(M, G * N).astype(f32))
     assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+
+
+def test_parity_rule_of_the_epilogue_catches_a_wrong_code():
+    # the GPU-side checker (tests/parity.py) against planted results: the ideal epilogue and the
+    # epilogue of fp32 values within the error budget pass; a code one step off where the value
+    # is far from a rounding boundary, or a scale one binade off, fails
+    from parity import check_mxfp8, rounding_budget, U
+    r = S.rng(97)
+    M, G, N, K = 3, 1, 64, 256
+    x = S.bf16_normal(r, (M, G * K))
+    q = S.e4m3_codes(r, (G, N, K))
+    e = S.exponent_bytes(r, (G, N // 32, K // 32), 118, 126)
+    codes, scales, Y = EP.gemm_mxfp8_ideal(x, G, N, K, q, e)
+    Y = Y.reshape(M, G * N)
+    A = oracle.abs_products_sum(x, G, N, K, q, e).reshape(M, G * N)
+    st = check_mxfp8(codes, scales, Y, A, K, 1)
+    assert st["same"] == st["n"]
+    noisy = Y + (r.uniform(-1, 1, Y.shape) * rounding_budget(K, 1) * U * A)
+    c2, s2 = EP.quantize_mx_f32(oracle.f64_to_fp32(noisy))
+    check_mxfp8(c2, s2, Y, A, K, 1)
+    # one code one step up at an element whose scaled value is mid-way between two codes
+    s_el = np.repeat(scales.astype(np.int64) - 127, 32, axis=1)
+    t = np.abs(np.ldexp(Y, -s_el))
+    dec = oracle.decode_e4m3(codes & 0x7F)
+    i = np.argmax((np.abs(t - dec) < 1e-3 * np.maximum(dec, 1e-3)) & (t > 16) & (t < 400))
+    m, j = divmod(int(i), G * N)
+    bad = codes.copy()
+    bad[m, j] += 1
+    with pytest.raises(AssertionError):
+        check_mxfp8(bad, scales, Y, A, K, 1)
+    bad_s = scales.copy()
+    bad_s[0, 0] += 1
+    with pytest.raises(AssertionError):
+        check_mxfp8(codes, bad_s, Y, A, K, 1)
