@@ -65,8 +65,9 @@ def parse():
     p.add_argument("--workload", default="wo_a", choices=sorted(WORKLOADS))
     p.add_argument("--m", type=int, default=None)
     p.add_argument("--split-k", type=int, default=0)
-    p.add_argument("--path", default="bf16", choices=["bf16", "mx"],
-                   help="bf16: the exact twin GEMM (default); mx: the fp8 x fp8 GEMM on MXFP8 activations")
+    p.add_argument("--path", default="bf16", choices=["bf16", "mx", "mxfp8"],
+                   help="bf16: the exact twin GEMM (default); mx: the fp8 x fp8 GEMM on MXFP8 activations; "
+                        "mxfp8: the exact twin GEMM with the MXFP8 output epilogue")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--all", default=None, help="also time every workload and row count; write JSON lines here")
@@ -125,7 +126,8 @@ def graph_us(torch, fn, steps):
 def time_workload(name, M, steps, warmup, split_k=0, path="bf16"):
     """path "bf16": the exact twin GEMM (bsfp8_gemm). path "mx": the fp8 x fp8 GEMM
     (bsfp8_gemm_mx) on activations quantized once before the timed region; the quantizer is timed
-    on its own and reported as quantize_us."""
+    on its own and reported as quantize_us. path "mxfp8": the twin GEMM with the MXFP8 output
+    epilogue (bsfp8_gemm_mxfp8: GEMM + fused sum-and-quantise kernel per call)."""
     import torch
     import block_scaled_fp8_skinny_amd as B
     import synthetic as S
@@ -136,6 +138,8 @@ def time_workload(name, M, steps, warmup, split_k=0, path="bf16"):
     w_b, e_b, x_b, y_b = algorithmic_bytes(M, G, N, K, out_bytes, row_scales)
     if path == "mx":
         x_b = M * G * K + M * G * K // 32             # e4m3 codes + scale bytes
+    if path == "mxfp8":
+        y_b = M * G * N + M * G * N // 32             # e4m3 codes + scale bytes of the output
     copy_bytes = w_b + e_b
     n_copies = max(4, min(steps, math.ceil(COLD_BYTES / copy_bytes)))
     qs, es = make_copies(torch, B, G, N, K, elo, ehi, n_copies, seed=7000 + M, row_scales=row_scales)
@@ -161,6 +165,14 @@ def time_workload(name, M, steps, warmup, split_k=0, path="bf16"):
 
         def call(i):
             B.bsfp8_gemm_row32(x, qs[i % n_copies], es[i % n_copies], split_k=split_k, ws=ws, out=y, out_dtype=out)
+    elif path == "mxfp8":
+        plan = B.bsfp8_plan_info(M, G, N, K, split_k, path=3)
+        ws = B.workspace_mxfp8(M, G, N, K, split_k)
+        yq = torch.empty((M, G * N), dtype=torch.uint8, device="cuda")
+        ys = torch.empty((M, G * N // 32), dtype=torch.uint8, device="cuda")
+
+        def call(i):
+            B.bsfp8_gemm_mxfp8(x, qs[i % n_copies], es[i % n_copies], split_k=split_k, ws=ws, yq=yq, ys=ys)
     else:
         plan = B.bsfp8_plan_info(M, G, N, K, split_k)
 
@@ -287,9 +299,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": (round(r["weight_stream_gbs_wall"] / PAGES_GBS, 2)
                         if args.workload == "wo_a" and M == 6 and args.path == "bf16" else None),
-        "dtype": "bf16" if args.path == "bf16" else "fp8",
+        "dtype": "fp8" if args.path == "mx" else "bf16",
         "data": "synthetic",
-        "config": {"workload": r["desc"] + f"; M={M}" + ("; fp8 x fp8 path (MXFP8 activations)" if args.path == "mx" else ""),
+        "config": {"workload": r["desc"] + f"; M={M}" + {"mx": "; fp8 x fp8 path (MXFP8 activations)",
+                                                          "mxfp8": "; MXFP8 output epilogue"}.get(args.path, ""),
                    "path": args.path, "M": M, "G": G, "N": N, "K": K,
                    "weight_copies": r["copies"], "copy_bytes": r["copy_bytes"], "plan": r["plan"]},
         "us_per_call": round(r["wall_us_per_call"], 3),
@@ -320,6 +333,12 @@ def main():
             rr = time_workload("main_proj", m, 2000, 50)
             rows.append(rr)
             print(json.dumps(rr), file=sys.stderr, flush=True)
+        # the MXFP8 output epilogue (GEMM + fused sum-and-quantise kernel)
+        for name, ms in (("wo_a", [2, 6, 8]), ("wo_a_mid", [16, 64, 192])):
+            for m in ms:
+                rr = time_workload(name, m, 2000, 50, path="mxfp8")
+                rows.append(rr)
+                print(json.dumps(rr), file=sys.stderr, flush=True)
         # the fp8 x fp8 path (MXFP8 activations) on the same weights
         for name, ms in (("wo_a", [6]), ("wo_a_mid", [16, 64, 128, 192]), ("lm_head", [16, 64, 128])):
             for m in ms:
