@@ -88,10 +88,17 @@ int check_gemm_mx(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int64_t M, 
   return BSFP8_OK;
 }
 
-// The GEMM into the workspace (fp32 results or split partials), then the MXFP8 epilogue.
+// The GEMM with the MXFP8 epilogue: fused into one kernel for a decode plan with one split (when
+// `fuse`), else the GEMM into the workspace (fp32 results or split partials) and the epilogue
+// kernel.
 int run_gemm_mxfp8(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,
-                   const uint8_t* e, void* ws, size_t ws_bytes, uint8_t* yq, uint8_t* ys, hipStream_t stream) {
+                   const uint8_t* e, void* ws, size_t ws_bytes, uint8_t* yq, uint8_t* ys, bool fuse,
+                   hipStream_t stream) {
   if (!ws || ws_bytes < gemm_partials_bytes(s, p) || !aligned16(ws)) return BSFP8_EWORKSPACE;
+  if (fuse) {
+    const int fst = launch_decode_mxfp8(s, p, x, q, e, yq, ys, stream);
+    if (fst != BSFP8_EINVAL) return fst;
+  }
   int st = launch_gemm(s, p, x, q, e, ws, nullptr, 1, stream, /*partials=*/1);
   if (st != BSFP8_OK) return st;
   return launch_reduce_quantize_mx(reinterpret_cast<const float*>(ws), p.splits, s.M, (int64_t)s.G * s.N,
@@ -391,7 +398,7 @@ int bsfp8_gemm_mxfp8(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64
   GemmPlan p;
   st = plan_gemm_mxfp8(s, split_k, &p);
   if (st != BSFP8_OK) return st;
-  return run_gemm_mxfp8(s, p, x, q, e, ws, ws_bytes, yq, ys, as_stream(stream));
+  return run_gemm_mxfp8(s, p, x, q, e, ws, ws_bytes, yq, ys, /*fuse=*/true, as_stream(stream));
 }
 
 size_t bsfp8_workspace_bytes_mxfp8_config(int64_t M, int64_t G, int64_t N, int64_t K, int cfg, int cps) {
@@ -412,7 +419,7 @@ int bsfp8_gemm_mxfp8_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G
   GemmPlan p;
   st = plan_with(s, cfg, cps, &p);
   if (st != BSFP8_OK) return st;
-  return run_gemm_mxfp8(s, p, x, q, e, ws, ws_bytes, yq, ys, as_stream(stream));
+  return run_gemm_mxfp8(s, p, x, q, e, ws, ws_bytes, yq, ys, /*fuse=*/false, as_stream(stream));
 }
 
 }  // extern "C"

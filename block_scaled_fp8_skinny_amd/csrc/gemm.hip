@@ -1636,18 +1636,18 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
   return plan_with(s, 2, cps, plan);
 }
 
-// Built-in choice for weights with one exponent per row and 32 columns (a GEMV for up to 16
-// rows, page "recipes/docker-images/mia-tp4/docs/tp4-adapters.md", row draft_main_proj): the
-// decode kernel with row exponents and 8 rows of X per workgroup, with the waves and chunks the
-// 32x32 plan uses for decode rows (so replicated block exponents give bitwise its results) up to
-// 32 chunks; 33..40 chunks (K = 5120, the page's shape) run in one pass on half tiles; longer K
-// is split over workgroups (the pairwise exchange combines the splits).
 // The MXFP8-epilogue GEMM runs the plan bsfp8_gemm would pick for the same arguments, so its
 // codes quantise exactly the fp32 outputs of that call.
 int plan_gemm_mxfp8(const GemmShape& s, int split_k, GemmPlan* plan) {
   return plan_gemm(s, s.M <= 8 ? PATH_SMALL : PATH_MID, split_k, plan);
 }
 
+// Built-in choice for weights with one exponent per row and 32 columns (a GEMV for up to 16
+// rows, page "recipes/docker-images/mia-tp4/docs/tp4-adapters.md", row draft_main_proj): the
+// decode kernel with row exponents and 8 rows of X per workgroup, with the waves and chunks the
+// 32x32 plan uses for decode rows (so replicated block exponents give bitwise its results) up to
+// 32 chunks; 33..40 chunks (K = 5120, the page's shape) run in one pass on half tiles; longer K
+// is split over workgroups (the pairwise exchange combines the splits).
 int plan_gemm_row32(const GemmShape& s, int split_k, GemmPlan* plan) {
   if (s.K % KCH != 0 || s.M > 16) return BSFP8_ESHAPE;
   const int kchunks = s.K / KCH;

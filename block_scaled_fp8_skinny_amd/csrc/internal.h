@@ -57,6 +57,10 @@ size_t gemm_partials_bytes(const GemmShape& s, const GemmPlan& p);
 // quantisation along L (codes [M][L], scale bytes [M][L/32]).
 int launch_reduce_quantize_mx(const float* part, int S, int64_t M, int64_t L, int order, uint8_t* yq,
                               uint8_t* ys, hipStream_t stream);
+// The fused form (decode plans with one split): GEMM and epilogue in one kernel. Returns
+// BSFP8_EINVAL when the plan is not a 16-row decode plan with one split.
+int launch_decode_mxfp8(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,
+                        const uint8_t* e, uint8_t* yq, uint8_t* ys, hipStream_t stream);
 
 int launch_scales_from_f32(const float* s, int64_t n, uint8_t* out, unsigned long long* bad,
                            hipStream_t stream);

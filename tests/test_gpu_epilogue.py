@@ -160,6 +160,33 @@ def test_gemm_mxfp8_shared_down_and_lm_head_rows():
     print(check_mxfp8(yq.cpu().numpy()[rows], ys.cpu().numpy()[rows], Y, A, 5120), flush=True)
 
 
+# decode shapes where the built-in plan is the 16-row decode kernel with one split: the fused
+# kernel runs (32 weight rows per workgroup, GEMM and epilogue in one launch); the explicit
+# configuration call takes the two-kernel form with the same plan, so both must agree bitwise
+FUSED_CASES = [(1, 2, 1024, 4096), (6, 2, 1024, 4096), (8, 2, 1024, 4096), (13, 2, 1024, 4096),
+               (16, 2, 1024, 4096), (6, 4, 1024, 4096), (6, 1, 5120, 640), (5, 1, 96, 384), (3, 1, 64, 1152)]
+
+
+@pytest.mark.parametrize("M,G,N,K", FUSED_CASES)
+def test_fused_decode_equals_the_two_kernel_form(M, G, N, K):
+    r = S.rng(9500 + M + K)
+    x = S.bf16_normal(r, (M, G * K))
+    q = S.e4m3_codes(r, (G, N, K))
+    e = S.exponent_bytes(r, (G, N // 32, K // 32), 112, 126)
+    plan = B.bsfp8_plan_info(M, G, N, K, path=3)
+    info = B.bsfp8_config_info(plan["cfg"])
+    print(f"fused M={M} G={G} N={N} K={K} plan {plan} kind {info['kind']}", flush=True)
+    assert info["kind"] == 4 and plan["splits"] == 1
+    xt, qt, et = to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e)
+    yq, ys = B.bsfp8_gemm_mxfp8(xt, qt, et)
+    q2, s2 = B.bsfp8_gemm_mxfp8_config(xt, qt, et, plan["cfg"], plan["cps"])
+    torch.cuda.synchronize()
+    assert torch.equal(ys, s2) and torch.equal(yq, q2)
+    W = oracle.dequant_values(q, e)
+    Y, A = _exact_and_absum(x, W, np.abs(W), G, K)
+    print(check_mxfp8(yq.cpu().numpy(), ys.cpu().numpy(), Y, A, K, 1), flush=True)
+
+
 def test_gemm_mxfp8_graph_replay_and_repeats(wo_a_weight):
     d, W, Wabs, qt, et = wo_a_weight
     M, G, N, K = 6, 2, 1024, 4096
