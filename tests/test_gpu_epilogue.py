@@ -164,7 +164,8 @@ def test_gemm_mxfp8_shared_down_and_lm_head_rows():
 # kernel runs (32 weight rows per workgroup, GEMM and epilogue in one launch); the explicit
 # configuration call takes the two-kernel form with the same plan, so both must agree bitwise
 FUSED_CASES = [(1, 2, 1024, 4096), (6, 2, 1024, 4096), (8, 2, 1024, 4096), (13, 2, 1024, 4096),
-               (16, 2, 1024, 4096), (6, 4, 1024, 4096), (6, 1, 5120, 640), (5, 1, 96, 384), (3, 1, 64, 1152)]
+               (16, 2, 1024, 4096), (6, 4, 1024, 4096), (6, 1, 5120, 640), (5, 1, 96, 384), (3, 1, 64, 1152),
+               (9, 1, 32, 1280), (4, 1, 32, 128), (1, 3, 96, 256), (2, 1, 64, 4096)]
 
 
 @pytest.mark.parametrize("M,G,N,K", FUSED_CASES)
@@ -213,3 +214,26 @@ def test_gemm_mxfp8_graph_replay_and_repeats(wo_a_weight):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(yq, yq0) and torch.equal(ys, ys0)
+
+
+def test_gemm_mxfp8_empty_and_errors():
+    G, N, K = 1, 64, 128
+    q = torch.zeros((G, N, K), dtype=torch.uint8, device="cuda")
+    e = torch.full((G, N // 32, K // 32), 127, dtype=torch.uint8, device="cuda")
+    yq, ys = B.bsfp8_gemm_mxfp8(torch.zeros((0, K), dtype=torch.bfloat16, device="cuda"), q, e)
+    assert yq.shape == (0, G * N) and ys.shape == (0, G * N // 32)
+    x = torch.zeros((4, K), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.BsfpError) as ei:                  # workspace too small
+        B.bsfp8_gemm_mxfp8(x, q, e, ws=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert ei.value.status == B.EWORKSPACE
+    with pytest.raises(B.BsfpError) as ei:
+        B.bsfp8_gemm_mxfp8(torch.zeros((257, K), dtype=torch.bfloat16, device="cuda"), q, e)
+    assert ei.value.status == B.ESHAPE
+    part = torch.zeros((65, 1, 32), dtype=torch.float32, device="cuda")
+    with pytest.raises(B.BsfpError) as ei:
+        B.bsfp8_reduce_quantize_mx(part)
+    assert ei.value.status == B.EINVAL
+    # an all-zero product: scale byte 0 and zero codes
+    yq, ys = B.bsfp8_gemm_mxfp8(x, q, e)
+    torch.cuda.synchronize()
+    assert int(yq.abs().sum()) == 0 and int(ys.sum()) == 0
