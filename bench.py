@@ -210,6 +210,43 @@ def time_workload(name, M, steps, warmup, split_k=0, path="bf16"):
     return res
 
 
+def time_make_twin(n_layers=43, G=4, R=1024, D=4096, elo=115, ehi=123):
+    """The twin encoder at the padded-TP3 layer shape: n_layers distinct bf16 weights [G, R, D],
+    each exactly e4m3 x 2^e per 32x32 block (e = byte - 127 in [elo, ehi], built on the device
+    from seeded codes by bsfp8_dequant), encoded once each by bsfp8_make_twin (a synchronous
+    prepare call: it allocates and clears an 8-byte counter, runs the encoder and reads the
+    verdict back). Reported: the GPU span between HIP events around each call on its stream, and
+    the host wall time per call."""
+    import torch
+    import block_scaled_fp8_skinny_amd as B
+    qs, es = make_copies(torch, B, G, R, D, elo, ehi, n_layers, seed=7500)
+    ws = [B.bsfp8_dequant(qs[i], es[i]) for i in range(n_layers)]
+    del qs, es
+    for i in range(3):
+        B.bsfp8_make_twin(ws[i])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_layers)]
+    accepted = 0
+    t0 = time.perf_counter()
+    for i in range(n_layers):
+        evs[2 * i].record(stream)
+        t = B.bsfp8_make_twin(ws[i])
+        evs[2 * i + 1].record(stream)
+        accepted += int(t.accepted)
+    torch.cuda.synchronize()
+    wall_us = 1e6 * (time.perf_counter() - t0) / n_layers
+    spans = sorted(1e3 * evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n_layers))
+    gpu_us = sum(spans) / n_layers
+    nbytes = G * R * D * 2 + G * R * D + 2 * G * (R // 32) * (D // 32)   # read bf16, write codes, exps, ok
+    del ws
+    torch.cuda.empty_cache()
+    return dict(workload="twin_tp3", path="make_twin", desc=f"make_twin of {n_layers} exact bf16 layers [{G},{R},{D}]",
+                G=G, N=R, K=D, layers=n_layers, accepted=accepted, gpu_span_us_per_layer=gpu_us,
+                gpu_span_us_median=spans[n_layers // 2], wall_us_per_layer=wall_us, bytes_per_layer=nbytes,
+                algorithmic_gbs=nbytes / (gpu_us * 1e3), pct_hbm_peak=100 * nbytes / (gpu_us * 1e3) / HBM_PEAK_GBS)
+
+
 def cpu_baseline(name, M, seconds):
     """The oracle as it stands, timed on this host on a bounded sample of the same workload:
     whole GEMM calls on weight copies of the real shape until `seconds` have passed."""
@@ -328,6 +365,10 @@ def main():
                 rr = time_workload(name, m, st, 50)
                 rows.append(rr)
                 print(json.dumps(rr), file=sys.stderr, flush=True)
+        # the twin encoder at the padded-TP3 layer shape
+        rr = time_make_twin()
+        rows.append(rr)
+        print(json.dumps(rr), file=sys.stderr, flush=True)
         # the row-scale twin (one exponent per row and 32 columns) at its page's shape
         for m in (1, 6, 16):
             rr = time_workload("main_proj", m, 2000, 50)

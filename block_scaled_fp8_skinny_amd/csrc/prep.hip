@@ -21,9 +21,19 @@ __global__ void scales_kernel(const uint32_t* s, int64_t n, uint8_t* out, unsign
 }
 
 // ---------------------------------------------------------------------------------------------
-// Twin encoder (page "wo_a_w8.py", make_twin). One wave per 32x32 block: lane l holds row l/2,
-// columns 16*(l&1) .. +15 of the block (two 16-byte loads).
+// Twin encoder (page "wo_a_w8.py", make_twin). One wave per block row (32 rows) and strip of 128
+// columns (4 blocks): lane (r4, c16) = (lane / 16, lane % 16) holds columns 8*c16 .. 8*c16+7 of
+// the strip in rows r4, r4 + 4, ..., r4 + 28. Each load then reads four rows x 256 contiguous
+// bytes (HBM streams this near its best rate; a wave per block reading 64 bytes of each of 32
+// rows ran at about a quarter of the peak), and block b of the strip is the 16 lanes with
+// c16 / 4 == b (reductions by lane exchanges 1, 2, 16, 32).
+// The codes come from the hardware's scaled conversion of bf16 pairs (v_cvt_scalef32_pk_fp8_bf16
+// divides by 2^(scale exponent field - 127) and rounds to nearest even; with |w| / 2^e <= 448 by
+// the choice of e it neither saturates nor overflows) and the rebuild from its inverse: both are
+// exact for every bf16 value and every e in [-127, 127] (measured against the integer encoder),
+// two elements per instruction.
 // ---------------------------------------------------------------------------------------------
+constexpr int TWIN_STRIP = 128;                     // columns per wave: 16 lanes x 8
 
 // Least e with max(amax, 2^-126) <= 448 * 2^e, from the bf16 pattern of amax (finite):
 // amax = (128 + f) * 2^(E - 134); 448 * 2^e = 7 * 2^(6 + e). For a normal amax the bound holds
@@ -35,73 +45,69 @@ __device__ __forceinline__ int block_exp(uint32_t amax_bits) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-__global__ void __launch_bounds__(256) make_twin_kernel(const uint16_t* w, int64_t nblk_r,
-                                                        int64_t nblk_c, int64_t D, int64_t nblocks,
-                                                        uint8_t* q, uint8_t* e, uint8_t* okv,
-                                                        unsigned long long* bad) {
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+
+__global__ void __launch_bounds__(256) make_twin_kernel(const uint16_t* w, int64_t D, int64_t nstrips,
+                                                        int64_t nwaves, uint8_t* q, uint8_t* e,
+                                                        uint8_t* okv, unsigned long long* bad) {
   const int lane = threadIdx.x & 63;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= nblocks) return;                       // whole wave exits together
-  const int64_t cb = blk % nblk_c;
-  const int64_t rb = (blk / nblk_c) % nblk_r;
-  const int64_t g = blk / (nblk_c * nblk_r);
-  const int64_t R = nblk_r * 32;
-  const int64_t row = g * R + rb * 32 + (lane >> 1);
-  const int64_t col = cb * 32 + (lane & 1) * 16;
-  const uint4* src = reinterpret_cast<const uint4*>(w + row * D + col);
-  const uint4 v0 = src[0], v1 = src[1];
-  uint32_t h[16];
-  const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= nwaves) return;                        // whole wave exits together
+  const int r4 = lane >> 4, c16 = lane & 15;
+  const int64_t strip = wid % nstrips;
+  const int64_t grb = wid / nstrips;                // g * R/32 + block row
+  const int64_t col = strip * TWIN_STRIP + c16 * 8;
+  const bool live = col < D;                        // D % 32 == 0: the 4 lanes of a block agree
+  const int64_t row0 = grb * 32 + r4;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = live ? *reinterpret_cast<const uint4*>(w + (row0 + 4 * i) * D + col) : make_uint4(0, 0, 0, 0);
+  // block maximum of the magnitude patterns (inf and NaN patterns exceed every finite one)
+  uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    h[2 * i] = d[i] & 0xFFFF;
-    h[2 * i + 1] = d[i] >> 16;
-  }
-  uint32_t amax = 0;
-  bool finite = true;
+    const uint32_t d[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t m = h[i] & 0x7FFF;
-    finite = finite && (m < 0x7F80);
-    amax = m > amax ? m : amax;
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = d[j] & 0x7FFF, hi = (d[j] >> 16) & 0x7FFF;
+      amax = max(amax, max(lo, hi));
+    }
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)amax, off);
-    amax = o > amax ? o : amax;
+  for (int off = 1; off <= 32; off <<= 1) {
+    if (off == 4 || off == 8) continue;             // lanes 4b .. 4b+3 of each row group
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
   }
-  const bool all_finite = __all(finite);
-  const int eb = block_exp(amax);
-  const uint32_t eb_byte = (uint32_t)(eb + 127);
-  const float back_scale = __uint_as_float(eb_byte << 23);   // factor 2^e for the rebuild
-
-  uint32_t codes[16];
-  bool same = true;
+  const bool finite = amax < 0x7F80;
+  const int eb = block_exp(finite ? amax : 0);
+  const float scale = __uint_as_float((uint32_t)(eb + 127) << 23);   // 2^eb (field 0: 2^-127)
+  uint32_t same = 1;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float f = __uint_as_float(h[i] << 16);
-    const float sv = ldexpf(f, -eb);                          // exact (or below 2^-10)
-    codes[i] = e4m3_rne(sv);
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t d[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const s16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2_t{0, 0}, __builtin_bit_cast(bf16x2_t, d[j]),
+                                                                 scale, false);
+      c[j] = (uint32_t)(uint16_t)r[0];
+      const uint32_t back = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], scale, false));
+      same &= back == d[j] ? 1u : 0u;
+    }
+    uint2 out = make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
+    if (!finite) out = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    if (live) *reinterpret_cast<uint2*>(q + (row0 + 4 * i) * D + col) = out;
   }
 #pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    // bf16(e4m3(q) * 2^e) for two codes at once; exact RNE for every exponent byte
-    const bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[i] | (codes[i + 1] << 8),
-                                                                back_scale, false);
-    const uint32_t rb2 = bits_of(r);
-    same = same && ((rb2 & 0xFFFF) == h[i]) && ((rb2 >> 16) == h[i + 1]);
+  for (int off = 1; off <= 32; off <<= 1) {
+    if (off == 4 || off == 8) continue;
+    same &= (uint32_t)__shfl_xor((int)same, off);
   }
-  const bool ok = __all(same) && all_finite;
-  uint4 out;
-  uint32_t packed[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    packed[i] = codes[4 * i] | (codes[4 * i + 1] << 8) | (codes[4 * i + 2] << 16) | (codes[4 * i + 3] << 24);
-  out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  if (!all_finite) out = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
-  *reinterpret_cast<uint4*>(q + row * D + col) = out;
-  if (lane == 0) {
-    e[blk] = all_finite ? (uint8_t)eb_byte : (uint8_t)255;
+  const bool ok = same && finite;
+  if (live && r4 == 0 && (c16 & 3) == 0) {
+    const int64_t blk = grb * (D / 32) + col / 32;
+    e[blk] = finite ? (uint8_t)(eb + 127) : (uint8_t)255;
     if (okv) okv[blk] = ok ? 1 : 0;
     if (!ok) atomicAdd(bad, 1ull);
   }
@@ -223,28 +229,46 @@ __global__ void pad_input_scalar_kernel(const uint16_t* x, int64_t ldx, int64_t 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Standalone dequantisation (page "wo_a_w8.py", _dequant_kernel): one thread per 16 codes.
+// Standalone dequantisation (page "wo_a_w8.py", _dequant_kernel). A workgroup converts 4 x 256
+// consecutive 16-code pieces of the flattened [G*N][K] codes, thread t the pieces t, t + 256,
+// t + 512, t + 768: each wave load reads one contiguous kilobyte, and a thread keeps four loads
+// in flight.
 // ---------------------------------------------------------------------------------------------
-__global__ void dequant_kernel(const uint8_t* q, const uint8_t* e, int64_t rows, int64_t K,
-                               uint16_t* w) {
+constexpr int DQ_UNROLL = 4;
+
+__global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* q, const uint8_t* e, int64_t npieces,
+                                                      int64_t K, uint16_t* w) {
   const int64_t per_row = K / 16;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= rows * per_row) return;
-  const int64_t r = i / per_row, c = (i % per_row) * 16;
-  // rows run over [G*N]; block rows over [G*N/32] in the same order
-  const uint32_t b = e[(r / 32) * (K / 32) + c / 32];
-  const float sc = __uint_as_float(b << 23);
-  const uint4 v = *reinterpret_cast<const uint4*>(q + r * K + c);
-  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[8];
+  const int64_t base = (int64_t)blockIdx.x * (256 * DQ_UNROLL) + threadIdx.x;
+  uint4 v[DQ_UNROLL];
+  uint32_t b[DQ_UNROLL];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    o[2 * j] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[j], sc, false));
-    o[2 * j + 1] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[j], sc, true));
+  for (int u = 0; u < DQ_UNROLL; ++u) {
+    const int64_t i = base + u * 256;
+    if (i < npieces) {
+      const int64_t r = i / per_row, c = (i % per_row) * 16;
+      // rows run over [G*N]; block rows over [G*N/32] in the same order
+      b[u] = e[(r / 32) * (K / 32) + c / 32];
+      v[u] = *reinterpret_cast<const uint4*>(q + r * K + c);
+    }
   }
-  uint4* dst = reinterpret_cast<uint4*>(w + r * K + c);
-  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+#pragma unroll
+  for (int u = 0; u < DQ_UNROLL; ++u) {
+    const int64_t i = base + u * 256;
+    if (i >= npieces) continue;
+    const int64_t r = i / per_row, c = (i % per_row) * 16;
+    const float sc = __uint_as_float(b[u] << 23);
+    const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[2 * j] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[j], sc, false));
+      o[2 * j + 1] = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[j], sc, true));
+    }
+    uint4* dst = reinterpret_cast<uint4*>(w + r * K + c);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
 }
 
 inline unsigned grid_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
@@ -261,10 +285,11 @@ int launch_scales_from_f32(const float* s, int64_t n, uint8_t* out, unsigned lon
 
 int launch_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t* q, uint8_t* e,
                      uint8_t* ok, unsigned long long* bad, hipStream_t stream) {
-  const int64_t nblocks = G * (R / 32) * (D / 32);
-  if (nblocks == 0) return BSFP8_OK;
-  hipLaunchKernelGGL(make_twin_kernel, dim3(grid_for(nblocks, 4)), dim3(256), 0, stream, w, R / 32,
-                     D / 32, D, nblocks, q, e, ok, bad);
+  const int64_t nstrips = (D + TWIN_STRIP - 1) / TWIN_STRIP;
+  const int64_t nwaves = G * (R / 32) * nstrips;
+  if (nwaves == 0) return BSFP8_OK;
+  hipLaunchKernelGGL(make_twin_kernel, dim3(grid_for(nwaves, 4)), dim3(256), 0, stream, w, D, nstrips,
+                     nwaves, q, e, ok, bad);
   return hip_status(hipGetLastError());
 }
 
@@ -307,8 +332,9 @@ int launch_dequant(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int
                    hipStream_t stream) {
   const int64_t rows = G * N;
   if (rows == 0 || K == 0) return BSFP8_OK;
-  hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(rows * (K / 16), 256)), dim3(256), 0, stream, q,
-                     e, rows, K, w);
+  const int64_t npieces = rows * (K / 16);
+  hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(npieces, 256 * DQ_UNROLL)), dim3(256), 0, stream, q,
+                     e, npieces, K, w);
   return hip_status(hipGetLastError());
 }
 

@@ -94,6 +94,32 @@ def test_make_twin_all_bf16_magnitudes_one_per_block():
     assert np.array_equal(e, ref.e) and np.array_equal(ok, ref.ok) and np.array_equal(q, ref.q)
 
 
+def test_make_twin_amax_anywhere_in_its_block():
+    # the largest element of each block at a random row and column (every lane position of the
+    # encoder's row groups), ragged strips (the column count is not a multiple of 8 blocks), some
+    # blocks rejected by a value with too many significant bits, some holding inf or NaN
+    r = S.rng(3010)
+    src = S.twin_source(3011, G=3, R=64, D=32 * 13)
+    w = oracle.dequant_bf16(src["q"], src["e"]).copy()
+    G, R, D = w.shape
+    for g in range(G):
+        for rb in range(R // 32):
+            for cb in range(D // 32):
+                i, j = rb * 32 + int(r.integers(0, 32)), cb * 32 + int(r.integers(0, 32))
+                kind = int(r.integers(0, 10))
+                if kind == 0:
+                    w[g, i, j] = 0x3F81 | (w[g, i, j] & 0x8000)         # 8 significant bits
+                elif kind == 1:
+                    w[g, i, j] = 0x7F80 if r.integers(0, 2) else 0xFFC1  # inf or NaN
+                elif kind == 2:
+                    w[g, i, j] = 0x43E0                                   # 448 as the maximum
+    acc, q, e, ok, nbad = _twin_gpu(w)
+    ref = oracle.make_twin(w)
+    assert np.array_equal(e, ref.e) and np.array_equal(ok, ref.ok)
+    assert np.array_equal(q, ref.q)
+    assert nbad == int((ref.ok == 0).sum()) and acc == ref.accepted
+
+
 def test_pad_k_weight_and_input_bitwise():
     d = S.shared_down(3100, M=6, N=256, K=576)
     e = oracle.scales_from_f32(d["scales"], 256, 576)[None]
