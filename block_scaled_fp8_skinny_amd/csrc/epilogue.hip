@@ -237,15 +237,22 @@ __global__ void __launch_bounds__(WAVE * NWK) decode_mxfp8_kernel(DecodeMxParams
 #pragma unroll
   for (int j = 1; j < CW; ++j) load_chunk(qb, wk + j * NWK, wb + (j - 1) * TG);
 
-  // (5) dequant + MFMA in the decode kernel's order, tile A then tile B
+  // (5) dequant + MFMA in the decode kernel's order, tile A then tile B (the block factors of
+  //     the wave's chunks are read once: both tiles lie in one block row)
   const uint8_t* eb = reinterpret_cast<const uint8_t*>(e_lds);
   const int wsw = (r16 >> 1) & 7;
+  float scf[CW][2];
+#pragma unroll
+  for (int j = 0; j < CW; ++j) {
+    const int cl = wk + j * NWK;
+    scf[j][0] = block_scale(eb[cl * 4 + (q4 >> 1)]);
+    scf[j][1] = block_scale(eb[cl * 4 + 2 + (q4 >> 1)]);
+  }
   f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   auto chunk = [&](int ts, int j, const uint4* slot) {
     const int cl = wk + j * NWK;
     if (cl >= c_end) return;                        // not loaded: nothing defined in LDS
-    const float sc0 = block_scale(eb[cl * 4 + (q4 >> 1)]);
-    const float sc1 = block_scale(eb[cl * 4 + 2 + (q4 >> 1)]);
+    const float sc0 = scf[j][0], sc1 = scf[j][1];
     const uint4* wt = slot + r16 * 8;
     const uint4 a = wt[q4 ^ wsw], b = wt[(4 + q4) ^ wsw];
     f32x4_t c = acc[ts];

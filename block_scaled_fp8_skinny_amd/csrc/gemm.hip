@@ -1042,7 +1042,10 @@ gemm_decode_kernel(KParams p) {
   wait_vmcnt_le<WPW>();                             // this wave's exponent and X loads
   lds_barrier();                                    // ... everyone's
 
-  // (4) dequant + MFMA, chunk by chunk in ascending order, each once its own weights are in
+  // (4) X fragments and block factors of all this wave's chunks into registers (X and the
+  //     exponents are complete since the barrier), so that each chunk, once its own weights have
+  //     landed, costs one LDS round trip (its weight fragments) before its dequant + MFMAs. Chunks
+  //     are computed in ascending order.
   f32x4_t acc[NT];
 #pragma unroll
   for (int ts = 0; ts < NT; ++ts) acc[ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1050,26 +1053,35 @@ gemm_decode_kernel(KParams p) {
   const uint8_t* eb = reinterpret_cast<const uint8_t*>(e_lds);
   const int wr = r16 & (TR - 1);                   // the weight row this lane reads (rows TR..15
   const int wsw = (wr >> 1) & 7;                    // of a half tile repeat rows 0..7)
-  auto chunk = [&](int j) {
+  bf16x8_t xf[CW][4];
+  float sc[CW][NT][2];
+#pragma unroll
+  for (int j = 0; j < CW; ++j) {
     const int cl = wk + j * NWK;                    // chunk index inside the workgroup
-    // (a chunk past the range was not loaded: its LDS holds nothing defined)
-    if (c_begin + cl >= c_end) return;
-    const bf16x8_t x0 = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 2 * q4]);
-    const bf16x8_t x1 = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 2 * q4 + 1]);
-    const bf16x8_t x2 = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 8 + 2 * q4]);
-    const bf16x8_t x3 = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 9 + 2 * q4]);
+    xf[j][0] = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 2 * q4]);
+    xf[j][1] = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 2 * q4 + 1]);
+    xf[j][2] = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 8 + 2 * q4]);
+    xf[j][3] = __builtin_bit_cast(bf16x8_t, xrow[cl * 16 + 9 + 2 * q4]);
 #pragma unroll
     for (int ts = 0; ts < NT; ++ts) {
       const int er = RS ? wn * TR * NT + ts * TR + wr : (n0 + wn * TR * NT + ts * TR + wr) / 32 - n0 / 32;
-      const float sc0 = block_scale(eb[er * 256 + cl * 4 + (q4 >> 1)]);
-      const float sc1 = block_scale(eb[er * 256 + cl * 4 + 2 + (q4 >> 1)]);
+      sc[j][ts][0] = block_scale(eb[er * 256 + cl * 4 + (q4 >> 1)]);
+      sc[j][ts][1] = block_scale(eb[er * 256 + cl * 4 + 2 + (q4 >> 1)]);
+    }
+  }
+  auto chunk = [&](int j) {
+    const int cl = wk + j * NWK;
+    // (a chunk past the range was not loaded: its LDS holds nothing defined)
+    if (c_begin + cl >= c_end) return;
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) {
       const uint4* wt = wbase + (j * NT + ts) * TG + wr * 8;
       const uint4 a = wt[q4 ^ wsw], b = wt[(4 + q4) ^ wsw];
       f32x4_t c = acc[ts];
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(a.x, a.y, sc0), x0, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(a.z, a.w, sc0), x1, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(b.x, b.y, sc1), x2, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(b.z, b.w, sc1), x3, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(a.x, a.y, sc[j][ts][0]), xf[j][0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(a.z, a.w, sc[j][ts][0]), xf[j][1], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(b.x, b.y, sc[j][ts][1]), xf[j][2], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(b.z, b.w, sc[j][ts][1]), xf[j][3], c, 0, 0, 0);
       acc[ts] = c;
     }
   };
