@@ -254,7 +254,8 @@ BSFP8_API int bsfp8_reduce_quantize_mx(const float* part, int64_t S, int64_t M, 
                                        uint8_t* yq, uint8_t* ys, void* stream);
 
 /* Workspace bytes of bsfp8_gemm_mxfp8 for this shape and split_k (never 0 for a valid shape:
- * the fp32 results, one copy per split, pass through it). Nothing in it needs clearing. */
+ * the fp32 results, one copy per split, may pass through it). Nothing in it needs clearing; one
+ * workspace must not be used by two calls that can run at the same time. */
 BSFP8_API size_t bsfp8_workspace_bytes_mxfp8(int64_t M, int64_t G, int64_t N, int64_t K, int split_k);
 
 /* The GEMM of bsfp8_gemm with the MXFP8 epilogue: the fp32 results of the GEMM's plan for
@@ -266,7 +267,10 @@ BSFP8_API size_t bsfp8_workspace_bytes_mxfp8(int64_t M, int64_t G, int64_t N, in
  *   ws    : >= bsfp8_workspace_bytes_mxfp8(M, G, N, K, split_k) bytes (device, 16-byte aligned).
  *   yq    : uint8_t e4m3 codes [M][G*N] (device, contiguous, 16-byte aligned).
  *   ys    : uint8_t scale bytes [M][G*N/32] (device, contiguous).
- * Two kernels on `stream`: the GEMM, then the epilogue. */
+ * For a decode plan with one split (up to 16 rows, K a multiple of 128, at most 32 chunks) one
+ * fused kernel computes and quantises 32 output columns per workgroup; otherwise two kernels run
+ * on `stream`, the GEMM (writing the fp32 results into ws) and the epilogue. Both forms give the
+ * same bits. */
 BSFP8_API int bsfp8_gemm_mxfp8(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
                                const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes,
                                uint8_t* yq, uint8_t* ys, void* stream);
