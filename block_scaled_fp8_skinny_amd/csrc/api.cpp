@@ -88,15 +88,18 @@ int check_gemm_mx(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int64_t M, 
   return BSFP8_OK;
 }
 
-// The GEMM with the MXFP8 epilogue: fused into one kernel for a decode plan with one split (when
-// `fuse`), else the GEMM into the workspace (fp32 results or split partials) and the epilogue
-// kernel.
+// The GEMM with the MXFP8 epilogue, when `fuse`: the fused decode kernel for a decode plan with one
+// split, or the plan's own kernel quantising its output where its tile holds whole 32-column
+// blocks; otherwise the GEMM into the workspace (fp32 results or split partials) and the
+// epilogue kernel.
 int run_gemm_mxfp8(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,
                    const uint8_t* e, void* ws, size_t ws_bytes, uint8_t* yq, uint8_t* ys, bool fuse,
                    hipStream_t stream) {
   if (!ws || ws_bytes < gemm_partials_bytes(s, p) || !aligned16(ws)) return BSFP8_EWORKSPACE;
   if (fuse) {
-    const int fst = launch_decode_mxfp8(s, p, x, q, e, yq, ys, stream);
+    int fst = launch_decode_mxfp8(s, p, x, q, e, yq, ys, stream);
+    if (fst != BSFP8_EINVAL) return fst;
+    fst = launch_gemm(s, p, x, q, e, nullptr, nullptr, 1, stream, 0, yq, ys);   // in-kernel epilogue
     if (fst != BSFP8_EINVAL) return fst;
   }
   int st = launch_gemm(s, p, x, q, e, ws, nullptr, 1, stream, /*partials=*/1);

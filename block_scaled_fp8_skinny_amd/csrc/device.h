@@ -28,6 +28,8 @@ struct KParams {
   unsigned long long* slots;             // pairwise-combine slots (splits > 1)
   float* part;                           // non-null: each split stores its fp32 partial here,
                                          // [splits][M][G][N], for a later kernel to sum
+  uint8_t* yq;                           // non-null (one split, 32-column tiles): MXFP8 output,
+  uint8_t* ys;                           // codes [M][G*N] and scale bytes [M][G*N/32], not y
   int64_t ldx;
   uint32_t x_bytes, q_bytes, e_bytes;    // extents of the three buffer descriptors
   int M, G, N, K;
@@ -180,33 +182,78 @@ __device__ __forceinline__ void wait_vmcnt_le() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// e4m3 code of an fp32 value with |v| <= 448, round half to even (including the e4m3
-// subnormals, quantum 2^-9); magnitudes below 2^-10 give a signed zero.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80;
-  const uint32_t a = u & 0x7FFFFFFF;
-  const uint32_t E = a >> 23;
-  uint32_t code;
-  if (E >= 121) {                                   // >= 2^-6: e4m3 normal range
-    const uint32_t keep = ((E - 120) << 3) | ((a >> 20) & 7);
-    const uint32_t rest = a & 0xFFFFF;
-    code = keep + ((rest > 0x80000u || (rest == 0x80000u && (keep & 1))) ? 1 : 0);
-  } else if (E == 0) {
-    code = 0;                                       // fp32 zero/subnormal: far below 2^-10
-  } else {
-    const uint32_t full = (a & 0x7FFFFF) | 0x800000; // value = full * 2^(E - 150)
-    const uint32_t sh = 141 - E;                     // quantum 2^-9 = 2^(E-150) * 2^sh
-    if (sh > 24) {
-      code = 0;
-    } else {
-      const uint32_t keep = full >> sh;
-      const uint32_t rest = full & ((1u << sh) - 1);
-      const uint32_t half = 1u << (sh - 1);
-      code = keep + ((rest > half || (rest == half && (keep & 1))) ? 1 : 0);
-    }
+// e4m3 codes by the hardware's conversions, two values per instruction, round half to even:
+//  * e4m3x4: four fp32 values with |v| <= 448 (v_cvt_pk_fp8_f32), byte i = value i;
+//  * e4m3x2_bf16: a bf16 pair divided by 2^k, k = the scale operand's exponent field - 127 (field
+//    0 reads as 2^-127; v_cvt_scalef32_pk_fp8_bf16), for results within +-448, in bits 0..15.
+// Both were compared on the GPU with an integer RNE encoder written from the e4m3 definition
+// (ties to the even code, subnormal quantum 2^-9, magnitudes below 2^-10 to a signed zero): the
+// first over every fp32 value in [-448, 448], the second over every finite bf16 value and every
+// k in [-127, 127]; no difference.
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+}
+
+__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t pair, float scale) {
+  const s16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2_t{0, 0}, __builtin_bit_cast(bf16x2_t, pair),
+                                                             scale, false);
+  return (uint32_t)(uint16_t)r[0];
+}
+
+// One MX block (32 consecutive outputs of a row, OCP MX v1.0 MXFP8 rule) held by the four lanes
+// r16 + 16*q4 of a wave, eight fp32 values each: lo = columns 4*q4 .. +3, hi = 16 + 4*q4 .. +3 of
+// the block. Returns the lane's eight e4m3 codes (lo in the first dword) and the block's scale
+// byte: s = floor(log2 amax) - 8 from the fp32 exponent field, clamped below at -127; values
+// scaled by the exact power of two, saturated at +-448 and rounded to nearest even (e4m3x4); a
+// block holding inf or NaN gets byte 255 and NaN codes. Every lane of the wave must take part.
+__device__ __forceinline__ uint8_t mx_block_codes(const f32x4_t& lo, const f32x4_t& hi, uint32_t& c_lo,
+                                                  uint32_t& c_hi) {
+  uint32_t u[8], amax = 0, nonfinite = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u[i] = __float_as_uint(i < 4 ? lo[i] : hi[i - 4]);
+    const uint32_t mag = u[i] & 0x7FFFFFFFu;
+    nonfinite |= mag >= 0x7F800000u ? 1u : 0u;
+    amax = mag > amax ? mag : amax;
   }
-  return sign | code;
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)amax, off);
+    amax = o > amax ? o : amax;
+    nonfinite |= (uint32_t)__shfl_xor((int)nonfinite, off);
+  }
+  const int E = (int)(amax >> 23);
+  int s = E == 0 ? -127 : E - 135;
+  s = s < -127 ? -127 : s;
+  float sv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sv[i] = fminf(fmaxf(ldexpf(__uint_as_float(u[i]), -s), -448.f), 448.f);
+  c_lo = e4m3x4(sv[0], sv[1], sv[2], sv[3]);
+  c_hi = e4m3x4(sv[4], sv[5], sv[6], sv[7]);
+  if (nonfinite) {                                  // NaN codes carrying each entry's sign
+    uint32_t nl = 0, nh = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nl |= ((u[i] >> 31) ? 0xFFu : 0x7Fu) << (8 * i);
+      nh |= ((u[i + 4] >> 31) ? 0xFFu : 0x7Fu) << (8 * i);
+    }
+    c_lo = nl;
+    c_hi = nh;
+  }
+  return nonfinite ? (uint8_t)255 : (uint8_t)(s + 127);
+}
+
+// Store one lane's share of an MX block of row m, group g, starting at output column n0 (a
+// multiple of 32): codes [M][G*N], scale bytes [M][G*N/32].
+__device__ __forceinline__ void store_mx_block(uint8_t* yq, uint8_t* ys, int m, int g, int G, int N, int n0,
+                                               int q4, uint32_t c_lo, uint32_t c_hi, uint8_t scale) {
+  uint8_t* row = yq + ((size_t)m * G + g) * N + n0;
+  *reinterpret_cast<uint32_t*>(row + q4 * 4) = c_lo;
+  *reinterpret_cast<uint32_t*>(row + 16 + q4 * 4) = c_hi;
+  if (q4 == 0) ys[((size_t)m * G + g) * (N / 32) + n0 / 32] = scale;
 }
 
 }  // namespace

@@ -108,18 +108,14 @@ __global__ void __launch_bounds__(256) reduce_quantize_mx_kernel(const float* __
   const int E = (int)(amax >> 23);
   int s = E == 0 ? -127 : E - 135;
   s = s < -127 ? -127 : s;
-  uint32_t codes = 0;
+  float sv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t c;
-    if (nonfinite) {
-      c = (u[i] >> 31) ? 0xFFu : 0x7Fu;
-    } else {
-      float sv = ldexpf(v[i], -s);
-      sv = fminf(fmaxf(sv, -448.f), 448.f);         // saturating conversion
-      c = e4m3_rne(sv);
-    }
-    codes |= c << (8 * i);
+  for (int i = 0; i < 4; ++i) sv[i] = fminf(fmaxf(ldexpf(v[i], -s), -448.f), 448.f);   // saturating
+  uint32_t codes = e4m3x4(sv[0], sv[1], sv[2], sv[3]);
+  if (nonfinite) {
+    codes = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) codes |= ((u[i] >> 31) ? 0xFFu : 0x7Fu) << (8 * i);
   }
   if (live) {
     *reinterpret_cast<uint32_t*>(yq + blk * EP_BLOCK + sub * 4) = codes;
@@ -302,43 +298,10 @@ __global__ void __launch_bounds__(WAVE * NWK) decode_mxfp8_kernel(DecodeMxParams
   }
   // (7) MX block of row m = m0 + r16: lane (r16, q4) holds columns q4*4 .. +3 (tile A) and
   //     16 + q4*4 .. +3 (tile B); the four lanes of a row are r16 + 16*q4
-  uint32_t u[8], amax = 0, nonfinite = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    u[i] = __float_as_uint(acc[i >> 2][i & 3]);
-    const uint32_t mag = u[i] & 0x7FFFFFFFu;
-    nonfinite |= mag >= 0x7F800000u ? 1u : 0u;
-    amax = mag > amax ? mag : amax;
-  }
-#pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)amax, off);
-    amax = o > amax ? o : amax;
-    nonfinite |= (uint32_t)__shfl_xor((int)nonfinite, off);
-  }
-  const int E = (int)(amax >> 23);
-  int s = E == 0 ? -127 : E - 135;
-  s = s < -127 ? -127 : s;
-  uint32_t codes[2] = {0, 0};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t c;
-    if (nonfinite) {
-      c = (u[i] >> 31) ? 0xFFu : 0x7Fu;
-    } else {
-      float sv = ldexpf(__uint_as_float(u[i]), -s);
-      sv = fminf(fmaxf(sv, -448.f), 448.f);
-      c = e4m3_rne(sv);
-    }
-    codes[i >> 2] |= c << (8 * (i & 3));
-  }
+  uint32_t c_lo, c_hi;
+  const uint8_t sb = mx_block_codes(acc[0], acc[1], c_lo, c_hi);
   const int m = m0 + r16;
-  if (r16 < XR && m < M) {
-    uint8_t* row = p.yq + ((size_t)m * G + g) * N + n0;
-    *reinterpret_cast<uint32_t*>(row + q4 * 4) = codes[0];
-    *reinterpret_cast<uint32_t*>(row + 16 + q4 * 4) = codes[1];
-    if (q4 == 0) p.ys[((size_t)m * G + g) * (N / 32) + n0 / 32] = nonfinite ? (uint8_t)255 : (uint8_t)(s + 127);
-  }
+  if (r16 < XR && m < M) store_mx_block(p.yq, p.ys, m, g, G, N, n0, q4, c_lo, c_hi, sb);
 }
 
 }  // namespace

@@ -684,6 +684,36 @@ gemm_rows_kernel(KParams p) {
     for (int i = 0; i < TPW; ++i) v4[i] = acc[i / NT][i % NT];
   }
 
+  // MXFP8 output (one split): wave w finishes the 32-column blocks of strips w, w + NWK, ...,
+  // adding each tile's wave partials in the same ascending order as above, and quantises them
+  if (p.yq) {
+    if constexpr (NT % 2 == 0) {
+      constexpr int NBLK = NT / 2;
+      for (int j = wk; j < MT * NBLK; j += NWK) {
+        const int mt = j / NBLK, bk = j % NBLK;
+        f32x4_t half[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int tt = mt * NT + 2 * bk + h;
+          if constexpr (NWK > 1) {
+            const f32x4_t* red = reinterpret_cast<const f32x4_t*>(xs);
+            f32x4_t v = red[tt * WAVE + lane];
+#pragma unroll
+            for (int w = 1; w < NWK; ++w) v += red[w * XG + tt * WAVE + lane];
+            half[h] = v;
+          } else {
+            half[h] = acc[mt][2 * bk + h];
+          }
+        }
+        uint32_t c_lo, c_hi;
+        const uint8_t sb = mx_block_codes(half[0], half[1], c_lo, c_hi);
+        const int m = m0 + mt * 16 + r16;
+        if (m < M) store_mx_block(p.yq, p.ys, m, g, G, N, n0 + 32 * bk, q4, c_lo, c_hi, sb);
+      }
+    }
+    return;
+  }
+
   if (p.splits == 1) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -749,7 +779,6 @@ template <int MT, int NT, int NWM, int NWN, int D, int GI>
 __global__ void __launch_bounds__(WAVE * NWM * NWN)
 gemm_tile_kernel(KParams p) {
   constexpr int NWAVE = NWM * NWN;
-  constexpr int NTHR = WAVE * NWAVE;
   constexpr int BM = 16 * MT * NWM;
   constexpr int NB = 16 * NT * NWN;
   constexpr int XST = BM * 16;                      // 16-byte granules of an X stage
@@ -906,6 +935,23 @@ gemm_tile_kernel(KParams p) {
     if constexpr (GI > 3) step(j0 + 3, std::integral_constant<int, 3 % GI>{});
   }
   wait_vmcnt_le<0>();                               // no load may still be writing LDS at exit
+
+  // MXFP8 output (one split): the wave's sub-tile holds whole 32-column blocks (tiles 2b, 2b+1)
+  if (p.yq) {
+    if constexpr (NT % 2 == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = m0 + wm * 16 * MT + mt * 16 + r16;
+#pragma unroll
+        for (int bk = 0; bk < NT / 2; ++bk) {
+          uint32_t c_lo, c_hi;
+          const uint8_t sb = mx_block_codes(acc[mt][2 * bk], acc[mt][2 * bk + 1], c_lo, c_hi);
+          if (m < M) store_mx_block(p.yq, p.ys, m, g, G, N, n0 + wn * 16 * NT + 32 * bk, q4, c_lo, c_hi, sb);
+        }
+      }
+    }
+    return;
+  }
 
   // output: this wave's sub-tile, or its fp32 partial for the reduce kernel
   float* const part = reinterpret_cast<float*>(p.slots);
@@ -1188,6 +1234,8 @@ gemm_slab_kernel(KParams p) {
   static_assert(S >= 2 && (S - 2) * PC <= 63, "ring depth, counter range");
   static_assert(NB % 32 == 0, "whole exponent block rows");
   static_assert((NWK - 1) * NWM * NWN * TILES * WAVE * 16 <= S * (XG + WGR) * 16, "reduction fits the ring");
+  // MXFP8 output in the kernel: whole 32-column blocks, every wave's partial tiles in the ring
+  constexpr bool MX_OK = NB % 32 == 0 && NWK * NWM * NWN * TILES * WAVE * 16 <= S * (XG + WGR) * 16;
   __shared__ uint4 ring[S][XG + WGR];
   __shared__ uint8_t e_lds[EROWS * ESTR];
 
@@ -1314,6 +1362,42 @@ gemm_slab_kernel(KParams p) {
     }
   }
   wait_vmcnt_le<0>();                               // no load may still be writing LDS
+
+  // MXFP8 output (one split): every wave parks its tiles in the ring; each job (a 16-row strip
+  // and a 32-column block) adds the waves' tiles of its two 16-column halves in ascending wave
+  // order - the sums of the bf16/fp32 path below - and quantises the block
+  if (p.yq) {
+    if constexpr (MX_OK) {
+      lds_barrier();                                // every wave is done with the ring
+      f32x4_t* red = reinterpret_cast<f32x4_t*>(&ring[0][0]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ts = 0; ts < NT; ++ts)
+          red[((wk * NWM * NWN + wmn) * TILES + mt * NT + ts) * WAVE + lane] = acc[mt][ts];
+      __syncthreads();
+      constexpr int NBLK = NB / 32;
+      constexpr int JOBS = NWM * MT * NBLK;
+      for (int j = wave; j < JOBS; j += NWAVE) {
+        const int jm = j / (MT * NBLK), mt = (j / NBLK) % MT, bk = j % NBLK;
+        f32x4_t half[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c16 = 32 * bk + 16 * h;         // first column of the half in the tile
+          const int base = (jm * NWN + c16 / (16 * NT)) * TILES + mt * NT + (c16 / 16) % NT;
+          f32x4_t v = red[base * WAVE + lane];
+#pragma unroll
+          for (int w = 1; w < NWK; ++w) v += red[(w * NWM * NWN * TILES + base) * WAVE + lane];
+          half[h] = v;
+        }
+        uint32_t c_lo, c_hi;
+        const uint8_t sb = mx_block_codes(half[0], half[1], c_lo, c_hi);
+        const int m = m0 + jm * 16 * MT + mt * 16 + r16;
+        if (m < M) store_mx_block(p.yq, p.ys, m, g, G, N, n0 + 32 * bk, q4, c_lo, c_hi, sb);
+      }
+    }
+    return;
+  }
 
   // waves along K: ascending-order sum through LDS (aliasing the ring)
   if constexpr (NWK > 1) {
@@ -1672,8 +1756,30 @@ int plan_gemm_row32(const GemmShape& s, int split_k, GemmPlan* plan) {
   return plan_with(s, cfg, cps, plan);
 }
 
+// Whether a configuration can quantise its own output to MXFP8 (one split): its workgroup tile
+// has whole 32-column blocks that one wave can finish (the tile and rows kernels with an even
+// number of 16-column tiles per wave, the slab kernel when every wave's partial tiles fit its
+// ring). The kernels test the same conditions at compile time.
+bool mx_fusable(const Config& c) {
+  const int NB = c.TR * c.NT * c.NWN;
+  if (NB % 32) return false;
+  switch (c.kind) {
+    case TILE:
+    case ROWS:
+      return c.NT % 2 == 0;
+    case SLAB: {
+      const int BM = 16 * c.MT * c.NWM, XG = BM * 64, WGR = NB * 32;
+      return c.NWK * c.NWM * c.NWN * (c.MT * c.NT) * WAVE * 16 <= c.CW * (XG + WGR) * 16;
+    }
+    default:
+      return false;
+  }
+}
+
 int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,
-                const uint8_t* e, void* ws, void* y, int out_f32, hipStream_t stream, int partials) {
+                const uint8_t* e, void* ws, void* y, int out_f32, hipStream_t stream, int partials,
+                uint8_t* yq, uint8_t* ys) {
+  if (yq && (p.splits != 1 || partials || !mx_fusable(kConfigs[p.cfg]))) return BSFP8_EINVAL;
   if (partials) {
     // fp32 results for a later kernel: the sum itself with one split, else every split's partial
     if (p.splits == 1) {
@@ -1707,6 +1813,8 @@ int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const 
   k.nblocks = p.nblocks;
   k.out_f32 = out_f32;
   if (partials && p.splits > 1 && kConfigs[p.cfg].kind != TILE) k.part = reinterpret_cast<float*>(ws);
+  k.yq = yq;
+  k.ys = ys;
   k.levels = tree_levels(p.splits);
   int base = 0, lv = 0;
   for (int c2 = p.splits; c2 > 1; c2 = (c2 + 1) >> 1) {

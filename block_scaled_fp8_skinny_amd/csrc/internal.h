@@ -45,8 +45,12 @@ int gemm_config_info(int cfg, int* out);
 // partials != 0: leave fp32 results in ws for a later kernel instead of writing y: the result
 // itself when the plan has one split, else the partial of every split ([splits][M][G][N]), in
 // the order gemm_partials_order names.
+// yq, ys non-null: the kernel quantises its fp32 results to MXFP8 itself (codes [M][G*N], scale
+// bytes [M][G*N/32]) instead of writing y; only for one split and a configuration whose tile
+// holds whole 32-column blocks (else BSFP8_EINVAL, before anything is launched).
 int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const uint8_t* q,
-                const uint8_t* e, void* ws, void* y, int out_f32, hipStream_t stream, int partials = 0);
+                const uint8_t* e, void* ws, void* y, int out_f32, hipStream_t stream, int partials = 0,
+                uint8_t* yq = nullptr, uint8_t* ys = nullptr);
 // Order in which a plan's own combine adds its split partials: BSFP8_SUM_ASCENDING (tile kernel
 // and its reduce kernel) or BSFP8_SUM_PAIRWISE (the one-pass kernels' exchange tree).
 int gemm_partials_order(const GemmPlan& p);

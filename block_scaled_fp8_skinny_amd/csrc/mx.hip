@@ -10,7 +10,7 @@
 // Design (gfx950, wave64):
 //  * quantize_mx_kernel: four lanes per 32-value block (eight values each), amax by two lane
 //    exchanges, the scale exponent read off the bf16 exponent field, each element scaled by an
-//    exact power of two and rounded with the integer e4m3 encoder shared with the twin encoder.
+//    exact power of two, saturated and rounded by the hardware conversion (e4m3x4, device.h).
 //  * gemm_mx_kernel: v_mfma_scale_f32_16x16x128_f8f6f4 takes both operands as e4m3 codes with
 //    one E8M0 scale per 32 values of each row, so there is no dequantisation at all. Measured
 //    operand layout: a lane (r16, q) of a 128-wide chunk holds k = 16q + [0, 16) and
@@ -79,20 +79,18 @@ __global__ void __launch_bounds__(256) quantize_mx_kernel(const uint16_t* x, int
   const int E = (int)(amax >> 7);
   int s = E == 0 ? -127 : E - 135;
   s = s < -127 ? -127 : (s > 127 ? 127 : s);
-  uint32_t codes[8];
+  float sv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (nonfinite) {
-      codes[i] = (h[i] & 0x8000) ? 0xFFu : 0x7Fu;
-    } else {
-      float sv = ldexpf(__uint_as_float(h[i] << 16), -s);   // exact: a power-of-two scaling
-      sv = fminf(fmaxf(sv, -448.f), 448.f);                   // saturating conversion
-      codes[i] = e4m3_rne(sv);
-    }
+  for (int i = 0; i < 8; ++i)   // exact power-of-two scaling, then the saturating conversion
+    sv[i] = fminf(fmaxf(ldexpf(__uint_as_float(h[i] << 16), -s), -448.f), 448.f);
+  uint2 o = make_uint2(e4m3x4(sv[0], sv[1], sv[2], sv[3]), e4m3x4(sv[4], sv[5], sv[6], sv[7]));
+  if (nonfinite) {
+    uint32_t nan[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) nan[i >> 2] |= ((h[i] & 0x8000) ? 0xFFu : 0x7Fu) << (8 * (i & 3));
+    o = make_uint2(nan[0], nan[1]);
   }
   if (live) {
-    const uint2 o = make_uint2(codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24),
-                               codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24));
     *reinterpret_cast<uint2*>(xq + m * L + cb * MX_BLOCK + part * 8) = o;
     if (part == 0) xs[m * bpr + cb] = nonfinite ? (uint8_t)255 : (uint8_t)(s + 127);
   }

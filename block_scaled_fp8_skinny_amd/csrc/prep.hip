@@ -45,8 +45,6 @@ __device__ __forceinline__ int block_exp(uint32_t amax_bits) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-typedef short s16x2_t __attribute__((ext_vector_type(2)));
-
 __global__ void __launch_bounds__(256) make_twin_kernel(const uint16_t* w, int64_t D, int64_t nstrips,
                                                         int64_t nwaves, uint8_t* q, uint8_t* e,
                                                         uint8_t* okv, unsigned long long* bad) {
@@ -89,9 +87,7 @@ __global__ void __launch_bounds__(256) make_twin_kernel(const uint16_t* w, int64
     uint32_t c[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const s16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2_t{0, 0}, __builtin_bit_cast(bf16x2_t, d[j]),
-                                                                 scale, false);
-      c[j] = (uint32_t)(uint16_t)r[0];
+      c[j] = e4m3x2_bf16(d[j], scale);
       const uint32_t back = bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], scale, false));
       same &= back == d[j] ? 1u : 0u;
     }
@@ -118,7 +114,8 @@ __global__ void __launch_bounds__(256) make_twin_kernel(const uint16_t* w, int64
 // docs/tp4-adapters.md", row draft_main_proj: e4m3 with per-(row, 32-column) power-of-two
 // scales, checked to reproduce the weight exactly). The per-block rule is the 32x32 encoder's.
 // Two lanes per 1x32 block, sixteen values each; a block's 64 bytes are contiguous, so lane t
-// reads values 16t .. 16t + 15 of the flat weight.
+// reads values 16t .. 16t + 15 of the flat weight. Codes and rebuild by the hardware's scaled
+// conversions, as in make_twin_kernel.
 // ---------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) make_twin_row32_kernel(const uint16_t* w, int64_t nblocks, uint8_t* q,
                                                               uint8_t* e, uint8_t* okv, unsigned long long* bad) {
@@ -149,27 +146,19 @@ __global__ void __launch_bounds__(256) make_twin_row32_kernel(const uint16_t* w,
   const uint32_t o = (uint32_t)__shfl_xor((int)amax, 1);
   amax = o > amax ? o : amax;
   nonfinite |= (uint32_t)__shfl_xor((int)nonfinite, 1);
-  const int eb = block_exp(amax);
+  const int eb = block_exp(nonfinite ? 0u : amax);
   const uint32_t eb_byte = (uint32_t)(eb + 127);
-  const float back_scale = __uint_as_float(eb_byte << 23);   // factor 2^e for the rebuild
-  uint32_t codes[16];
+  const float scale = __uint_as_float(eb_byte << 23);   // 2^e, for the codes and the rebuild
+  // codes of each bf16 pair (w / 2^e, RNE; within +-448 by the choice of e), rebuilt and compared
+  uint32_t c2[8], same = 1;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) codes[i] = e4m3_rne(ldexpf(__uint_as_float(h[i] << 16), -eb));
-  uint32_t same = 1;
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    const bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[i] | (codes[i + 1] << 8),
-                                                                back_scale, false);
-    const uint32_t rb2 = bits_of(r);
-    same &= ((rb2 & 0xFFFF) == h[i]) && ((rb2 >> 16) == h[i + 1]) ? 1u : 0u;
+  for (int i = 0; i < 8; ++i) {
+    c2[i] = e4m3x2_bf16(d[i], scale);
+    same &= bits_of(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c2[i], scale, false)) == d[i] ? 1u : 0u;
   }
   same &= (uint32_t)__shfl_xor((int)same, 1);
   const bool ok = same && !nonfinite;
-  uint32_t packed[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    packed[i] = codes[4 * i] | (codes[4 * i + 1] << 8) | (codes[4 * i + 2] << 16) | (codes[4 * i + 3] << 24);
-  uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  uint4 out = make_uint4(c2[0] | (c2[1] << 16), c2[2] | (c2[3] << 16), c2[4] | (c2[5] << 16), c2[6] | (c2[7] << 16));
   if (nonfinite) out = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
   if (live) {
     *reinterpret_cast<uint4*>(q + t * 16) = out;

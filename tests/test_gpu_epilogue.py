@@ -188,6 +188,35 @@ def test_fused_decode_equals_the_two_kernel_form(M, G, N, K):
     print(check_mxfp8(yq.cpu().numpy(), ys.cpu().numpy(), Y, A, K, 1), flush=True)
 
 
+# plans whose own kernel quantises its output (one split, 32-column blocks per wave or per
+# workgroup): the slab kernel (33..64 rows), the rows kernel (65..256 rows) and the tile kernel
+# (wide weights); the explicit configuration call takes the two-kernel form of the same plan
+IN_KERNEL_CASES = [(33, 2, 1024, 4096, 5), (64, 1, 256, 2048, 5), (65, 2, 1024, 4096, 2), (128, 1, 512, 1024, 2),
+                   (200, 1, 256, 1152, 2), (256, 1, 64, 256, 2), (16, 1, 16384, 1024, 3), (64, 1, 16384, 512, 3),
+                   (100, 1, 16384, 256, 3)]
+
+
+@pytest.mark.parametrize("M,G,N,K,kind", IN_KERNEL_CASES)
+def test_in_kernel_epilogue_equals_the_two_kernel_form(M, G, N, K, kind):
+    r = S.rng(9600 + M + N)
+    x = S.bf16_normal(r, (M, G * K))
+    q = S.e4m3_codes(r, (G, N, K))
+    e = S.exponent_bytes(r, (G, N // 32, K // 32), 112, 126)
+    plan = B.bsfp8_plan_info(M, G, N, K, path=3)
+    info = B.bsfp8_config_info(plan["cfg"])
+    print(f"in-kernel M={M} G={G} N={N} K={K} plan {plan} kind {info['kind']}", flush=True)
+    assert info["kind"] == kind and plan["splits"] == 1
+    xt, qt, et = to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e)
+    yq, ys = B.bsfp8_gemm_mxfp8(xt, qt, et)
+    q2, s2 = B.bsfp8_gemm_mxfp8_config(xt, qt, et, plan["cfg"], plan["cps"])
+    torch.cuda.synchronize()
+    assert torch.equal(ys, s2) and torch.equal(yq, q2)
+    rows = list(range(0, M, max(1, M // 7)))[:8]
+    W = oracle.dequant_values(q, e)
+    Y, A = _exact_and_absum(x[rows], W, np.abs(W), G, K)
+    print(check_mxfp8(yq.cpu().numpy()[rows], ys.cpu().numpy()[rows], Y, A, K, 1), flush=True)
+
+
 def test_gemm_mxfp8_graph_replay_and_repeats(wo_a_weight):
     d, W, Wabs, qt, et = wo_a_weight
     M, G, N, K = 6, 2, 1024, 4096
