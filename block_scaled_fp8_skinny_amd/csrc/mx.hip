@@ -136,7 +136,11 @@ gemm_mx_kernel(MxParams p) {
   constexpr int XI = BM / RPL, WI = NB / RPL;       // loads per stage
   constexpr int PCX = XI / NWAVE, PCW = WI / NWAVE;
   constexpr bool XS_STAGED = SC >= 4;               // activation scales travel with the stage
-  constexpr int XSI = (BM * SC + 63) / 64;          // scale-word loads per stage (64 words each)
+  // Words per row of a staged scale array: odd where an even count would put rows r and r + 8 of
+  // a fragment read in one bank (the 16 rows then fall in 16 distinct banks; the extra word of a
+  // row is filled with zeros and never read).
+  constexpr int SCW = SC >= 8 ? SC + 1 : SC;
+  constexpr int XSI = (BM * SCW + 63) / 64;         // scale-word loads per stage (64 words each)
   constexpr int PCS = XS_STAGED ? (XSI + NWAVE - 1) / NWAVE : 0;   // per wave (surplus: dummies)
   constexpr int XSG = PCS * NWAVE * 16;             // granules of the scale part (a 256-byte slot per load)
   constexpr int PC = PCX + PCW + PCS;
@@ -150,7 +154,7 @@ gemm_mx_kernel(MxParams p) {
   static_assert((NWK - 1) * NWM * NWN * TILES * WAVE <= S * (XG + WGR + XSG), "reduction fits the ring");
   __shared__ uint4 ring[S][XG + WGR + XSG];
   __shared__ uint32_t e_lds[EROWS * MX_MAX_CH];
-  __shared__ uint32_t xs_lds[XS_STAGED ? 1 : BM * MX_MAX_CH];
+  __shared__ uint32_t xs_lds[XS_STAGED ? 1 : BM * (MX_MAX_CH + 1) + 64];
 
   prefetch_mx_args(p);
   const int tid = threadIdx.x;
@@ -182,15 +186,19 @@ gemm_mx_kernel(MxParams p) {
     const uint32_t off = (uint32_t)((g * (N / 32) + n0 / 32 + er) * KB + lane * 4);
     lds_load4(re, lds_addr(e_lds + er * MX_MAX_CH), lane < nch ? off : OOB);
   }
-  // (2) unless they travel with the stages: the activation scale words of the whole range, dense
-  //     [BM][nch] (word f is chunk f % nch of tile row f / nch)
+  // (2) unless they travel with the stages: the activation scale words of the whole range,
+  //     [BM][xst] with xst = nch rounded up to odd (word f is chunk f % xst of tile row f / xst;
+  //     chunk nch, when present, is zero). With an odd row stride the scale reads of 16
+  //     consecutive rows hit 16 distinct banks. The last load may fill up to 63 words past
+  //     BM * xst, which the array's size allows for.
+  const int xst = nch | 1;
   if constexpr (!XS_STAGED) {
-    for (int i = wave; i * 64 < BM * nch; i += NWAVE) {
+    for (int i = wave; i * 64 < BM * xst; i += NWAVE) {
       const int f = i * 64 + lane;
-      const int row = f / nch, c = f % nch;
+      const int row = f / xst, c = f % xst;
       const int m = m0 + row;
       const uint32_t off = (uint32_t)m * ldsx + (uint32_t)(g * KB + c * 4);
-      lds_load4(rs, lds_addr(xs_lds + i * 64), f < BM * nch && m < M ? off : OOB);
+      lds_load4(rs, lds_addr(xs_lds + i * 64), f < BM * xst && c < nch && m < M ? off : OOB);
     }
   }
 
@@ -216,17 +224,18 @@ gemm_mx_kernel(MxParams p) {
     wgran[u] = lslot ^ mx_swz<P>(row);
     woff[u] = (uint32_t)(g * N + n0 + row) * (uint32_t)K + 16 * wgran[u];
   }
-  // Scale load u of a stage: words i*64 .. i*64 + 63 (i = wave + u*NWAVE) of the stage's dense
-  // [BM][SC] array (row f / SC, chunk f % SC); loads with i >= XSI fill their slot with zeros.
+  // Scale load u of a stage: words i*64 .. i*64 + 63 (i = wave + u*NWAVE) of the stage's
+  // [BM][SCW] array (row f / SCW, chunk f % SCW; chunks SC .. SCW - 1 are padding); loads with
+  // i >= XSI fill their slot with zeros.
   uint32_t soff[PCS > 0 ? PCS : 1];
   int schunk[PCS > 0 ? PCS : 1];
   bool sok[PCS > 0 ? PCS : 1];
 #pragma unroll
   for (int u = 0; u < PCS; ++u) {
     const int f = (wave + u * NWAVE) * 64 + lane;
-    const int row = f / SC, m = m0 + row;
-    schunk[u] = f % SC;
-    sok[u] = f < BM * SC && m < M;
+    const int row = f / SCW, m = m0 + row;
+    schunk[u] = f % SCW;
+    sok[u] = f < BM * SCW && schunk[u] < SC && m < M;
     soff[u] = sok[u] ? (uint32_t)m * ldsx + (uint32_t)(g * KB + schunk[u] * 4) : 0u;
   }
   auto issue = [&](int j) {
@@ -270,7 +279,7 @@ gemm_mx_kernel(MxParams p) {
     const uint4* st = ring[j % S];
     const uint8_t* xsb = XS_STAGED ? reinterpret_cast<const uint8_t*>(st + XG + WGR)
                                    : reinterpret_cast<const uint8_t*>(xs_lds);
-    const int xrow_words = XS_STAGED ? SC : nch;    // words per row in the scale array read here
+    const int xrow_words = XS_STAGED ? SCW : xst;   // words per row in the scale array read here
     const int xcol = XS_STAGED ? 0 : j * SC;        // word of chunk cc of this stage
 #pragma unroll
     for (int cc = wk * CPW; cc < wk * CPW + CPW; ++cc) {
