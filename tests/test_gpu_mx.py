@@ -102,17 +102,19 @@ def test_gemm_mx_parity(M, G, N, K):
     print(f"M={M} G={G} N={N} K={K} cfg {B.bsfp8_mx_plan(M, G, N)}: {st}")
 
 
-def test_every_mx_configuration():
+@pytest.mark.parametrize("N,K", [(256, 640), (256, 1024), (128, 8192)])
+def test_every_mx_configuration(N, K):
     """Each compiled configuration on a shape with several m-blocks, a ragged last m-block and a
-    partial last ring stage, bf16 and fp32 outputs."""
-    G, N, K = 2, 256, 640
+    partial last ring stage, bf16 and fp32 outputs; K with an odd (5), an even (8) and the
+    largest (64) chunk count, which decide the row stride of the staged activation scales."""
+    G = 2
     for cfg in range(B.bsfp8_mx_num_configs()):
         info = B.bsfp8_mx_config_info(cfg)
         M = min(2 * info["BM"] - 3, 256)
-        xq, xs, q, e = _mx_inputs(8300 + cfg, M, G, N, K)
+        xq, xs, q, e = _mx_inputs(8300 + cfg + K, M, G, N, K)
         exact = MX.gemm_mx_exact_f64(xq, xs, G, N, K, q, e)
         absum = MX.abs_products_sum_mx(xq, xs, G, N, K, q, e)
-        print(f"mx cfg {cfg} {info} M {M}", flush=True)
+        print(f"mx cfg {cfg} {info} M {M} N {N} K {K}", flush=True)
         check_mx_bf16(bf16_bits(_gemm_mx(xq, xs, q, e, cfg)), exact, absum, K)
         rel = check_mx_f32(_gemm_mx(xq, xs, q, e, cfg, "f32").cpu().numpy(), exact, absum, K)
         print(f"    fp32 max |err|/sum|xw| = {rel:.3e} (2^{np.log2(max(rel, 1e-300)):.1f})")
