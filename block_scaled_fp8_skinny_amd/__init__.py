@@ -108,13 +108,68 @@ def _codes(q):
     return q
 
 
-def _need(t, dtype, name, cuda=True):
+def _need(t, dtype, name, cuda=True, numel=None, device=None):
+    """Type, placement and size checks of a tensor handed to the library. The library addresses
+    every buffer by the sizes it is given, so a buffer smaller than those sizes, or one on another
+    device, is refused here rather than read or written out of bounds."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if cuda and not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+
+
+def _out_dtype(out_dtype):
+    return OUT_F32 if out_dtype in ("f32", torch.float32, OUT_F32) else OUT_BF16
+
+
+def _operands(x, q, e, e_numel):
+    """Checked GEMM operands -> (x, M, ldx, q, G, N, K): q [G, N, K] codes, e exponent bytes of at
+    least e_numel(G, N, K) elements, x [M, >= G*K] (or [M, G, K]) on q's device."""
+    q = _codes(q)
+    if q.dim() != 3:
+        raise ValueError("q must be [G, N, K]")
+    _need(q, torch.uint8, "q")
+    G, N, K = q.shape
+    _need(e, torch.uint8, "e", numel=e_numel(G, N, K), device=q.device)
+    x, M, ldx = _x_view(x)
+    if x.device != q.device:
+        raise ValueError(f"x is on {x.device}, q on {q.device}")
+    cols = x.shape[1] * x.shape[2] if x.dim() == 3 else x.shape[1]
+    if cols < G * K:
+        raise ValueError(f"x has {cols} columns per row, needs G*K = {G * K}")
+    return x, M, ldx, q, G, N, K
+
+
+def _block_exps(G, N, K):
+    return G * (N // 32) * (K // 32)
+
+
+def _row_exps(G, N, K):
+    return G * N * (K // 32)
+
+
+def _out(out, M, G, N, od, device):
+    dtype = torch.float32 if od == OUT_F32 else torch.bfloat16
+    if out is None:
+        return torch.empty((M, G, N), dtype=dtype, device=device)
+    _need(out, dtype, "out", numel=M * G * N, device=device)
+    return out
+
+
+def _ws(ws, n, device):
+    """The caller's workspace (checked to hold n bytes) or a zero-filled one of n bytes."""
+    if ws is None:
+        return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+    _need(ws, torch.uint8, "ws", numel=n, device=device)
+    return ws
 
 
 # ------------------------------------------------------------------------------------------------
@@ -124,10 +179,12 @@ def bsfp8_scales_from_f32(scales, exp_out=None):
     """fp32 block scales [rows, cols] -> uint8 exponent bytes. Raises BsfpError(ESCALE) when any
     scale is not a positive finite power of two (the error carries .n_bad)."""
     _need(scales, torch.float32, "scales")
+    if scales.dim() != 2:
+        raise ValueError("scales must be [rows, cols]")
     rows, cols = scales.shape
     if exp_out is None:
         exp_out = torch.empty((rows, cols), dtype=torch.uint8, device=scales.device)
-    _need(exp_out, torch.uint8, "exp_out")
+    _need(exp_out, torch.uint8, "exp_out", numel=rows * cols, device=scales.device)
     bad = _I64(0)
     st = lib().bsfp8_scales_from_f32(_ptr(scales), rows, cols, _ptr(exp_out), ctypes.byref(bad), _stream(scales))
     if st < 0:
@@ -165,9 +222,11 @@ def make_twin(w):
 def bsfp8_pad_k_weight(q, e, K_pad):
     """Twin codes [G,N,K] and exponents [G,N/32,K/32] -> padded to K_pad (zero codes, byte 127)."""
     q = _codes(q)
+    if q.dim() != 3:
+        raise ValueError("q must be [G, N, K]")
     _need(q, torch.uint8, "q")
-    _need(e, torch.uint8, "e")
     G, N, K = q.shape
+    _need(e, torch.uint8, "e", numel=_block_exps(G, N, K), device=q.device)
     qp = torch.empty((G, N, K_pad), dtype=torch.uint8, device=q.device)
     ep = torch.empty((G, N // 32, K_pad // 32), dtype=torch.uint8, device=q.device)
     _check(lib().bsfp8_pad_k_weight(_ptr(q), _ptr(e), G, N, K, K_pad, _ptr(qp), _ptr(ep), _stream(q)),
@@ -193,9 +252,12 @@ def _x_view(x):
 def bsfp8_pad_k_input(x, G, K, K_pad, out=None):
     """x [M, >=G*K] (group g at columns g*K) -> [M, G*K_pad] with zero tails."""
     x, M, ldx = _x_view(x)
+    cols = x.shape[1] * x.shape[2] if x.dim() == 3 else x.shape[1]
+    if cols < G * K:
+        raise ValueError(f"x has {cols} columns per row, needs G*K = {G * K}")
     if out is None:
         out = torch.empty((M, G * K_pad), dtype=torch.bfloat16, device=x.device)
-    _need(out, torch.bfloat16, "out")
+    _need(out, torch.bfloat16, "out", numel=M * G * K_pad, device=x.device)
     _check(lib().bsfp8_pad_k_input(_ptr(x), ldx, M, G, K, K_pad, _ptr(out), _stream(x)), "bsfp8_pad_k_input")
     return out
 
@@ -203,12 +265,14 @@ def bsfp8_pad_k_input(x, G, K, K_pad, out=None):
 def bsfp8_dequant(q, e, out=None):
     """Twin -> bf16 weight [G, N, K], exact."""
     q = _codes(q)
+    if q.dim() != 3:
+        raise ValueError("q must be [G, N, K]")
     _need(q, torch.uint8, "q")
-    _need(e, torch.uint8, "e")
     G, N, K = q.shape
+    _need(e, torch.uint8, "e", numel=_block_exps(G, N, K), device=q.device)
     if out is None:
         out = torch.empty((G, N, K), dtype=torch.bfloat16, device=q.device)
-    _need(out, torch.bfloat16, "out")
+    _need(out, torch.bfloat16, "out", numel=G * N * K, device=q.device)
     _check(lib().bsfp8_dequant(_ptr(q), _ptr(e), G, N, K, _ptr(out), _stream(q)), "bsfp8_dequant")
     return out
 
@@ -227,18 +291,10 @@ def workspace(M, G, N, K, split_k=0, device="cuda"):
 
 
 def _gemm(entry, x, q, e, split_k, ws, out, out_dtype):
-    q = _codes(q)
-    _need(q, torch.uint8, "q")
-    _need(e, torch.uint8, "e")
-    G, N, K = q.shape
-    x, M, ldx = _x_view(x)
-    od = OUT_F32 if out_dtype in ("f32", torch.float32, OUT_F32) else OUT_BF16
-    if out is None:
-        out = torch.empty((M, G, N), dtype=torch.float32 if od == OUT_F32 else torch.bfloat16, device=x.device)
-    _need(out, torch.float32 if od == OUT_F32 else torch.bfloat16, "out")
-    if ws is None:
-        n = bsfp8_workspace_bytes(max(M, 1), G, N, K, split_k)
-        ws = torch.zeros(n, dtype=torch.uint8, device=x.device) if n else None
+    x, M, ldx, q, G, N, K = _operands(x, q, e, _block_exps)
+    od = _out_dtype(out_dtype)
+    out = _out(out, M, G, N, od, x.device)
+    ws = _ws(ws, bsfp8_workspace_bytes(max(M, 1), G, N, K, split_k), x.device)
     wsb = ws.numel() if ws is not None else 0
     fn = getattr(lib(), entry)
     _check(fn(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), split_k, _ptr(ws), wsb, _ptr(out), od, _stream(x)), entry)
@@ -284,15 +340,10 @@ def bsfp8_workspace_bytes_config(M, G, N, K, cfg, cps):
 
 
 def bsfp8_gemm_config(x, q, e, cfg, cps, ws=None, out=None, out_dtype="bf16"):
-    q = _codes(q)
-    G, N, K = q.shape
-    x, M, ldx = _x_view(x)
-    od = OUT_F32 if out_dtype in ("f32", torch.float32, OUT_F32) else OUT_BF16
-    if out is None:
-        out = torch.empty((M, G, N), dtype=torch.float32 if od == OUT_F32 else torch.bfloat16, device=x.device)
-    if ws is None:
-        n = bsfp8_workspace_bytes_config(max(M, 1), G, N, K, cfg, cps)
-        ws = torch.zeros(n, dtype=torch.uint8, device=x.device) if n else None
+    x, M, ldx, q, G, N, K = _operands(x, q, e, _block_exps)
+    od = _out_dtype(out_dtype)
+    out = _out(out, M, G, N, od, x.device)
+    ws = _ws(ws, bsfp8_workspace_bytes_config(max(M, 1), G, N, K, cfg, cps), x.device)
     wsb = ws.numel() if ws is not None else 0
     _check(lib().bsfp8_gemm_config(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), cfg, cps, _ptr(ws), wsb,
                                    _ptr(out), od, _stream(x)), "bsfp8_gemm_config")
@@ -308,32 +359,40 @@ def bsfp8_quantize_mx(x, L=None, xq=None, xs=None):
     if x.dim() == 3:
         raise ValueError("x must be [M, L]")
     L = x.shape[1] if L is None else L
+    if L > x.shape[1]:
+        raise ValueError(f"L = {L} exceeds the {x.shape[1]} columns of x")
     if xq is None:
         xq = torch.empty((M, L), dtype=torch.uint8, device=x.device)
     if xs is None:
         xs = torch.empty((M, L // 32), dtype=torch.uint8, device=x.device)
-    _need(xq, torch.uint8, "xq")
-    _need(xs, torch.uint8, "xs")
+    _need(xq, torch.uint8, "xq", numel=M * L, device=x.device)
+    _need(xs, torch.uint8, "xs", numel=M * (L // 32), device=x.device)
     _check(lib().bsfp8_quantize_mx(_ptr(x), ldx, M, L, _ptr(xq), _ptr(xs), _stream(x)), "bsfp8_quantize_mx")
     return xq, xs
 
 
 def _mx_args(xq, xs, q, e, out, out_dtype):
     q = _codes(q)
+    if q.dim() != 3:
+        raise ValueError("q must be [G, N, K]")
     _need(q, torch.uint8, "q")
-    _need(e, torch.uint8, "e")
+    G, N, K = q.shape
+    _need(e, torch.uint8, "e", numel=_block_exps(G, N, K), device=q.device)
     xq = _codes(xq)
     if xq.dtype != torch.uint8 or xq.dim() != 2 or xq.stride(1) != 1 or not xq.is_cuda:
         raise ValueError("xq must be a uint8 GPU tensor [M, ldq] with unit column stride")
+    if not isinstance(xs, torch.Tensor) or xs.dtype != torch.uint8 or xs.dim() != 2 or xs.stride(1) != 1:
+        raise ValueError("xs must be a uint8 tensor [M, ldq/32] with unit column stride")
+    if xq.device != q.device or xs.device != q.device:
+        raise ValueError("xq, xs, q and e must be on one GPU")
     M = xq.shape[0]
     ldq = xq.stride(0) if M > 1 else xq.shape[1]
-    if xs.dtype != torch.uint8 or xs.dim() != 2 or xs.stride(1) != 1 or (M > 1 and xs.stride(0) * 32 != ldq):
+    if M > 1 and xs.stride(0) * 32 != ldq:
         raise ValueError("xs must be uint8 [M, ldq/32] with rows aligned to the codes")
-    G, N, K = q.shape
-    od = OUT_F32 if out_dtype in ("f32", torch.float32, OUT_F32) else OUT_BF16
-    if out is None:
-        out = torch.empty((M, G, N), dtype=torch.float32 if od == OUT_F32 else torch.bfloat16, device=xq.device)
-    _need(out, torch.float32 if od == OUT_F32 else torch.bfloat16, "out")
+    if xs.shape[0] != M or xq.shape[1] < G * K or xs.shape[1] < G * K // 32:
+        raise ValueError(f"xq [M, >= G*K] and xs [M, >= G*K/32] needed (G*K = {G * K})")
+    od = _out_dtype(out_dtype)
+    out = _out(out, M, G, N, od, xq.device)
     return xq, q, M, ldq, G, N, K, od, out
 
 
@@ -397,18 +456,10 @@ def workspace_row32(M, G, N, K, split_k=0, device="cuda"):
 def bsfp8_gemm_row32(x, q, e, split_k=0, ws=None, out=None, out_dtype="bf16"):
     """Y [M, G, N] = per group X[:, g*K:(g+1)*K] @ W_g^T with W rebuilt from a row-scale twin
     (e [G, N, K/32]); up to 16 rows."""
-    q = _codes(q)
-    _need(q, torch.uint8, "q")
-    _need(e, torch.uint8, "e")
-    G, N, K = q.shape
-    x, M, ldx = _x_view(x)
-    od = OUT_F32 if out_dtype in ("f32", torch.float32, OUT_F32) else OUT_BF16
-    if out is None:
-        out = torch.empty((M, G, N), dtype=torch.float32 if od == OUT_F32 else torch.bfloat16, device=x.device)
-    _need(out, torch.float32 if od == OUT_F32 else torch.bfloat16, "out")
-    if ws is None:
-        n = bsfp8_workspace_bytes_row32(max(M, 1), G, N, K, split_k)
-        ws = torch.zeros(n, dtype=torch.uint8, device=x.device) if n else None
+    x, M, ldx, q, G, N, K = _operands(x, q, e, _row_exps)
+    od = _out_dtype(out_dtype)
+    out = _out(out, M, G, N, od, x.device)
+    ws = _ws(ws, bsfp8_workspace_bytes_row32(max(M, 1), G, N, K, split_k), x.device)
     wsb = ws.numel() if ws is not None else 0
     _check(lib().bsfp8_gemm_row32(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), split_k, _ptr(ws), wsb, _ptr(out), od,
                                   _stream(x)), "bsfp8_gemm_row32")
@@ -416,15 +467,10 @@ def bsfp8_gemm_row32(x, q, e, split_k=0, ws=None, out=None, out_dtype="bf16"):
 
 
 def bsfp8_gemm_row32_config(x, q, e, cfg, cps, ws=None, out=None, out_dtype="bf16"):
-    q = _codes(q)
-    G, N, K = q.shape
-    x, M, ldx = _x_view(x)
-    od = OUT_F32 if out_dtype in ("f32", torch.float32, OUT_F32) else OUT_BF16
-    if out is None:
-        out = torch.empty((M, G, N), dtype=torch.float32 if od == OUT_F32 else torch.bfloat16, device=x.device)
-    if ws is None:
-        n = bsfp8_workspace_bytes_config(max(M, 1), G, N, K, cfg, cps)
-        ws = torch.zeros(n, dtype=torch.uint8, device=x.device) if n else None
+    x, M, ldx, q, G, N, K = _operands(x, q, e, _row_exps)
+    od = _out_dtype(out_dtype)
+    out = _out(out, M, G, N, od, x.device)
+    ws = _ws(ws, bsfp8_workspace_bytes_config(max(M, 1), G, N, K, cfg, cps), x.device)
     wsb = ws.numel() if ws is not None else 0
     _check(lib().bsfp8_gemm_row32_config(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), cfg, cps, _ptr(ws), wsb,
                                          _ptr(out), od, _stream(x)), "bsfp8_gemm_row32_config")
@@ -439,10 +485,8 @@ def _mx_out(M, L, device, yq, ys):
         yq = torch.empty((M, L), dtype=torch.uint8, device=device)
     if ys is None:
         ys = torch.empty((M, L // 32), dtype=torch.uint8, device=device)
-    _need(yq, torch.uint8, "yq")
-    _need(ys, torch.uint8, "ys")
-    if yq.numel() < M * L or ys.numel() < M * (L // 32):
-        raise ValueError("yq or ys too small")
+    _need(yq, torch.uint8, "yq", numel=M * L, device=device)
+    _need(ys, torch.uint8, "ys", numel=M * (L // 32), device=device)
     return yq, ys
 
 
@@ -471,14 +515,12 @@ def workspace_mxfp8(M, G, N, K, split_k=0, device="cuda"):
 def bsfp8_gemm_mxfp8(x, q, e, split_k=0, ws=None, yq=None, ys=None):
     """The GEMM of bsfp8_gemm with the MXFP8 epilogue -> (codes uint8 [M, G*N], scale bytes uint8
     [M, G*N/32])."""
-    q = _codes(q)
-    _need(q, torch.uint8, "q")
-    _need(e, torch.uint8, "e")
-    G, N, K = q.shape
-    x, M, ldx = _x_view(x)
+    x, M, ldx, q, G, N, K = _operands(x, q, e, _block_exps)
     yq, ys = _mx_out(M, G * N, x.device, yq, ys)
     if ws is None and M > 0:
         ws = workspace_mxfp8(M, G, N, K, split_k, device=x.device)
+    elif ws is not None:
+        _need(ws, torch.uint8, "ws", numel=bsfp8_workspace_bytes_mxfp8(M, G, N, K, split_k), device=x.device)
     wsb = ws.numel() if ws is not None else 0
     _check(lib().bsfp8_gemm_mxfp8(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), split_k, _ptr(ws), wsb,
                                   _ptr(yq), _ptr(ys), _stream(x)), "bsfp8_gemm_mxfp8")
@@ -490,13 +532,13 @@ def bsfp8_workspace_bytes_mxfp8_config(M, G, N, K, cfg, cps):
 
 
 def bsfp8_gemm_mxfp8_config(x, q, e, cfg, cps, ws=None, yq=None, ys=None):
-    q = _codes(q)
-    G, N, K = q.shape
-    x, M, ldx = _x_view(x)
+    x, M, ldx, q, G, N, K = _operands(x, q, e, _block_exps)
     yq, ys = _mx_out(M, G * N, x.device, yq, ys)
+    n = bsfp8_workspace_bytes_mxfp8_config(M, G, N, K, cfg, cps) if M > 0 else 0
     if ws is None and M > 0:
-        ws = torch.empty(bsfp8_workspace_bytes_mxfp8_config(M, G, N, K, cfg, cps), dtype=torch.uint8,
-                         device=x.device)
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    elif ws is not None:
+        _need(ws, torch.uint8, "ws", numel=n, device=x.device)
     wsb = ws.numel() if ws is not None else 0
     _check(lib().bsfp8_gemm_mxfp8_config(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), cfg, cps, _ptr(ws), wsb,
                                          _ptr(yq), _ptr(ys), _stream(x)), "bsfp8_gemm_mxfp8_config")

@@ -252,9 +252,15 @@ def test_gemm_mxfp8_empty_and_errors():
     yq, ys = B.bsfp8_gemm_mxfp8(torch.zeros((0, K), dtype=torch.bfloat16, device="cuda"), q, e)
     assert yq.shape == (0, G * N) and ys.shape == (0, G * N // 32)
     x = torch.zeros((4, K), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(B.BsfpError) as ei:                  # workspace too small
+    with pytest.raises(ValueError):                          # workspace too small (binding)
         B.bsfp8_gemm_mxfp8(x, q, e, ws=torch.empty(16, dtype=torch.uint8, device="cuda"))
-    assert ei.value.status == B.EWORKSPACE
+    n = B.bsfp8_workspace_bytes_mxfp8(4, G, N, K)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    yq4 = torch.empty((4, G * N), dtype=torch.uint8, device="cuda")
+    ys4 = torch.empty((4, G * N // 32), dtype=torch.uint8, device="cuda")
+    st = B.lib().bsfp8_gemm_mxfp8(B._ptr(x), K, 4, G, N, K, B._ptr(q), B._ptr(e), 0, B._ptr(ws), n - 16,
+                                  B._ptr(yq4), B._ptr(ys4), B._stream(x))   # ... and the library
+    assert st == B.EWORKSPACE
     with pytest.raises(B.BsfpError) as ei:
         B.bsfp8_gemm_mxfp8(torch.zeros((257, K), dtype=torch.bfloat16, device="cuda"), q, e)
     assert ei.value.status == B.ESHAPE

@@ -245,7 +245,52 @@ def test_empty_and_error_cases():
     small_ws = torch.zeros(n - 16, dtype=torch.uint8, device="cuda")
     qq = torch.zeros((2, 1024, 4096), dtype=torch.uint8, device="cuda")
     ee = torch.full((2, 32, 128), 127, dtype=torch.uint8, device="cuda")
-    with pytest.raises(B.BsfpError) as ei:
-        B.bsfp8_gemm(torch.zeros((6, 8192), dtype=torch.bfloat16, device="cuda"), qq, ee, split_k=8, ws=small_ws)
-    assert ei.value.status == B.EWORKSPACE
+    x6 = torch.zeros((6, 8192), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):                          # the binding sees the short buffer
+        B.bsfp8_gemm(x6, qq, ee, split_k=8, ws=small_ws)
+    y6 = torch.empty((6, 2, 1024), dtype=torch.bfloat16, device="cuda")
+    full_ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    st = B.lib().bsfp8_gemm(B._ptr(x6), 8192, 6, 2, 1024, 4096, B._ptr(qq), B._ptr(ee), 8, B._ptr(full_ws), n - 16,
+                            B._ptr(y6), B.OUT_BF16, B._stream(x6))   # the library sees a short ws_bytes
+    assert st == B.EWORKSPACE
+    torch.cuda.synchronize()
+
+
+def test_binding_refuses_short_or_misplaced_buffers():
+    """Every buffer the binding hands over is checked against the sizes the library will address
+    (the C ABI cannot see allocation sizes), so a short or host buffer never reaches a kernel."""
+    G, N, K, M = 2, 64, 256, 4
+    q = torch.zeros((G, N, K), dtype=torch.uint8, device="cuda")
+    e = torch.full((G, N // 32, K // 32), 127, dtype=torch.uint8, device="cuda")
+    x = torch.zeros((M, G * K), dtype=torch.bfloat16, device="cuda")
+    cases = [
+        lambda: B.bsfp8_gemm(x, q, e, out=torch.empty((M, G, N - 1), dtype=torch.bfloat16, device="cuda")),
+        lambda: B.bsfp8_gemm(x, q, e, out=torch.empty((M, G, N), dtype=torch.float32, device="cuda")),
+        lambda: B.bsfp8_gemm(x, q, e[:, :1].contiguous()),
+        lambda: B.bsfp8_gemm(x[:, : G * K - 8], q, e),
+        lambda: B.bsfp8_gemm(x, q, e, split_k=2, ws=torch.zeros(8, dtype=torch.uint8)),   # host memory
+        lambda: B.bsfp8_gemm(x, q, e, split_k=2, ws=torch.zeros(1 << 20, dtype=torch.float32, device="cuda")),
+        lambda: B.bsfp8_gemm_config(x, q, e, 54, 2, out=torch.empty(1, dtype=torch.bfloat16, device="cuda")),
+        lambda: B.bsfp8_gemm_row32(x, q, e),                  # block exponents where row exponents are due
+        lambda: B.bsfp8_gemm_mxfp8(x, q, e, yq=torch.empty((M, G * N - 32), dtype=torch.uint8, device="cuda")),
+        lambda: B.bsfp8_gemm_mxfp8(x, q, e, ws=torch.empty(4, dtype=torch.uint8, device="cuda")),
+        lambda: B.bsfp8_quantize_mx(x, xs=torch.empty((M, 1), dtype=torch.uint8, device="cuda")),
+        lambda: B.bsfp8_quantize_mx(x, L=G * K + 32),
+        lambda: B.bsfp8_pad_k_input(x, G, K, K + 128, out=torch.empty((M, G * K), dtype=torch.bfloat16, device="cuda")),
+        lambda: B.bsfp8_dequant(q, e, out=torch.empty((G, N, K - 1), dtype=torch.bfloat16, device="cuda")),
+        lambda: B.bsfp8_pad_k_weight(q, e[:1].contiguous(), K + 128),
+        lambda: B.bsfp8_scales_from_f32(torch.ones((2, 8), dtype=torch.float32, device="cuda"),
+                                        exp_out=torch.empty(15, dtype=torch.uint8, device="cuda")),
+    ]
+    xq, xs = B.bsfp8_quantize_mx(x)
+    cases += [
+        lambda: B.bsfp8_gemm_mx(xq, xs, q, e, out=torch.empty(7, dtype=torch.bfloat16, device="cuda")),
+        lambda: B.bsfp8_gemm_mx(xq[:, : G * K - 128], xs[:, : (G * K - 128) // 32], q, e),
+        lambda: B.bsfp8_gemm_mx(xq, xs[:2], q, e),
+        lambda: B.bsfp8_gemm_mx(xq, xs.cpu(), q, e),
+    ]
+    for i, case in enumerate(cases):
+        with pytest.raises((ValueError, TypeError)):
+            case()
+            print(f"case {i} was not refused", flush=True)
     torch.cuda.synchronize()
