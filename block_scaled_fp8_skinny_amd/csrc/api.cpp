@@ -40,7 +40,9 @@ int check_gemm(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, 
   // every operand is addressed with 32-bit byte offsets
   if (M > 0 && ((M - 1) * ldx + G * K) * 2 >= ((int64_t)1 << 31)) return BSFP8_ESHAPE;
   if (G * N * K >= ((int64_t)1 << 31)) return BSFP8_ESHAPE;
-  if (M > 0 && (!aligned16(x) || !aligned16(q) || !aligned16(y))) return BSFP8_ESTRIDE;
+  // the kernels read exponent bytes as 4-byte words (one word = the four blocks of a chunk)
+  if (M > 0 && (!aligned16(x) || !aligned16(q) || !aligned16(y) || (reinterpret_cast<uintptr_t>(e) & 3)))
+    return BSFP8_ESTRIDE;
   shape->ldx = ldx;
   return BSFP8_OK;
 }

@@ -145,7 +145,7 @@ BSFP8_API size_t bsfp8_workspace_bytes(int64_t M, int64_t G, int64_t N, int64_t 
 /* The GEMM. Page "wo_a_w8.py": _wo_a_partial_w8 (2..8 rows) and _wo_a_mid_kernel (9..192 rows).
  *   x       : uint16_t bf16 [M][ldx] (device, 16-byte aligned), group g at columns [g*K,(g+1)*K);
  *             ldx >= G*K and ldx % 8 == 0.
- *   q, e    : twin codes [G][N][K] and exponent bytes [G][N/32][K/32] (device, 16-byte aligned);
+ *   q, e    : twin codes [G][N][K] and exponent bytes [G][N/32][K/32] (device; q 16-byte, e 4-byte aligned);
  *             N and K multiples of 32. Exponent byte 255 and e4m3 NaN codes give NaN outputs.
  *   split_k : number of workgroups that share one output tile's K range (fixed-order reduction);
  *             0 = the built-in table for this shape; otherwise 1..64.

@@ -240,6 +240,10 @@ def test_empty_and_error_cases():
     with pytest.raises(B.BsfpError) as ei:
         B.bsfp8_gemm(xs, q, e)
     assert ei.value.status == B.ESTRIDE
+    e_odd = torch.full((e.numel() + 1,), 127, dtype=torch.uint8, device="cuda")[1:].view(e.shape)
+    with pytest.raises(B.BsfpError) as ei:                  # exponent bytes not 4-byte aligned
+        B.bsfp8_gemm(torch.zeros((4, K), dtype=torch.bfloat16, device="cuda"), q, e_odd)
+    assert ei.value.status == B.ESTRIDE
     n = B.bsfp8_workspace_bytes(6, 2, 1024, 4096, 8)
     assert n > 0
     small_ws = torch.zeros(n - 16, dtype=torch.uint8, device="cuda")
