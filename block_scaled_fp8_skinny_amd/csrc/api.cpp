@@ -3,6 +3,8 @@
 
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "bsfp8_tuning.h"
 #include "internal.h"
 
@@ -12,6 +14,52 @@ namespace {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// A buffer's byte range, for the check that outputs overlap no input, workspace or other output
+// (the kernels read the inputs while other workgroups write the outputs).
+struct Range {
+  const void* p;
+  size_t n;
+};
+inline bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || !a.n || !b.n) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+inline bool outputs_alias(std::initializer_list<Range> outs, std::initializer_list<Range> others) {
+  for (const Range* o = outs.begin(); o != outs.end(); ++o) {
+    for (const Range* r = others.begin(); r != others.end(); ++r)
+      if (overlap(*o, *r)) return true;
+    for (const Range* o2 = o + 1; o2 != outs.end(); ++o2)
+      if (overlap(*o, *o2)) return true;
+  }
+  return false;
+}
+// Bytes of x [M][ldx] (bf16) that a GEMM reads, of the codes and of the exponent bytes.
+inline size_t x_span(const GemmShape& s) { return ((size_t)(s.M - 1) * s.ldx + (size_t)s.G * s.K) * 2; }
+inline size_t q_span(const GemmShape& s) { return (size_t)s.G * s.N * s.K; }
+inline size_t e_span(const GemmShape& s, bool row_exps) {
+  return (size_t)s.G * (row_exps ? s.N : s.N / 32) * (s.K / 32);
+}
+inline size_t y_span(const GemmShape& s, int out_dtype) {
+  return (size_t)s.M * s.G * s.N * (out_dtype == BSFP8_OUT_F32 ? 4 : 2);
+}
+// y against x, q, e and the workspace (BSFP8_EINVAL on overlap)
+inline int check_gemm_alias(const GemmShape& s, const void* x, const void* q, const void* e, bool row_exps,
+                            const void* ws, size_t ws_bytes, const void* y, int out_dtype) {
+  return outputs_alias({{y, y_span(s, out_dtype)}},
+                       {{x, x_span(s)}, {q, q_span(s)}, {e, e_span(s, row_exps)}, {ws, ws_bytes}})
+             ? BSFP8_EINVAL
+             : BSFP8_OK;
+}
+// MXFP8 outputs (codes [M][G*N], scale bytes [M][G*N/32]) against the inputs, the workspace and
+// each other
+inline bool mxfp8_alias(const GemmShape& s, const void* x, const void* q, const void* e, const void* ws,
+                        size_t ws_bytes, const void* yq, const void* ys) {
+  const size_t L = (size_t)s.G * s.N;
+  return outputs_alias({{yq, (size_t)s.M * L}, {ys, (size_t)s.M * L / 32}},
+                       {{x, x_span(s)}, {q, q_span(s)}, {e, e_span(s, false)}, {ws, ws_bytes}});
+}
 
 // Size checks shared by the GEMM entry points and the plan report; fills `shape`.
 int check_dims(int64_t M, int64_t G, int64_t N, int64_t K, int split_k, int64_t max_m,
@@ -57,6 +105,8 @@ int run_gemm(int path, int64_t max_m, const uint16_t* x, int64_t ldx, int64_t M,
   st = plan_gemm(s, path, split_k, &p);
   if (st != BSFP8_OK) return st;
   if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned16(ws))) return BSFP8_EWORKSPACE;
+  st = check_gemm_alias(s, x, q, e, false, ws, ws_bytes, y, out_dtype);
+  if (st != BSFP8_OK) return st;
   return launch_gemm(s, p, x, q, e, ws, y, out_dtype == BSFP8_OUT_F32, as_stream(stream));
 }
 
@@ -87,6 +137,13 @@ int check_gemm_mx(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int64_t M, 
   if (!aligned16(xq) || !aligned16(q) || !aligned16(y) || (reinterpret_cast<uintptr_t>(xs) & 3) ||
       (reinterpret_cast<uintptr_t>(e) & 3))
     return BSFP8_ESTRIDE;
+  if (M > 0) {
+    const size_t xqb = (size_t)(M - 1) * ldq + (size_t)G * K;
+    const size_t xsb = (size_t)(M - 1) * (ldq / 32) + (size_t)G * K / 32;
+    const size_t yb = (size_t)M * G * N * (out_dtype == BSFP8_OUT_F32 ? 4 : 2);
+    if (outputs_alias({{y, yb}}, {{xq, xqb}, {xs, xsb}, {q, (size_t)G * N * K}, {e, (size_t)G * (N / 32) * (K / 32)}}))
+      return BSFP8_EINVAL;
+  }
   return BSFP8_OK;
 }
 
@@ -98,6 +155,7 @@ int run_gemm_mxfp8(const GemmShape& s, const GemmPlan& p, const uint16_t* x, con
                    const uint8_t* e, void* ws, size_t ws_bytes, uint8_t* yq, uint8_t* ys, bool fuse,
                    hipStream_t stream) {
   if (!ws || ws_bytes < gemm_partials_bytes(s, p) || !aligned16(ws)) return BSFP8_EWORKSPACE;
+  if (mxfp8_alias(s, x, q, e, ws, ws_bytes, yq, ys)) return BSFP8_EINVAL;
   if (fuse) {
     int fst = launch_decode_mxfp8(s, p, x, q, e, yq, ys, stream);
     if (fst != BSFP8_EINVAL) return fst;
@@ -137,6 +195,7 @@ int bsfp8_scales_from_f32(const float* scales, int64_t rows, int64_t cols, uint8
   if (n_bad_out) *n_bad_out = 0;
   if (n == 0) return BSFP8_OK;
   if (!scales || !exp_out) return BSFP8_EINVAL;
+  if (outputs_alias({{exp_out, (size_t)n}}, {{scales, (size_t)n * 4}})) return BSFP8_EINVAL;
   hipStream_t s = as_stream(stream);
   Counter c;
   int st = c.init(s);
@@ -157,6 +216,10 @@ int bsfp8_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t*
   if (G * R * D == 0) return BSFP8_OK;
   if (!w || !q_out || !e_out) return BSFP8_EINVAL;
   if (!aligned16(w) || !aligned16(q_out)) return BSFP8_ESTRIDE;
+  {
+    const size_t n = (size_t)G * R * D, nb = n / 1024;
+    if (outputs_alias({{q_out, n}, {e_out, nb}, {block_ok, nb}}, {{w, n * 2}})) return BSFP8_EINVAL;
+  }
   hipStream_t s = as_stream(stream);
   Counter c;
   int st = c.init(s);
@@ -177,6 +240,10 @@ int bsfp8_make_twin_row32(const uint16_t* w, int64_t G, int64_t N, int64_t K, ui
   if (G * N * K == 0) return BSFP8_OK;
   if (!w || !q_out || !e_out) return BSFP8_EINVAL;
   if (!aligned16(w) || !aligned16(q_out)) return BSFP8_ESTRIDE;
+  {
+    const size_t n = (size_t)G * N * K, nb = n / 32;
+    if (outputs_alias({{q_out, n}, {e_out, nb}, {block_ok, nb}}, {{w, n * 2}})) return BSFP8_EINVAL;
+  }
   hipStream_t s = as_stream(stream);
   Counter c;
   int st = c.init(s);
@@ -196,6 +263,9 @@ int bsfp8_pad_k_weight(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N,
   if (G * N * K_pad == 0) return BSFP8_OK;
   if (!q_pad || !e_pad || (K > 0 && (!q || !e))) return BSFP8_EINVAL;
   if ((K > 0 && !aligned16(q)) || !aligned16(q_pad)) return BSFP8_ESTRIDE;
+  if (outputs_alias({{q_pad, (size_t)G * N * K_pad}, {e_pad, (size_t)G * (N / 32) * (K_pad / 32)}},
+                    {{q, (size_t)G * N * K}, {e, (size_t)G * (N / 32) * (K / 32)}}))
+    return BSFP8_EINVAL;
   return launch_pad_k_weight(q, e, G, N, K, K_pad, q_pad, e_pad, as_stream(stream));
 }
 
@@ -205,6 +275,8 @@ int bsfp8_pad_k_input(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int6
   if (ldx < G * K) return BSFP8_ESTRIDE;
   if (M == 0 || K_pad == 0) return BSFP8_OK;
   if (!x_pad || (K > 0 && !x)) return BSFP8_EINVAL;
+  if (outputs_alias({{x_pad, (size_t)M * G * K_pad * 2}}, {{x, ((size_t)(M - 1) * ldx + (size_t)G * K) * 2}}))
+    return BSFP8_EINVAL;
   return launch_pad_k_input(x, ldx, M, G, K, K_pad, x_pad, as_stream(stream));
 }
 
@@ -214,6 +286,8 @@ int bsfp8_dequant(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int6
   if (G * N * K == 0) return BSFP8_OK;
   if (!q || !e || !w_out) return BSFP8_EINVAL;
   if (!aligned16(q) || !aligned16(w_out)) return BSFP8_ESTRIDE;
+  if (outputs_alias({{w_out, (size_t)G * N * K * 2}}, {{q, (size_t)G * N * K}, {e, (size_t)G * (N / 32) * (K / 32)}}))
+    return BSFP8_EINVAL;
   return launch_dequant(q, e, G, N, K, w_out, as_stream(stream));
 }
 
@@ -267,6 +341,8 @@ int bsfp8_gemm_row32(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64
   st = plan_gemm_row32(s, split_k, &p);
   if (st != BSFP8_OK) return st;
   if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned16(ws))) return BSFP8_EWORKSPACE;
+  st = check_gemm_alias(s, x, q, e, true, ws, ws_bytes, y, out_dtype);
+  if (st != BSFP8_OK) return st;
   return launch_gemm(s, p, x, q, e, ws, y, out_dtype == BSFP8_OUT_F32, as_stream(stream));
 }
 
@@ -281,6 +357,8 @@ int bsfp8_gemm_row32_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G
   st = plan_with(s, cfg, cps, &p);
   if (st != BSFP8_OK) return st;
   if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned16(ws))) return BSFP8_EWORKSPACE;
+  st = check_gemm_alias(s, x, q, e, true, ws, ws_bytes, y, out_dtype);
+  if (st != BSFP8_OK) return st;
   return launch_gemm(s, p, x, q, e, ws, y, out_dtype == BSFP8_OUT_F32, as_stream(stream));
 }
 
@@ -333,6 +411,8 @@ int bsfp8_gemm_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int6
   st = plan_with(s, cfg, cps, &p);
   if (st != BSFP8_OK) return st;
   if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned16(ws))) return BSFP8_EWORKSPACE;
+  st = check_gemm_alias(s, x, q, e, false, ws, ws_bytes, y, out_dtype);
+  if (st != BSFP8_OK) return st;
   return launch_gemm(s, p, x, q, e, ws, y, out_dtype == BSFP8_OUT_F32, as_stream(stream));
 }
 
@@ -342,6 +422,8 @@ int bsfp8_quantize_mx(const uint16_t* x, int64_t ldx, int64_t M, int64_t L, uint
   if (M == 0) return BSFP8_OK;
   if (!x || !xq || !xs) return BSFP8_EINVAL;
   if (ldx < L || ldx % 8 || !aligned16(x) || !aligned16(xq)) return BSFP8_ESTRIDE;
+  if (outputs_alias({{xq, (size_t)M * L}, {xs, (size_t)M * L / 32}}, {{x, ((size_t)(M - 1) * ldx + L) * 2}}))
+    return BSFP8_EINVAL;
   return launch_quantize_mx(x, ldx, M, L, xq, xs, as_stream(stream));
 }
 
@@ -383,6 +465,8 @@ int bsfp8_reduce_quantize_mx(const float* part, int64_t S, int64_t M, int64_t L,
   if (S * M * L > ((int64_t)1 << 40)) return BSFP8_ESHAPE;
   if (!part || !yq || !ys) return BSFP8_EINVAL;
   if (!aligned16(part) || !aligned16(yq)) return BSFP8_ESTRIDE;
+  if (outputs_alias({{yq, (size_t)M * L}, {ys, (size_t)M * L / 32}}, {{part, (size_t)S * M * L * 4}}))
+    return BSFP8_EINVAL;
   return launch_reduce_quantize_mx(part, (int)S, M, L, order, yq, ys, as_stream(stream));
 }
 

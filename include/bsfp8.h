@@ -46,7 +46,8 @@ extern "C" {
 typedef enum bsfp8_status {
   BSFP8_OK = 0,
   BSFP8_NOT_EXACT = 1,      /* make_twin verdict: the twin does not rebuild the weight (not an error) */
-  BSFP8_EINVAL = -1,        /* null pointer where one is required, bad enum value */
+  BSFP8_EINVAL = -1,        /* null pointer where one is required, bad enum value, or an output
+                               buffer overlapping an input, the workspace or another output */
   BSFP8_ESHAPE = -2,        /* sizes out of range or not multiples of the 32x32 block */
   BSFP8_ESCALE = -3,        /* a block scale is not a positive finite power of two */
   BSFP8_ESTRIDE = -4,       /* leading dimension too small or misaligned, pointer not 16-byte aligned */
@@ -152,7 +153,7 @@ BSFP8_API size_t bsfp8_workspace_bytes(int64_t M, int64_t G, int64_t N, int64_t 
  *   ws      : workspace of ws_bytes >= bsfp8_workspace_bytes(M,G,N,K,split_k) (may be NULL when
  *             that is 0).
  *   y       : [M][G][N] contiguous, bf16 (uint16_t) or float per out_dtype (device, 16-byte
- *             aligned); must not overlap x, q, e or ws.
+ *             aligned); must not overlap x, q, e or ws (BSFP8_EINVAL).
  * Summation order: each output is an fp32 sum over 128-wide K chunks in a fixed order that
  * depends only on (M, G, N, split_k) and on K rounded up to a multiple of 128, so results are
  * bitwise reproducible run to run, and K zero-padded within the same multiple of 128 (e.g.

@@ -119,8 +119,21 @@ def test_argument_checks_return_before_gpu_work(lib):
     assert G(fake, 60, 1, 1, 64, 64, fake, fake, 0, null, 0, fake, 0, null) == B.ESTRIDE
     assert G(fake, 68, 1, 1, 64, 64, fake, fake, 0, null, 0, fake, 0, null) == B.ESTRIDE
     assert G(ctypes.c_void_p(4104), 64, 1, 1, 64, 64, fake, fake, 0, null, 0, fake, 0, null) == B.ESTRIDE
-    # a split plan without its workspace
-    assert G(fake, 8192, 6, 2, 1024, 4096, fake, fake, 8, null, 0, fake, 0, null) == B.EWORKSPACE
+    # a split plan without its workspace (distinct, non-overlapping buffers)
+    xa, qa, ea, ya = (ctypes.c_void_p(i << 32) for i in (1, 2, 3, 4))
+    assert G(xa, 8192, 6, 2, 1024, 4096, qa, ea, 8, null, 0, ya, 0, null) == B.EWORKSPACE
+    # outputs overlapping an input, the workspace or another output
+    assert G(xa, 8192, 6, 2, 1024, 4096, qa, ea, 0, null, 0, ctypes.c_void_p((1 << 32) + 4096), 0, null) == B.EINVAL
+    assert G(xa, 8192, 6, 2, 1024, 4096, qa, ea, 0, null, 0, ctypes.c_void_p((3 << 32) - 16), 1, null) == B.EINVAL
+    wsa = ctypes.c_void_p(5 << 32)
+    assert G(xa, 8192, 6, 2, 1024, 4096, qa, ea, 8, wsa, 1 << 24, ctypes.c_void_p((5 << 32) + 256), 0, null) == B.EINVAL
+    assert lib.bsfp8_gemm_mxfp8(xa, 8192, 6, 2, 1024, 4096, qa, ea, 0, wsa, 1 << 24, ya,
+                                ctypes.c_void_p((4 << 32) + 1024), null) == B.EINVAL      # ys inside yq
+    assert lib.bsfp8_quantize_mx(xa, 8192, 6, 8192, ctypes.c_void_p((1 << 32) + 8192), ya, null) == B.EINVAL
+    assert lib.bsfp8_reduce_quantize_mx(xa, 2, 6, 1024, 0, ya, ctypes.c_void_p((1 << 32) + 64), null) == B.EINVAL
+    assert lib.bsfp8_dequant(qa, ea, 1, 64, 64, ctypes.c_void_p((2 << 32) + 16), null) == B.EINVAL
+    assert lib.bsfp8_pad_k_input(xa, 64, 2, 1, 64, 128, ctypes.c_void_p((1 << 32) + 64), null) == B.EINVAL
+    assert lib.bsfp8_pad_k_weight(qa, ea, 1, 64, 64, 128, ya, ctypes.c_void_p((3 << 32) + 2), null) == B.EINVAL
     bad = ctypes.c_int64(0)
     assert lib.bsfp8_make_twin(null, 1, 33, 32, null, null, null, ctypes.byref(bad), null) == B.ESHAPE
     assert lib.bsfp8_pad_k_weight(null, null, 1, 32, 64, 48, null, null, null) == B.ESHAPE

@@ -2,6 +2,8 @@
 
 Sizes here span several workgroup tiles, m-blocks, splits and ragged K tails while the float64
 oracle still finishes in seconds; full workload sizes are in test_gpu_workloads.py."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -257,6 +259,30 @@ def test_empty_and_error_cases():
     st = B.lib().bsfp8_gemm(B._ptr(x6), 8192, 6, 2, 1024, 4096, B._ptr(qq), B._ptr(ee), 8, B._ptr(full_ws), n - 16,
                             B._ptr(y6), B.OUT_BF16, B._stream(x6))   # the library sees a short ws_bytes
     assert st == B.EWORKSPACE
+    torch.cuda.synchronize()
+
+
+def test_outputs_overlapping_inputs_are_refused():
+    """The C ABI refuses an output range that overlaps an input, the workspace or another output
+    (checked on address ranges before any launch)."""
+    G, N, K, M = 1, 64, 256, 4
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    base = buf.data_ptr()
+    q = B._ptr(buf[: G * N * K])
+    e = ctypes.c_void_p(base + 65536)
+    x = ctypes.c_void_p(base + 131072)
+    s = B._stream(buf)
+    L = B.lib()
+    y_over_x = ctypes.c_void_p(base + 131072 + 512)
+    assert L.bsfp8_gemm(x, G * K, M, G, N, K, q, e, 0, None, 0, y_over_x, B.OUT_BF16, s) == B.EINVAL
+    assert L.bsfp8_gemm(x, G * K, M, G, N, K, q, e, 0, None, 0, q, B.OUT_F32, s) == B.EINVAL
+    y_ok = ctypes.c_void_p(base + 262144)
+    assert L.bsfp8_gemm(x, G * K, M, G, N, K, q, e, 0, None, 0, y_ok, B.OUT_BF16, s) == B.OK
+    yq, ys = ctypes.c_void_p(base + 393216), ctypes.c_void_p(base + 393216 + 64)   # ys inside yq
+    ws = ctypes.c_void_p(base + 524288)
+    assert L.bsfp8_gemm_mxfp8(x, G * K, M, G, N, K, q, e, 0, ws, 65536, yq, ys, s) == B.EINVAL
+    assert L.bsfp8_quantize_mx(x, G * K, M, G * K, ctypes.c_void_p(base + 131072 + 256), ys, s) == B.EINVAL
+    assert L.bsfp8_dequant(q, e, G, N, K, ctypes.c_void_p(base + 65536 - 64), s) == B.EINVAL
     torch.cuda.synchronize()
 
 
