@@ -84,8 +84,9 @@ def test_round_trip_of_exact_weights_is_accepted_and_bit_identical():
     t = oracle.make_twin(w)
     assert t.accepted and t.ok.all()
     assert np.array_equal(oracle.dequant_bf16(t.q, t.e), w)
-    # the encoded exponent never exceeds the generating one; equal when the block holds a
-    # code above 224 (the survey's reading (iii))
+    # the encoded exponent never exceeds the generating one, and equals it when the block's
+    # largest code magnitude exceeds 224 (a block whose codes stay at or below 224 = 448 / 2 fits
+    # one exponent lower)
     assert np.all(t.e <= src["e"])
 
 
