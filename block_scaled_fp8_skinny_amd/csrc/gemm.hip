@@ -992,13 +992,16 @@ gemm_tile_kernel(KParams p) {
 // at or beyond M (not loaded at all) feed only output columns that are not stored. Waves along K
 // are summed through LDS in ascending order, as in the other one-pass kernels, so an output's fp32
 // sum is the same chain of chunks as in gemm_direct_kernel with the same NWK and chunks per split.
+// RG = true takes K that is not a multiple of 128: the last chunk's X, weight and exponent
+// reads past K return zeros (exponent factors there are 1), so the fp32 chains are those of K
+// zero-padded to whole chunks; the aligned instances carry none of these checks.
 // RS = 1 takes one exponent byte per weight row and 32 columns (e [G][N][K/32]; page
 // "recipes/docker-images/mia-tp4/docs/tp4-adapters.md", row draft_main_proj) instead of one per
 // 32x32 block: the exponent words are then staged per weight row, nothing else changes.
 // TR = real weight rows per 16-row MFMA tile: with TR = 8 a workgroup holds half as many weight
 // rows, so a long K range still fits its LDS in one pass; the MFMA's rows 8..15 then repeat rows
 // 0..7 and their outputs are not stored.
-template <int NT, int NWN, int NWK, int CW, int XR, int RS, int TR>
+template <int NT, int NWN, int NWK, int CW, int XR, int RS, int TR, bool RG = false>
 __global__ void __launch_bounds__(WAVE * NWN * NWK)
 gemm_decode_kernel(KParams p) {
   constexpr int NWAVE = NWN * NWK;
@@ -1012,6 +1015,7 @@ gemm_decode_kernel(KParams p) {
   constexpr int EROWS = RS ? NB : (NB >= 32 ? NB / 32 : 1);   // exponent rows staged
   static_assert(XI % NWAVE == 0 && XPW >= 1, "every wave issues the same X loads");
   static_assert(PCH <= 64, "one exponent word per lane and chunk");
+  static_assert(!RG || (RS == 0 && PCH * 4 + 3 <= 256), "ragged K: block exponents, a shifted row in one load");
   static_assert((XR & (XR - 1)) == 0 && XR <= 16, "X rows: a power of two up to 16");
   static_assert(XPW + WPW + 1 <= 63, "vector memory counter range");
   static_assert(TR == 8 || TR == 16, "tile rows");
@@ -1047,11 +1051,21 @@ gemm_decode_kernel(KParams p) {
   // (1) exponent words: wave w loads exponent rows w, w + NWAVE, ... (block rows, or weight rows
   //     with RS), lane l the word of chunk c_begin + l. The count may differ between waves: these
   //     loads come first, and the waits below count only the weight loads issued after them.
+  //     RG (K not a multiple of 128): a row's bytes need not start on a word; the words are
+  //     loaded from the aligned address below the range's first byte, and the reads add that
+  //     offset.
   for (int er = wave; er < EROWS; er += NWAVE) {
     const int c = c_begin + lane;
     const int erow = RS ? g * N + n0 + er : g * (N / 32) + n0 / 32 + er;
-    const uint32_t off = (uint32_t)(erow * KB + c * 4);
-    lds_load4(re, lds_addr(e_lds + er * 64), c < c_end ? off : OOB);
+    if constexpr (RG) {
+      const uint32_t first = (uint32_t)(erow * KB + c_begin * 4);
+      const uint32_t end = (uint32_t)(erow * KB + min(c_end * 4, KB));
+      const uint32_t wd = (first & ~3u) + 4u * (uint32_t)lane;
+      lds_load4(re, lds_addr(e_lds + er * 64), wd < end ? wd : OOB);
+    } else {
+      const uint32_t off = (uint32_t)(erow * KB + c * 4);
+      lds_load4(re, lds_addr(e_lds + er * 64), c < c_end ? off : OOB);
+    }
   }
   // (2) X rows m0 .. m0+XR-1 over the workgroup's chunks: load i covers row i / (PCH/4), granules
   //     64*(i % (PCH/4)) .. +63 of the row's range. Rows at or beyond M are not loaded (the waits
@@ -1063,7 +1077,8 @@ gemm_decode_kernel(KParams p) {
     const int m = m0 + row;
     const int k = c_begin * KCH + (pc * 64 + lane) * 8;
     const uint32_t off = (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K + k) * 2);
-    if (m < M) lds_load16(rx, lds_addr(x_lds + row * ROWG + pc * 64), k < c_end * KCH ? off : OOB);
+    const bool ok = k < c_end * KCH && (!RG || k < K);   // RG: values past K read zeros
+    if (m < M) lds_load16(rx, lds_addr(x_lds + row * ROWG + pc * 64), ok ? off : OOB);
   }
   // (3) this wave's weight chunks: load (j, ts, v) covers rows 8v .. 8v+7 of its tile ts (TR
   //     rows), the lane fills row R = 8v + lane/8, slot lane%8 with granule (lane%8) ^ (R/2 % 8)
@@ -1081,7 +1096,8 @@ gemm_decode_kernel(KParams p) {
           const int R = 8 * v + R0;
           const int gsrc = (lane & 7) ^ ((R >> 1) & 7);
           const uint32_t off = qrow + (uint32_t)((ts * TR + 8 * v) * K + c * KCH + gsrc * 16);
-          lds_load16_stream(rq, lds_addr(wbase + (j * NT + ts) * TG + v * 64), c < c_end ? off : OOB);
+          const bool ok = c < c_end && (!RG || c * KCH + gsrc * 16 < K);   // RG: codes past K read zeros
+          lds_load16_stream(rq, lds_addr(wbase + (j * NT + ts) * TG + v * 64), ok ? off : OOB);
         }
     }
   }
@@ -1111,8 +1127,17 @@ gemm_decode_kernel(KParams p) {
 #pragma unroll
     for (int ts = 0; ts < NT; ++ts) {
       const int er = RS ? wn * TR * NT + ts * TR + wr : (n0 + wn * TR * NT + ts * TR + wr) / 32 - n0 / 32;
-      sc[j][ts][0] = block_scale(eb[er * 256 + cl * 4 + (q4 >> 1)]);
-      sc[j][ts][1] = block_scale(eb[er * 256 + cl * 4 + 2 + (q4 >> 1)]);
+      if constexpr (RG) {
+        const int erow = g * (N / 32) + n0 / 32 + er;
+        const int sh = (erow * KB + c_begin * 4) & 3;  // the range's first byte within its word
+        const int kb = (c_begin + cl) * 4 + (q4 >> 1);  // this lane's first block of the chunk
+        // blocks past K (their codes read as zeros) take a unit factor, never a stray byte
+        sc[j][ts][0] = kb < KB ? block_scale(eb[er * 256 + sh + cl * 4 + (q4 >> 1)]) : 1.0f;
+        sc[j][ts][1] = kb + 2 < KB ? block_scale(eb[er * 256 + sh + cl * 4 + 2 + (q4 >> 1)]) : 1.0f;
+      } else {
+        sc[j][ts][0] = block_scale(eb[er * 256 + cl * 4 + (q4 >> 1)]);
+        sc[j][ts][1] = block_scale(eb[er * 256 + cl * 4 + 2 + (q4 >> 1)]);
+      }
     }
   }
   auto chunk = [&](int j) {
@@ -1493,6 +1518,7 @@ struct Config {
   int kind;                              // DIRECT, ROWS and DECODE kernels make one pass
   int row_scales = 0;                    // 1: exponents per weight row and 32 columns
   int TR = 16;                           // DECODE: real weight rows per 16-row MFMA tile (8 or 16)
+  int ragged = 0;                        // DECODE: takes K that is not a multiple of 128
 };
 
 #define CFG(MT, NT, NWN, NWK, CW) {MT, NT, 1, NWN, NWK, CW, gemm_kernel<MT, NT, NWN, NWK, CW>, STAGED}
@@ -1586,6 +1612,9 @@ const Config kConfigs[] = {
     ERCFG(1, 1, 4, 4, 16, 16),  // 78 decode: 16 rows of X, 4 waves along K x 4 chunks
     ERCFG(1, 1, 8, 2, 16, 16),  // 79 decode: 16 rows of X, 8 waves along K x 2 chunks
     ERCFG(1, 1, 8, 5, 8, 8),    // 80 decode: 8 weight rows, 8 waves along K x 5 chunks (40 in one pass)
+    // the decode shapes of 54 and 59 for K that is not a multiple of 128
+    {8, 1, 1, 1, 8, 4, gemm_decode_kernel<1, 1, 8, 4, 8, 0, 16, true>, DECODE, 0, 16, 1},   // 81
+    {8, 1, 1, 1, 4, 2, gemm_decode_kernel<1, 1, 4, 2, 8, 0, 16, true>, DECODE, 0, 16, 1},   // 82
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1640,7 +1669,7 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   p.cps = cps < p.kchunks ? cps : p.kchunks;
   if ((c.kind == DIRECT || c.kind == ROWS || c.kind == DECODE) && p.cps > c.NWK * c.CW)
     return BSFP8_EINVAL;                                        // one pass
-  if (c.kind == DECODE && s.K % KCH != 0) return BSFP8_EINVAL;  // whole exponent words per chunk
+  if (c.kind == DECODE && !c.ragged && s.K % KCH != 0) return BSFP8_EINVAL;  // whole exponent words
   if (c.kind == TILE && (p.cps > TILE_MAX_CPS || s.K % KCH != 0)) return BSFP8_EINVAL;
   // slab kernel: K in whole chunks, splits begin on slab boundaries, one exponent word per lane
   if (c.kind == SLAB &&
@@ -1693,15 +1722,15 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
     else if (s.M <= 32) cfg = n64 ? 9 : 15;
     else cfg = n64 ? 10 : 16;
   } else if (s.M <= 8 || (s.M <= 16 && kchunks > 8)) {
-    // decode kernel (8 rows of X per workgroup) when K is whole chunks, else the one-pass kernel
-    // with the same waves and chunks (the same fp32 chains: K zero-padded to whole chunks gives
-    // bitwise the same Y)
+    // decode kernel (8 rows of X per workgroup); for K that is not whole chunks its ragged
+    // instance, whose last chunk reads zeros past K: K zero-padded to whole chunks gives bitwise
+    // the same Y (as does the one-pass register kernel with the same waves and chunks, 21 / 20)
     const bool whole = s.K % KCH == 0;
     if (kchunks <= 8) {
-      cfg = whole ? 59 : 21;         // 16 weight rows, 4 waves along K x 2 chunks
+      cfg = whole ? 59 : 82;         // 16 weight rows, 4 waves along K x 2 chunks
       cps = kchunks;
     } else {
-      cfg = whole ? 54 : 20;         // 16 weight rows, 8 waves along K x 4 chunks
+      cfg = whole ? 54 : 81;         // 16 weight rows, 8 waves along K x 4 chunks
       cps = kchunks < 32 ? kchunks : 32;
     }
   } else if (path == PATH_SMALL || s.M <= 32) {
@@ -1796,8 +1825,12 @@ int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const 
   k.ldx = s.ldx;
   const int64_t xb = ((int64_t)(s.M - 1) * s.ldx + (int64_t)s.G * s.K) * 2;
   const int64_t qb = (int64_t)s.G * s.N * s.K;
-  const int64_t eb = kConfigs[p.cfg].row_scales ? (int64_t)s.G * s.N * (s.K / 32)
-                                                 : (int64_t)s.G * (s.N / 32) * (s.K / 32);
+  // exponent bytes, rounded up to a whole word: the ragged decode instances read them as aligned
+  // words, and with K / 32 not a multiple of 4 the last row's final word runs up to 3 bytes past
+  // the array (inside the same page, as a page ends on a word; those bytes only reach blocks past
+  // K, whose factors are replaced)
+  const int64_t eb = ((kConfigs[p.cfg].row_scales ? (int64_t)s.G * s.N * (s.K / 32)
+                                                  : (int64_t)s.G * (s.N / 32) * (s.K / 32)) + 3) & ~(int64_t)3;
   if (xb >= (int64_t)OOB || qb >= (int64_t)OOB || eb >= (int64_t)OOB) return BSFP8_ESHAPE;
   k.x_bytes = (uint32_t)xb;
   k.q_bytes = (uint32_t)qb;
