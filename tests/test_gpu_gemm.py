@@ -79,16 +79,58 @@ def test_one_split_over_a_long_k(M, G, N, K):
     check_bf16(bf16_bits(y), x, G, N, K, q, e)
 
 
+def _takes_ragged_k(cfg):
+    """Whether a configuration accepts K that is not a multiple of 128 (the call is refused before
+    any launch when it does not)."""
+    x = torch.zeros((1, 800), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, 256, 800), dtype=torch.uint8, device="cuda")
+    e = torch.full((1, 8, 25), 127, dtype=torch.uint8, device="cuda")
+    try:
+        B.bsfp8_gemm_config(x, q, e, cfg, 7)
+    except B.BsfpError as err:
+        assert err.status in (B.EINVAL, B.ESHAPE)
+        return False
+    torch.cuda.synchronize()
+    return True
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (6, 96), (6, 576), (8, 800), (3, 1120), (16, 2080)])
+def test_ragged_k_decode_equals_the_register_kernel_and_the_padded_k(M, K):
+    """K that is not whole 128-wide chunks at decode row counts: the plan takes the decode
+    kernel's ragged instance, whose result equals bitwise the one-pass register kernel with the
+    same waves and chunks and the decode kernel on K zero-padded to whole chunks (the same fp32
+    chains with exact zeros added), and meets the parity rule against the oracle."""
+    G, N = 2, 128
+    x, q, e = _inputs(700 + K + M, M, G, N, K)
+    xt, qt, et = to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e)
+    plan = B.bsfp8_plan_info(M, G, N, K)
+    info = B.bsfp8_config_info(plan["cfg"])
+    print(f"M={M} K={K} plan {plan} {info}", flush=True)
+    assert info["kind"] == 4
+    y = B.bsfp8_gemm(xt, qt, et)
+    direct = 21 if (info["NWK"], info["CW"]) == (4, 2) else 20    # the register kernel's twins
+    yd = B.bsfp8_gemm_config(xt, qt, et, direct, plan["cps"])
+    Kp = -(-K // 128) * 128
+    qp, ep = B.bsfp8_pad_k_weight(qt, et, Kp)
+    yp = B.bsfp8_gemm(B.bsfp8_pad_k_input(xt, G, K, Kp), qp, ep)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), yd.view(torch.int16))
+    assert torch.equal(y.view(torch.int16), yp.view(torch.int16))
+    print(check_bf16(bf16_bits(y), x, G, N, K, q, e), flush=True)
+
+
 def test_every_kernel_configuration():
     """Each compiled configuration, with a few chunks-per-split values, on a shape with several
-    m-blocks (where the tile is smaller than M), a ragged K tail (the tile and decode kernels
-    take K in whole 128-wide chunks) and every N tile width."""
+    m-blocks (where the tile is smaller than M), a ragged K tail (the tile, slab and aligned
+    decode kernels take K in whole 128-wide chunks) and every N tile width."""
     G, N = 2, 256
     for cfg in range(B.bsfp8_num_configs()):
         info = B.bsfp8_config_info(cfg)
         if info["row_scales"]:              # these read [G][N][K/32] exponents: test_gpu_row32.py
             continue
         K = 768 if info["kind"] in (3, 4, 5) else 800
+        if info["kind"] == 4 and _takes_ragged_k(cfg):
+            K = 800                         # a decode instance built for a ragged last chunk
         M = min(2 * info["BM"] - 3, 256)
         x, q, e = _inputs(400 + cfg, M, G, N, K)
         exact = oracle.gemm_exact_f64(x, G, N, K, q, e)
