@@ -31,7 +31,9 @@ BSFP8_API int bsfp8_num_configs(void);
  * kernel (X shared through an LDS ring of 512-wide K slabs; out[3] = ring stages; splits begin
  * on slab boundaries). For kinds
  * 1, 2 and 4 the chunks per split must be at most out[3] * out[5]; for kind 3 at most 64. Kinds 3
- * and 4 take K in whole 128-wide chunks (K % 128 == 0).
+ * and 5 take K in whole 128-wide chunks (K % 128 == 0), and so do the kind-4 configurations
+ * except those built for a ragged last chunk (a call with K % 128 != 0 is refused with
+ * BSFP8_EINVAL by the others).
  * out[7] = 1 when the configuration reads one exponent per weight row and 32 columns (it then
  * runs only through bsfp8_gemm_row32_config). Returns BSFP8_EINVAL for an unknown cfg. `out` is
  * host memory of 8 ints. */
