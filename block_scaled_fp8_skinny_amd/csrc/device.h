@@ -151,27 +151,40 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Buffer loads in LDS mode: lane l's bytes land at LDS address lds + l*size (lds is wave-uniform,
-// passed in M0; the compiler cannot prove that values derived from the wave index are uniform,
-// hence the readfirstlane). Written as inline assembly so that the compiler neither reorders them nor adds
-// waits of its own for them (it would wait for every load in flight before any LDS read); the
-// kernel counts them itself with wait_vmcnt_le.
+// Buffer loads in LDS mode: lane l's bytes land at LDS address lds + l*size (lds is wave-uniform
+// and travels in M0; the compiler cannot prove that values derived from the wave index are
+// uniform, hence the readfirstlane). Written as inline assembly so that the compiler neither
+// reorders them nor adds waits of its own for them; the kernel counts them itself with
+// wait_vmcnt_le. (With __builtin_amdgcn_raw_ptr_buffer_load_lds the compiler cannot tell which
+// ring stage or chunk buffer a load fills, so it waits for every LDS-mode load in flight before
+// the first LDS read that might alias one: an s_waitcnt vmcnt(0) inside each ring loop, and
+// before every chunk but the first of the decode kernel, which would serialise the streams.)
+// M0 is a register the compiler reserves, so each load saves it into a scratch SGPR, sets it,
+// issues the load and puts the saved value back: nothing the compiler may keep in M0 changes
+// across the statement, and M0 is not on any clobber list. The s_nop gives the one wait state an
+// LDS-mode load needs after an SALU write of M0.
 typedef uint32_t lds_addr_t;
 template <typename T>
 __device__ __forceinline__ lds_addr_t lds_addr(const T* p) {
   return (lds_addr_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
 }
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_addr_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory");
 }
 __device__ __forceinline__ void lds_load16_stream(__amdgpu_buffer_rsrc_t r, lds_addr_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory");
 }
 __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, lds_addr_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, 0 offen lds\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r) : "memory");
 }
 
 // Wait until at most N of this wave's vector memory loads are outstanding (loads complete in
