@@ -110,3 +110,34 @@ def lm_head(seed, M, N=32768, K=5120, elo=118, ehi=122):
     r = rng(seed)
     return dict(x=bf16_normal(r, (M, K)), q=e4m3_codes(r, (1, N, K)),
                 e=exponent_bytes(r, (1, N // 32, K // 32), elo, ehi), M=M, G=1, N=N, K=K)
+
+
+# --------------------------------------------------------------------------------------------
+# edge inputs: exponent bytes at the ends of the range
+# --------------------------------------------------------------------------------------------
+TINY_BYTES = np.array([0, 1, 2, 3], dtype=np.uint8)          # factors 2^-127 .. 2^-124
+LARGE_BYTES = np.array([246, 250, 254], dtype=np.uint8)      # factors 2^119, 2^123, 2^127
+
+
+def edge_exponent_bytes(r, G, N, K, extreme, lo=110, hi=130):
+    """Exponent bytes [G, N/32, K/32] where block rows (32 weight rows) take one of three classes
+    in turn: every block from `extreme` (an array of bytes), blocks drawn half from `extreme` and
+    half from [lo, hi], and every block from [lo, hi]. Returns (bytes, class per block row)."""
+    nb, kb = N // 32, K // 32
+    cls = np.arange(G * nb).reshape(G, nb) % 3
+    pick_ext = extreme[r.integers(0, extreme.size, size=(G, nb, kb))]
+    pick_mid = r.integers(lo, hi + 1, size=(G, nb, kb)).astype(np.uint8)
+    half = r.random((G, nb, kb)) < 0.5
+    e = np.where(cls[:, :, None] == 0, pick_ext, np.where(cls[:, :, None] == 1, np.where(half, pick_ext, pick_mid),
+                                                          pick_mid))
+    return e.astype(np.uint8), cls
+
+
+def cap_code_exponent_field(codes, field_max):
+    """e4m3 codes with the 4-bit exponent field lowered to at most field_max (sign and fraction
+    bits kept): bit-pattern surgery on the inputs, so that large block factors keep the rebuilt
+    weights finite. field_max is an array broadcast against codes."""
+    c = np.asarray(codes, dtype=np.uint8)
+    field = (c >> 3) & 0xF
+    capped = np.minimum(field, np.asarray(field_max, dtype=np.uint8))
+    return ((c & 0x87) | (capped << 3)).astype(np.uint8)
