@@ -1,27 +1,38 @@
 """Benchmark of the block-scaled fp8 small-M GEMM on one MI355X.
 
-Default workload (one JSON line on stdout): the wo_a decode/verify shape at 6 rows, G=2 groups of
+Headline (the `value` of the JSON line): the wo_a decode/verify shape at 6 rows, G=2 groups of
 [1024 x 4096] e4m3 weights with 32x32 exponent blocks, bf16 activations [6, 8192], bf16 output
-[6, 2, 1024], the built-in split-K plan. A step is one GEMM call on one weight copy; the calls
-cycle through enough distinct weight copies (>= 512 MiB, twice the 256 MiB Infinity Cache) that
-every call streams its weights from HBM. The timed calls are captured once in a HIP graph and
-replayed (as the pages time their kernels), between a synchronize and HIP events on both sides.
+[6, 2, 1024], the built-in plan.
 
-value = effective weight-stream GB/s = (e4m3 bytes + exponent bytes) / time per call.
-roofline.achieved = algorithmic bytes (weights + exponents + X + Y) / time per call.
-The time per call is the timed graph replay (HIP events on the launch stream around it) divided
-by the number of calls in it: the average launch duration, gaps between launches included, which
-rocprofv3's average kernel duration for the same command matches within a few percent. HIP events
-around single eager calls are also reported; they include host launch gaps.
+Protocol (page "recipes/docker-images/mia-tp4/adapter/shared_pad_k.py", MEASUREMENT: distinct
+weight copies so that the cache is cold, captured graphs, interleaved rounds):
+  * every configuration draws C distinct seeded weight copies whose codes and exponent bytes
+    together hold at least 512 MiB (twice the 256 MiB Infinity Cache), whatever --steps says;
+  * a step is one GEMM call on each of the C copies, in order (the pages' ms/step over their 43
+    layers), captured once in a HIP graph;
+  * rounds: every configuration's step graph, and the plain-read floor graphs, replayed in turn
+    between HIP events on the replay stream (the headline: exactly --steps steps per round, each
+    timed region bracketed by synchronisation); at least 5 rounds; each figure is the median over
+    rounds;
+  * the plain-read floor of each weight set: the same graph with the GEMM replaced by a kernel
+    that only reads the copy's bytes with the GEMM's load shape (bsfp8_read_floor), and a bare
+    launch (the same kernel reading nothing).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--m M]
-       [--no-cpu-baseline] [--all FILE]
+Per call: us_per_call = step time / C (gaps between launches included, as a graph replays them).
+value = weight-stream GB/s = (e4m3 bytes + exponent bytes) / us_per_call. roofline.achieved =
+algorithmic bytes (weights + exponents + X + Y) / us_per_call, as a fraction of 8 TB/s.
+Every configuration named by the workloads gets such an entry in "configs", with the floor, the
+roofline fraction, the MFMA rate and the CPU oracle's time (all host threads and one thread).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--rounds R] [--no-cpu-baseline]
+       [--headline-only] [--workload NAME --m M [--path P] [--split-k S]] [--extra FILE]
 """
 import argparse
 import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -31,9 +42,11 @@ sys.path.insert(0, ROOT)
 METRIC = "us/call and effective weight-stream GB/s (% of HBM peak), M=6 block-fp8 GEMM"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 COLD_BYTES = 512 << 20
-# The pages' own figure for this workload (other hardware, context): on GB10 the twin path ran
-# 43 wo_a layers at 6 rows in 2.20 ms, i.e. 51.2 us/call, about 164 GB/s of weight stream.
+FLOOR_WGS = 256
+# The pages' own figure for the headline workload (other hardware, context): on GB10 the twin
+# path ran 43 wo_a layers at 6 rows in 2.20 ms, i.e. 51.2 us/call, about 164 GB/s of weight stream.
 PAGES_GBS = 8_396_800 / (2.20e-3 / 43) / 1e9
 
 WORKLOADS = {
@@ -43,11 +56,12 @@ WORKLOADS = {
     "wo_a_mid": (2, 1024, 4096, 64, (115, 125), "bf16",
                  "wo_a mid path: X bf16 [M, 2*4096], W e4m3 [2,1024,4096] + u8 exponents [2,32,128]"),
     "wo_a_tp3": (4, 1024, 4096, 6, (115, 123), "bf16",
-                 "wo_a padded-TP3 shard: X bf16 [M, 4*4096], W e4m3 [4,1024,4096] + u8 exponents [4,32,128]"),
+                 "wo_a padded-TP3 shard: X bf16 [M, 4*4096], W e4m3 [4,1024,4096] + u8 exponents [4,32,128] "
+                 "(the twins of 43 exact bf16 layers)"),
     "shared_down": (1, 5120, 576, 6, (117, 123), "bf16",
                     "shared-expert down_proj: X bf16 [M, 576], W e4m3 [5120, 576] + u8 exponents [160, 18]"),
     "shared_down_pad": (1, 5120, 640, 6, (117, 123), "bf16",
-                        "shared-expert down_proj, K zero-padded 576->640"),
+                        "shared-expert down_proj, K zero-padded 576->640 (zero codes, exponent byte 127)"),
     "lm_head": (1, 32768, 5120, 128, (118, 122), "f32",
                 "draft LM head: X bf16 [M, 5120], W e4m3 [32768, 5120] + u8 exponents [1024, 160], fp32 logits"),
     "main_proj": (1, 1280, 5120, 16, (115, 125), "bf16",
@@ -55,229 +69,397 @@ WORKLOADS = {
                   "per row and 32 columns [1280, 160]"),
 }
 ROW_SCALE_WORKLOADS = {"main_proj"}
+WEIGHT_SET = {"wo_a": "wo_a", "wo_a_mid": "wo_a", "wo_a_tp3": "wo_a_tp3", "shared_down": "shared_down",
+              "shared_down_pad": "shared_down_pad", "lm_head": "lm_head", "main_proj": "main_proj"}
+
+# The configurations of the workloads: (label, workload, M, split_k)
+DEFAULT_CONFIGS = (
+    [("d1", "shared_down", 6, 0), ("d1", "shared_down_pad", 6, 0)]
+    + [("d2", "wo_a", m, 0) for m in (2, 4, 6, 8)]
+    + [("d2 split", "wo_a", m, 8) for m in (2, 4, 6, 8)]
+    + [("d3", "wo_a_mid", m, 0) for m in (16, 32, 64, 128, 192)]
+    + [("d3 split", "wo_a_mid", 16, 4), ("d3 split", "wo_a_mid", 32, 2)]
+    + [("d4", "wo_a_tp3", m, 0) for m in (2, 6, 8)]
+    + [("d5", "lm_head", m, 0) for m in (16, 64, 128)]
+)
+HEADLINE = ("d2", "wo_a", 6, 0)
+TWIN_LAYERS = 43
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=2000)
-    p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--workload", default="wo_a", choices=sorted(WORKLOADS))
+    p.add_argument("--steps", type=int, default=20, help="steps of the headline per timed round")
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--rounds", type=int, default=7)
+    p.add_argument("--reps", type=int, default=8, help="steps per timed round of the other configurations")
+    p.add_argument("--headline-only", action="store_true")
+    p.add_argument("--workload", default=None, choices=sorted(WORKLOADS))
     p.add_argument("--m", type=int, default=None)
     p.add_argument("--split-k", type=int, default=0)
     p.add_argument("--path", default="bf16", choices=["bf16", "mx", "mxfp8"],
                    help="bf16: the exact twin GEMM (default); mx: the fp8 x fp8 GEMM on MXFP8 activations; "
                         "mxfp8: the exact twin GEMM with the MXFP8 output epilogue")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--all", default=None, help="also time every workload and row count; write JSON lines here")
+    p.add_argument("--cpu-seconds", type=float, default=8.0, help="CPU time per leg of the headline's baseline")
+    p.add_argument("--extra", default=None, help="also time the fp8 x fp8 path, the MXFP8 epilogue and the "
+                                                 "row-scale twin; write their entries as JSON lines here")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB, 20 times (counter calibration)")
     return p.parse_args()
 
 
-def algorithmic_bytes(M, G, N, K, out_bytes, row_scales=False):
-    w = G * N * K
-    e = G * N * (K // 32) if row_scales else G * (N // 32) * (K // 32)
-    return w, e, M * G * K * 2, M * G * N * out_bytes
+# ------------------------------------------------------------------------------------------------
+# inputs
+# ------------------------------------------------------------------------------------------------
+def shape_of(name):
+    G, N, K = WORKLOADS[name][:3]
+    erows = N if name in ROW_SCALE_WORKLOADS else N // 32
+    return G, N, K, erows
 
 
-def make_copies(torch, B, G, N, K, elo, ehi, n_copies, seed, row_scales=False):
-    """Seeded synthetic weight copies on the device: e4m3 codes uniform over the finite codes,
-    exponent bytes uniform in [elo, ehi] (one per 32x32 block, or per row and 32 columns)."""
-    erows = N if row_scales else N // 32
+def copy_nbytes(name):
+    G, N, K, erows = shape_of(name)
+    return G * N * K + G * erows * (K // 32)
+
+
+class WeightSet:
+    """C distinct weight copies, each one device buffer [codes | exponent bytes] (so that the
+    floor kernel reads exactly the bytes a GEMM call streams), with q and e views into it."""
+
+    def __init__(self, torch, name, bufs):
+        G, N, K, erows = shape_of(name)
+        self.name, self.bufs = name, bufs
+        nq = G * N * K
+        self.q = [b[:nq].view(G, N, K) for b in bufs]
+        self.e = [b[nq:nq + G * erows * (K // 32)].view(G, erows, K // 32) for b in bufs]
+        self.copy_bytes = copy_nbytes(name)
+
+    def __len__(self):
+        return len(self.bufs)
+
+
+def n_copies_for(name):
+    return max(4, math.ceil(COLD_BYTES / copy_nbytes(name)))
+
+
+def random_weight_set(torch, name, seed, n=None):
+    """Seeded codes uniform over the finite e4m3 codes and exponent bytes uniform in the
+    workload's range, drawn on the device."""
     import synthetic as S
+    G, N, K, erows = shape_of(name)
+    elo, ehi = WORKLOADS[name][4]
+    n = n or n_copies_for(name)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed)
     table = torch.from_numpy(S.FINITE_E4M3_CODES).cuda()
-    qs, es = [], []
-    for i in range(n_copies):
-        idx = torch.randint(0, table.numel(), (G, N, K), generator=gen, device="cuda", dtype=torch.int32)
-        qs.append(table[idx])
-        es.append(torch.randint(elo, ehi + 1, (G, erows, K // 32), generator=gen, device="cuda",
-                                dtype=torch.int32).to(torch.uint8))
+    nq = G * N * K
+    bufs = []
+    for _ in range(n):
+        b = torch.empty(copy_nbytes(name), dtype=torch.uint8, device="cuda")
+        idx = torch.randint(0, table.numel(), (nq,), generator=gen, device="cuda", dtype=torch.int32)
+        b[:nq] = table[idx]
+        b[nq:] = torch.randint(elo, ehi + 1, (G * erows * (K // 32),), generator=gen, device="cuda",
+                               dtype=torch.int32).to(torch.uint8)
+        bufs.append(b)
         del idx
-    return qs, es
+    return WeightSet(torch, name, bufs)
 
 
-def graph_us(torch, fn, steps):
-    """Average time per call of `steps` calls of fn(i) captured in one HIP graph and replayed
-    between HIP events on the replay stream (the first replay uploads the graph, untimed)."""
+def padded_weight_set(torch, B, src, name):
+    """The copies of src zero-padded along K (zero codes, exponent byte 127) by the library."""
+    G, N, K, erows = shape_of(name)
+    nq = G * N * K
+    bufs = []
+    for q, e in zip(src.q, src.e):
+        qp, ep = B.bsfp8_pad_k_weight(q, e, K)
+        b = torch.empty(copy_nbytes(name), dtype=torch.uint8, device="cuda")
+        b[:nq] = qp.reshape(-1)
+        b[nq:] = ep.reshape(-1)
+        bufs.append(b)
+    return WeightSet(torch, name, bufs)
+
+
+def twin_weight_set(torch, B, seed, n_layers=TWIN_LAYERS, reps=5):
+    """The padded-TP3 twin workload: n_layers exact bf16 layers [4, 1024, 4096] (each 32x32 block
+    e4m3 * 2^e, e - 127 in [115, 123] - 127, rebuilt from seeded codes by bsfp8_dequant), encoded by
+    bsfp8_make_twin (timed per layer, `reps` rounds), whose twins are the GEMM's weight copies."""
+    name = "wo_a_tp3"
+    src = random_weight_set(torch, name, seed, n=n_layers)
+    layers = [B.bsfp8_dequant(q, e) for q, e in zip(src.q, src.e)]
+    G, N, K, erows = shape_of(name)
+    nq = G * N * K
+    for w in layers[:3]:
+        B.bsfp8_make_twin(w)                        # warm-up
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    round_means, accepted, twins = [], 0, None
+    for rd in range(reps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_layers)]
+        out = []
+        for i, w in enumerate(layers):
+            evs[2 * i].record(stream)
+            t = B.bsfp8_make_twin(w)
+            evs[2 * i + 1].record(stream)
+            out.append(t)
+        torch.cuda.synchronize()
+        round_means.append(1e3 * sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n_layers)) / n_layers)
+        if twins is None:
+            twins = out
+            accepted = sum(int(t.accepted) for t in out)
+    bufs = []
+    for t, q0, e0 in zip(twins, src.q, src.e):
+        b = torch.empty(copy_nbytes(name), dtype=torch.uint8, device="cuda")
+        b[:nq] = t.q.reshape(-1)
+        b[nq:] = t.e.reshape(-1)
+        bufs.append(b)
+    same = all(torch.equal(t.q, q0) and torch.equal(t.e, e0) for t, q0, e0 in zip(twins, src.q, src.e))
+    nbytes = G * N * K * 2 + G * N * K + 2 * G * (N // 32) * (K // 32)   # read bf16; write codes, exps, ok
+    us = statistics.median(round_means)
+    twin_entry = {
+        "label": "d4 make_twin", "workload": "wo_a_tp3", "path": "make_twin",
+        "desc": f"make_twin of {n_layers} exact bf16 layers [{G},{N},{K}] (synchronous prepare call: "
+                f"counter clear, encoder kernel, verdict read back), GPU span per layer",
+        "layers": n_layers, "accepted": accepted, "twins_equal_source": bool(same),
+        "us_per_layer": us, "us_per_layer_rounds": round_means, "bytes_per_layer": nbytes,
+        "algorithmic_gbs": nbytes / (us * 1e3),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e3), 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / (us * 1e3) / HBM_PEAK_GBS, 4)},
+    }
+    del layers, src
+    return WeightSet(torch, name, bufs), twin_entry
+
+
+def activations(torch, M, G, K, seed):
+    import synthetic as S
+    return torch.from_numpy(S.bf16_normal(S.rng(seed), (M, G * K)).view("int16")).view(torch.bfloat16).cuda()
+
+
+# ------------------------------------------------------------------------------------------------
+# graphs and rounds
+# ------------------------------------------------------------------------------------------------
+def capture(torch, fn, n_calls):
+    """One HIP graph of fn(0), fn(1), ..., fn(n_calls - 1), captured on a side stream."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
-            for i in range(steps):
+            for i in range(n_calls):
                 fn(i)
     torch.cuda.current_stream().wait_stream(side)
-    graph.replay()
     torch.cuda.synchronize()
+    return graph
+
+
+def time_replays(torch, graph, reps):
+    """Milliseconds for `reps` replays of graph, between HIP events on the replay stream, with the
+    device synchronised before and after."""
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    graph.replay()
-    t1.record()
+    t0.record(s)
+    for _ in range(reps):
+        graph.replay()
+    t1.record(s)
     torch.cuda.synchronize()
-    del graph
-    return 1e3 * t0.elapsed_time(t1) / steps
+    return t0.elapsed_time(t1)
 
 
-def time_workload(name, M, steps, warmup, split_k=0, path="bf16"):
-    """path "bf16": the exact twin GEMM (bsfp8_gemm). path "mx": the fp8 x fp8 GEMM
-    (bsfp8_gemm_mx) on activations quantized once before the timed region; the quantizer is timed
-    on its own and reported as quantize_us. path "mxfp8": the twin GEMM with the MXFP8 output
-    epilogue (bsfp8_gemm_mxfp8: GEMM + fused sum-and-quantise kernel per call)."""
-    import torch
-    import block_scaled_fp8_skinny_amd as B
-    import synthetic as S
+class Timed:
+    """A step graph (n_calls calls) and its per-round times."""
 
-    G, N, K, _, (elo, ehi), out, desc = WORKLOADS[name]
-    row_scales = name in ROW_SCALE_WORKLOADS
-    out_bytes = 4 if out == "f32" else 2
-    w_b, e_b, x_b, y_b = algorithmic_bytes(M, G, N, K, out_bytes, row_scales)
+    def __init__(self, key, graph, n_calls, reps):
+        self.key, self.graph, self.n_calls, self.reps = key, graph, n_calls, reps
+        self.round_us = []              # per-call microseconds, one per round
+
+    def run_round(self, torch):
+        ms = time_replays(torch, self.graph, self.reps)
+        self.round_us.append(1e3 * ms / (self.reps * self.n_calls))
+        return ms
+
+    @property
+    def us(self):
+        return statistics.median(self.round_us)
+
+    @property
+    def spread(self):
+        return (max(self.round_us) - min(self.round_us)) / self.us if self.round_us else 0.0
+
+
+# ------------------------------------------------------------------------------------------------
+# configurations
+# ------------------------------------------------------------------------------------------------
+def algorithmic_bytes(name, M, path="bf16"):
+    G, N, K, erows = shape_of(name)
+    out_bytes = 4 if WORKLOADS[name][5] == "f32" else 2
+    w, e = G * N * K, G * erows * (K // 32)
+    x = M * G * K * 2
+    y = M * G * N * out_bytes
     if path == "mx":
-        x_b = M * G * K + M * G * K // 32             # e4m3 codes + scale bytes
+        x = M * G * K + M * G * K // 32
     if path == "mxfp8":
-        y_b = M * G * N + M * G * N // 32             # e4m3 codes + scale bytes of the output
-    copy_bytes = w_b + e_b
-    n_copies = max(4, min(steps, math.ceil(COLD_BYTES / copy_bytes)))
-    qs, es = make_copies(torch, B, G, N, K, elo, ehi, n_copies, seed=7000 + M, row_scales=row_scales)
-    x = torch.from_numpy(S.bf16_normal(S.rng(7100 + M), (M, G * K)).view("int16")).view(torch.bfloat16).cuda()
-    if row_scales:
-        ws = B.workspace_row32(M, G, N, K, split_k)
-    else:
-        ws = B.workspace(M, G, N, K, split_k) if path == "bf16" else None
-    y = torch.empty((M, G, N), dtype=torch.float32 if out == "f32" else torch.bfloat16, device="cuda")
-    quant_us = None
+        y = M * G * N + M * G * N // 32
+    return w, e, x, y
+
+
+def make_call(torch, B, ws_set, name, M, split_k, path, x, out):
+    """The per-call function over the copies of ws_set, its plan report and its buffers."""
+    G, N, K, _ = shape_of(name)
+    od = WORKLOADS[name][5]
+    C = len(ws_set)
     if path == "mx":
         xq, xs = B.bsfp8_quantize_mx(x)
         plan = {"mx_cfg": B.bsfp8_mx_plan(M, G, N), **B.bsfp8_mx_config_info(B.bsfp8_mx_plan(M, G, N))}
-
-        def call(i):
-            B.bsfp8_gemm_mx(xq, xs, qs[i % n_copies], es[i % n_copies], out=y, out_dtype=out)
-
-        for i in range(20):
-            B.bsfp8_quantize_mx(x, xq=xq, xs=xs)
-        quant_us = graph_us(torch, lambda i: B.bsfp8_quantize_mx(x, xq=xq, xs=xs), min(steps, 1000))
-    elif row_scales:
-        plan = {"row_scale_twin": True}
-
-        def call(i):
-            B.bsfp8_gemm_row32(x, qs[i % n_copies], es[i % n_copies], split_k=split_k, ws=ws, out=y, out_dtype=out)
-    elif path == "mxfp8":
+        return (lambda i: B.bsfp8_gemm_mx(xq, xs, ws_set.q[i % C], ws_set.e[i % C], out=out, out_dtype=od)), plan
+    if name in ROW_SCALE_WORKLOADS:
+        ws = B.workspace_row32(M, G, N, K, split_k)
+        return (lambda i: B.bsfp8_gemm_row32(x, ws_set.q[i % C], ws_set.e[i % C], split_k=split_k, ws=ws, out=out,
+                                             out_dtype=od)), {"row_scale_twin": True}
+    if path == "mxfp8":
         plan = B.bsfp8_plan_info(M, G, N, K, split_k, path=3)
         ws = B.workspace_mxfp8(M, G, N, K, split_k)
         yq = torch.empty((M, G * N), dtype=torch.uint8, device="cuda")
         ys = torch.empty((M, G * N // 32), dtype=torch.uint8, device="cuda")
-
-        def call(i):
-            B.bsfp8_gemm_mxfp8(x, qs[i % n_copies], es[i % n_copies], split_k=split_k, ws=ws, yq=yq, ys=ys)
-    else:
-        plan = B.bsfp8_plan_info(M, G, N, K, split_k)
-
-        def call(i):
-            B.bsfp8_gemm(x, qs[i % n_copies], es[i % n_copies], split_k=split_k, ws=ws, out=y, out_dtype=out)
-
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
-
-    # (1) kernel duration: HIP events around each call on the launch stream
-    stream = torch.cuda.current_stream()
-    n_ev = min(steps, 1000)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_ev)]
-    for i in range(n_ev):
-        evs[2 * i].record(stream)
-        call(i)
-        evs[2 * i + 1].record(stream)
-    torch.cuda.synchronize()
-    kern_ms = sorted(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n_ev))
-    kern_us_mean = 1e3 * sum(kern_ms) / n_ev
-    kern_us_median = 1e3 * kern_ms[n_ev // 2]
-
-    # (2) wall time per call: all `steps` calls captured in one graph, replayed once
-    wall_us = graph_us(torch, call, steps)
-    wall_ms = wall_us * steps / 1e3
-    res = dict(workload=name, path=path, desc=desc, M=M, G=G, N=N, K=K, out=out, plan=plan, copies=n_copies,
-               copy_bytes=copy_bytes, wall_us_per_call=wall_us, kernel_us_mean=kern_us_mean,
-               kernel_us_median=kern_us_median, weight_stream_gbs_wall=copy_bytes / (wall_us * 1e3),
-               algorithmic_bytes=w_b + e_b + x_b + y_b, flops=2 * M * G * N * K,
-               algorithmic_gbs=(w_b + e_b + x_b + y_b) / (wall_us * 1e3),
-               tflops=2 * M * G * N * K / (wall_us * 1e6), wall_ms_total=wall_ms, quantize_us=quant_us)
-    del qs, es
-    torch.cuda.empty_cache()
-    return res
+        return (lambda i: B.bsfp8_gemm_mxfp8(x, ws_set.q[i % C], ws_set.e[i % C], split_k=split_k, ws=ws, yq=yq,
+                                             ys=ys)), plan
+    plan = B.bsfp8_plan_info(M, G, N, K, split_k)
+    ws = B.workspace(M, G, N, K, split_k)
+    return (lambda i: B.bsfp8_gemm(x, ws_set.q[i % C], ws_set.e[i % C], split_k=split_k, ws=ws, out=out,
+                                   out_dtype=od)), plan
 
 
-def time_make_twin(n_layers=43, G=4, R=1024, D=4096, elo=115, ehi=123):
-    """The twin encoder at the padded-TP3 layer shape: n_layers distinct bf16 weights [G, R, D],
-    each exactly e4m3 x 2^e per 32x32 block (e = byte - 127 in [elo, ehi], built on the device
-    from seeded codes by bsfp8_dequant), encoded once each by bsfp8_make_twin (a synchronous
-    prepare call: it allocates and clears an 8-byte counter, runs the encoder and reads the
-    verdict back). Reported: the GPU span between HIP events around each call on its stream, and
-    the host wall time per call."""
-    import torch
-    import block_scaled_fp8_skinny_amd as B
-    qs, es = make_copies(torch, B, G, R, D, elo, ehi, n_layers, seed=7500)
-    ws = [B.bsfp8_dequant(qs[i], es[i]) for i in range(n_layers)]
-    del qs, es
-    for i in range(3):
-        B.bsfp8_make_twin(ws[i])
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_layers)]
-    accepted = 0
-    t0 = time.perf_counter()
-    for i in range(n_layers):
-        evs[2 * i].record(stream)
-        t = B.bsfp8_make_twin(ws[i])
-        evs[2 * i + 1].record(stream)
-        accepted += int(t.accepted)
-    torch.cuda.synchronize()
-    wall_us = 1e6 * (time.perf_counter() - t0) / n_layers
-    spans = sorted(1e3 * evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n_layers))
-    gpu_us = sum(spans) / n_layers
-    nbytes = G * R * D * 2 + G * R * D + 2 * G * (R // 32) * (D // 32)   # read bf16, write codes, exps, ok
-    del ws
-    torch.cuda.empty_cache()
-    return dict(workload="twin_tp3", path="make_twin", desc=f"make_twin of {n_layers} exact bf16 layers [{G},{R},{D}]",
-                G=G, N=R, K=D, layers=n_layers, accepted=accepted, gpu_span_us_per_layer=gpu_us,
-                gpu_span_us_median=spans[n_layers // 2], wall_us_per_layer=wall_us, bytes_per_layer=nbytes,
-                algorithmic_gbs=nbytes / (gpu_us * 1e3), pct_hbm_peak=100 * nbytes / (gpu_us * 1e3) / HBM_PEAK_GBS)
+def entry_for(label, name, M, split_k, path, plan, t, ws_set, floor_t, launch_t):
+    G, N, K, erows = shape_of(name)
+    w, e, x, y = algorithmic_bytes(name, M, path)
+    us = t.us
+    alg = w + e + x + y
+    flops = 2 * M * G * N * K
+    pages = G * N * K + G * N * K // 32
+    peak = MFMA_FP8_PEAK_TFLOPS if path == "mx" else MFMA_BF16_PEAK_TFLOPS
+    ent = {
+        "label": label, "workload": name, "desc": WORKLOADS[name][6], "M": M, "G": G, "N": N, "K": K, "path": path,
+        "split_k": split_k, "plan": plan, "copies": len(ws_set), "copy_bytes": ws_set.copy_bytes,
+        "us_per_call": round(us, 3), "us_per_call_rounds": [round(v, 3) for v in t.round_us],
+        "round_spread": round(t.spread, 4),
+        "weight_stream_gbs": round((w + e) / (us * 1e3), 1),
+        "pages_convention_gbs": round(pages / (us * 1e3), 1),
+        "algorithmic_bytes": alg,
+        "roofline": {"bound": "hbm", "achieved": round(alg / (us * 1e3), 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg / (us * 1e3) / HBM_PEAK_GBS, 4)},
+        "tflops": round(flops / (us * 1e6), 2),
+        "mfma_frac": round(flops / (us * 1e6) / peak, 4),
+    }
+    if floor_t is not None:
+        ent["floor_us_per_call"] = round(floor_t.us, 3)
+        ent["floor_frac"] = round(floor_t.us / us, 4)
+        ent["launch_us_per_call"] = round(launch_t.us, 3)
+    return ent
 
 
-def cpu_baseline(name, M, seconds):
-    """The oracle as it stands, timed on this host on a bounded sample of the same workload:
-    whole GEMM calls on weight copies of the real shape until `seconds` have passed."""
+# ------------------------------------------------------------------------------------------------
+# the CPU oracle as a baseline
+# ------------------------------------------------------------------------------------------------
+def cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": usable}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return None
+
+
+def _oracle_leg(fn, seconds, min_calls=1):
+    calls, t_total = 0, 0.0
+    while calls < min_calls or t_total < seconds:
+        t0 = time.perf_counter()
+        fn()
+        t_total += time.perf_counter() - t0
+        calls += 1
+    return calls, t_total
+
+
+def cpu_baseline(name, M, seconds, n_rows=None):
+    """The oracle as it stands (oracle.gemm, float64 NumPy) timed on this host on a bounded sample
+    of the workload: whole calls of the real shape (or, for the LM head, n_rows of its vocabulary
+    rows per call, scaled to the full call), until `seconds` have passed, once with every BLAS
+    thread and once with one. Returns the baseline in the headline's unit (GB/s of weight stream)
+    and microseconds per call."""
     import numpy as np
     import oracle
     import synthetic as S
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
     except Exception:
-        threads = 1
-    G, N, K, _, (elo, ehi), out, _ = WORKLOADS[name]
+        threadpool_limits = None
+    G, N, K, erows = shape_of(name)
+    elo, ehi = WORKLOADS[name][4]
+    out = "f32" if WORKLOADS[name][5] == "f32" else "bf16"
+    rows = n_rows or N
     r = S.rng(9000 + M)
     x = S.bf16_normal(r, (M, G * K))
-    calls, t_total = 0, 0.0
-    while t_total < seconds:
-        q = S.e4m3_codes(r, (G, N, K))
-        e = S.exponent_bytes(r, (G, N // 32, K // 32), elo, ehi)
-        t0 = time.perf_counter()
-        oracle.gemm(x, G, N, K, q, e, out="f32" if out == "f32" else "bf16")
-        t_total += time.perf_counter() - t0
-        calls += 1
-    copy_bytes = G * N * K + G * (N // 32) * (K // 32)
-    gbs = copy_bytes * calls / t_total / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "us_per_call": 1e6 * t_total / calls,
-            "sample": f"{calls} oracle.gemm calls (float64) on distinct weight copies of the same "
-                      f"shape (M={M}, G={G}, N={N}, K={K}), {t_total:.1f} s of CPU time, "
-                      f"BLAS threads={threads}, os.cpu_count()={os.cpu_count()}"}
+    q = S.e4m3_codes(r, (G, rows, K))
+    e = S.exponent_bytes(r, (G, rows // 32, K // 32), elo, ehi)
+    fn = lambda: oracle.gemm(x, G, rows, K, q, e, out=out)
+    scale = N / rows
+    copy_bytes = copy_nbytes(name)
+    res = {}
+    for leg, limit in (("all_threads", None), ("one_thread", 1)):
+        if limit is not None and threadpool_limits is None:
+            continue
+        if limit is None:
+            calls, t = _oracle_leg(fn, seconds)
+            threads = blas_threads()
+        else:
+            with threadpool_limits(limits=1):
+                calls, t = _oracle_leg(fn, seconds)
+            threads = 1
+        us = 1e6 * t / calls * scale
+        res[leg] = {"us_per_call": round(us, 1), "gbs": copy_bytes / (us * 1e3), "threads": threads, "calls": calls,
+                    "cpu_seconds": round(t, 2)}
+    a = res["all_threads"]
+    sample = (f"{a['calls']} oracle.gemm calls (float64 NumPy) on one seeded weight of the shape "
+              f"(M={M}, G={G}, N={rows}{f' of {N} rows, time scaled by {scale:g}' if rows != N else ''}, K={K}), "
+              f"{a['cpu_seconds']} s with {a['threads']} BLAS threads")
+    if "one_thread" in res:
+        o = res["one_thread"]
+        sample += f"; {o['calls']} calls, {o['cpu_seconds']} s with one thread"
+    return {"value": a["gbs"], "unit": "GB/s", "cores": a["threads"], "kind": "oracle",
+            "us_per_call": a["us_per_call"], "sample": sample,
+            "one_thread": res.get("one_thread"), **cpu_info()}
 
 
+def cpu_twin_baseline(seconds):
+    """oracle.make_twin on one group [1, 1024, 4096] of the padded-TP3 layer, scaled to the layer."""
+    import oracle
+    import synthetic as S
+    src = S.twin_source(7600, G=1, R=1024, D=4096)
+    w = oracle.dequant_bf16(src["q"], src["e"])
+    calls, t = _oracle_leg(lambda: oracle.make_twin(w), seconds)
+    us = 1e6 * t / calls * 4
+    return {"us_per_layer": round(us, 1), "kind": "oracle", "threads": 1,
+            "sample": f"{calls} oracle.make_twin calls on one group [1,1024,4096] of a layer, {t:.2f} s, "
+                      f"scaled by 4 to the [4,1024,4096] layer (NumPy elementwise work, one thread)"}
+
+
+# ------------------------------------------------------------------------------------------------
 def gemm_source_sha256():
     """Hash of the sources the bf16 GEMM kernels are built from (gemm.hip and device.h)."""
     h = hashlib.sha256()
@@ -295,10 +477,169 @@ def traffic_from_profile(name, M):
         return None
     with open(path) as f:
         rec = json.load(f)
-    sha = gemm_source_sha256()
-    if rec.get("gemm_source_sha256") != sha:
+    if rec.get("gemm_source_sha256") != gemm_source_sha256():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def run(args):
+    import torch
+    import block_scaled_fp8_skinny_amd as B
+
+    t_start = time.perf_counter()
+    if args.workload:
+        M = args.m or WORKLOADS[args.workload][3]
+        configs = [("single", args.workload, M, args.split_k)]
+        headline = configs[0]
+        path = args.path
+    elif args.headline_only:
+        configs = [HEADLINE]
+        headline = HEADLINE
+        path = "bf16"
+    else:
+        configs = list(DEFAULT_CONFIGS)
+        headline = HEADLINE
+        path = "bf16"
+
+    # weight sets
+    sets, twin_entry = {}, None
+    needed = {WEIGHT_SET[c[1]] for c in configs}
+    seeds = {"wo_a": 7000, "shared_down": 7200, "lm_head": 7300, "main_proj": 7400}
+    for ws_name in sorted(needed):
+        if ws_name == "shared_down_pad":
+            continue
+        if ws_name == "wo_a_tp3":
+            sets[ws_name], twin_entry = twin_weight_set(torch, B, 7500, reps=max(3, args.rounds))
+        else:
+            sets[ws_name] = random_weight_set(torch, ws_name, seeds[ws_name])
+    if "shared_down_pad" in needed:
+        if "shared_down" not in sets:
+            sets["shared_down"] = random_weight_set(torch, "shared_down", seeds["shared_down"])
+        sets["shared_down_pad"] = padded_weight_set(torch, B, sets["shared_down"], "shared_down_pad")
+    torch.cuda.synchronize()
+
+    # step graphs
+    timed, meta = [], []
+    keep = []                                       # buffers the graphs address
+    for (label, name, M, split_k) in configs:
+        G, N, K, _ = shape_of(name)
+        ws_set = sets[WEIGHT_SET[name]]
+        x = activations(torch, M, G, K, 7100 + M)
+        od = torch.float32 if WORKLOADS[name][5] == "f32" else torch.bfloat16
+        out = torch.empty((M, G, N), dtype=od, device="cuda")
+        fn, plan = make_call(torch, B, ws_set, name, M, split_k, path, x, out)
+        C = len(ws_set)
+        for i in range(C):                          # eager warm-up over every copy
+            fn(i)
+        torch.cuda.synchronize()
+        g = capture(torch, fn, C)
+        reps = args.steps if (label, name, M, split_k) == headline else args.reps
+        timed.append(Timed((label, name, M, split_k), g, C, reps))
+        meta.append((label, name, M, split_k, plan, ws_set))
+        keep.append((x, out))
+    # plain-read floors and a bare launch over each weight set's copies
+    floors = {}
+    sink = torch.empty(FLOOR_WGS, dtype=torch.int32, device="cuda")
+    for ws_name in sorted({WEIGHT_SET[c[1]] for c in configs}):
+        ws_set = sets[ws_name]
+        C = len(ws_set)
+        gf = capture(torch, lambda i, s=ws_set: B.bsfp8_read_floor(s.bufs[i], nwg=FLOOR_WGS, sink=sink), C)
+        gl = capture(torch, lambda i, s=ws_set: B.bsfp8_read_floor(s.bufs[i], nbytes=0, nwg=FLOOR_WGS, sink=sink), C)
+        floors[ws_name] = (Timed(("floor", ws_name), gf, C, args.reps), Timed(("launch", ws_name), gl, C, args.reps))
+    every = timed + [t for pair in floors.values() for t in pair]
+
+    # warm-up replays, then interleaved rounds
+    for t in every:
+        for _ in range(args.warmup if t.key == headline else 1):
+            t.graph.replay()
+    torch.cuda.synchronize()
+    for rd in range(args.rounds):
+        for t in every:
+            t.run_round(torch)
+        print(f"round {rd + 1}/{args.rounds} done", file=sys.stderr, flush=True)
+    gpu_s = time.perf_counter() - t_start
+
+    entries = []
+    for t, (label, name, M, split_k, plan, ws_set) in zip(timed, meta):
+        ft, lt = floors[WEIGHT_SET[name]]
+        entries.append(entry_for(label, name, M, split_k, path, plan, t, ws_set, ft, lt))
+    floor_summary = {k: {"copy_bytes": sets[k].copy_bytes, "copies": len(sets[k]),
+                         "read_us_per_call": round(f.us, 3), "read_gbs": round(sets[k].copy_bytes / (f.us * 1e3), 1),
+                         "launch_us_per_call": round(l.us, 3), "workgroups": FLOOR_WGS}
+                     for k, (f, l) in floors.items()}
+
+    # CPU baselines (the oracle; rank 0 at N=1)
+    hl_index = configs.index(headline)
+    if not args.no_cpu_baseline:
+        for ent, (label, name, M, split_k, plan, ws_set) in zip(entries, meta):
+            if name in ROW_SCALE_WORKLOADS or path != "bf16":
+                continue
+            is_head = (label, name, M, split_k) == headline
+            secs = args.cpu_seconds if is_head else 0.5
+            rows = 2048 if name == "lm_head" else None
+            if split_k and not is_head:             # same oracle call as the built-in plan's entry
+                continue
+            ent["cpu_baseline"] = cpu_baseline(name, M, secs, n_rows=rows)
+        if twin_entry is not None:
+            twin_entry["cpu_baseline"] = cpu_twin_baseline(2.0)
+
+    head = entries[hl_index]
+    name, M = headline[1], headline[2]
+    G, N, K, _ = shape_of(name)
+    line = {
+        "metric": METRIC,
+        "value": head["weight_stream_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": timed[hl_index].us * timed[hl_index].n_calls / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (round(head["weight_stream_gbs"] / PAGES_GBS, 2)
+                        if (name, M, path) == ("wo_a", 6, "bf16") else None),
+        "dtype": "fp8" if path == "mx" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[name][6] + f"; M={M}", "path": path, "M": M, "G": G, "N": N, "K": K,
+                   "split_k": headline[3], "plan": head["plan"], "weight_copies": head["copies"],
+                   "copy_bytes": head["copy_bytes"], "calls_per_step": head["copies"],
+                   "rounds": args.rounds, "statistic": "median over interleaved rounds"},
+        "us_per_call": head["us_per_call"],
+        "us_per_call_rounds": head["us_per_call_rounds"],
+        "pct_hbm_peak": round(100 * head["weight_stream_gbs"] / HBM_PEAK_GBS, 1),
+        "floor_us_per_call": head.get("floor_us_per_call"),
+        "floor_frac": head.get("floor_frac"),
+        "roofline": dict(head["roofline"], traffic=traffic_from_profile(name, M) if path == "bf16" else None,
+                         algorithmic_bytes_per_launch=head["algorithmic_bytes"]),
+        "baseline_ref": "pages (GB10, other hardware): twin path 2.20 ms / 43 layers = 51.2 us/call at M=6",
+    }
+    if "cpu_baseline" in head:
+        line["cpu_baseline"] = head["cpu_baseline"]
+    if len(entries) > 1 or twin_entry is not None:
+        line["configs"] = entries + ([twin_entry] if twin_entry is not None else [])
+        line["floors"] = floor_summary
+    line["timing"] = {"gpu_setup_and_rounds_s": round(gpu_s, 1), "total_s": round(time.perf_counter() - t_start, 1)}
+    return line
+
+
+def run_extra(args, path_out):
+    """The next-step paths on the same protocol: fp8 x fp8 (MXFP8 activations), the MXFP8 output
+    epilogue, the row-scale twin. One JSON line per entry."""
+    rows = []
+    for path, cases in (("mx", [("wo_a", 6), ("wo_a_mid", 64), ("wo_a_mid", 192), ("lm_head", 16), ("lm_head", 128)]),
+                        ("mxfp8", [("wo_a", 6), ("wo_a_mid", 64), ("wo_a_mid", 192)]),
+                        ("bf16", [("main_proj", 1), ("main_proj", 6), ("main_proj", 16)])):
+        for name, M in cases:
+            a = argparse.Namespace(**vars(args))
+            a.workload, a.m, a.path, a.split_k, a.no_cpu_baseline = name, M, path, 0, True
+            ln = run(a)
+            rows.append({"path": path, "workload": name, "M": M, "us_per_call": ln["us_per_call"],
+                         "weight_stream_gbs": ln["value"], "roofline": ln["roofline"],
+                         "floor_frac": ln["floor_frac"], "plan": ln["config"]["plan"]})
+            print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    with open(path_out, "w") as f:
+        for r in rows:
+            f.write(json.dumps(r) + "\n")
 
 
 def main():
@@ -321,75 +662,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 20}), flush=True)
         return
-    M = args.m or WORKLOADS[args.workload][3]
-    r = time_workload(args.workload, M, args.steps, args.warmup, args.split_k, path=args.path)
-    G, N, K = r["G"], r["N"], r["K"]
-    line = {
-        "metric": METRIC,
-        "value": round(r["weight_stream_gbs_wall"], 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": r["wall_us_per_call"] / 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": (round(r["weight_stream_gbs_wall"] / PAGES_GBS, 2)
-                        if args.workload == "wo_a" and M == 6 and args.path == "bf16" else None),
-        "dtype": "fp8" if args.path == "mx" else "bf16",
-        "data": "synthetic",
-        "config": {"workload": r["desc"] + f"; M={M}" + {"mx": "; fp8 x fp8 path (MXFP8 activations)",
-                                                          "mxfp8": "; MXFP8 output epilogue"}.get(args.path, ""),
-                   "path": args.path, "M": M, "G": G, "N": N, "K": K,
-                   "weight_copies": r["copies"], "copy_bytes": r["copy_bytes"], "plan": r["plan"]},
-        "us_per_call": round(r["wall_us_per_call"], 3),
-        "quantize_us_per_call": round(r["quantize_us"], 3) if r["quantize_us"] is not None else None,
-        "pct_hbm_peak": round(100 * r["weight_stream_gbs_wall"] / HBM_PEAK_GBS, 1),
-        "eager_event_us_per_call_mean": round(r["kernel_us_mean"], 3),
-        "eager_event_us_per_call_median": round(r["kernel_us_median"], 3),
-        "roofline": {"bound": "hbm", "achieved": round(r["algorithmic_gbs"], 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(r["algorithmic_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(args.workload, M) if args.path == "bf16" else None,
-                     "algorithmic_bytes_per_launch": r["algorithmic_bytes"]},
-        "baseline_ref": "pages (GB10, other hardware): twin path 2.20 ms / 43 layers = 51.2 us/call at M=6",
-    }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.workload, M, args.cpu_seconds)
-    if args.all:
-        rows = []
-        for name, ms in (("shared_down", [6]), ("shared_down_pad", [6]), ("wo_a", [2, 4, 6, 8]),
-                         ("wo_a_mid", [16, 32, 64, 128, 192]), ("wo_a_tp3", [2, 6, 8]),
-                         ("lm_head", [16, 64, 128])):
-            for m in ms:
-                st = 400 if name == "lm_head" else 2000
-                rr = time_workload(name, m, st, 50)
-                rows.append(rr)
-                print(json.dumps(rr), file=sys.stderr, flush=True)
-        # the twin encoder at the padded-TP3 layer shape
-        rr = time_make_twin()
-        rows.append(rr)
-        print(json.dumps(rr), file=sys.stderr, flush=True)
-        # the row-scale twin (one exponent per row and 32 columns) at its page's shape
-        for m in (1, 6, 16):
-            rr = time_workload("main_proj", m, 2000, 50)
-            rows.append(rr)
-            print(json.dumps(rr), file=sys.stderr, flush=True)
-        # the MXFP8 output epilogue (GEMM + fused sum-and-quantise kernel)
-        for name, ms in (("wo_a", [2, 6, 8]), ("wo_a_mid", [16, 64, 192])):
-            for m in ms:
-                rr = time_workload(name, m, 2000, 50, path="mxfp8")
-                rows.append(rr)
-                print(json.dumps(rr), file=sys.stderr, flush=True)
-        # the fp8 x fp8 path (MXFP8 activations) on the same weights
-        for name, ms in (("wo_a", [6]), ("wo_a_mid", [16, 64, 128, 192]), ("lm_head", [16, 64, 128])):
-            for m in ms:
-                st = 400 if name == "lm_head" else 2000
-                rr = time_workload(name, m, st, 50, path="mx")
-                rows.append(rr)
-                print(json.dumps(rr), file=sys.stderr, flush=True)
-        with open(args.all, "w") as f:
-            for rr in rows:
-                f.write(json.dumps(rr) + "\n")
+    line = run(args)
+    if args.extra:
+        run_extra(args, args.extra)
     print(json.dumps(line), flush=True)
 
 

@@ -38,6 +38,7 @@ _SIGS = {
     "bsfp8_gemm_mid": (_I, _GEMM_ARGS),
     "bsfp8_gemm": (_I, _GEMM_ARGS),
     "bsfp8_num_configs": (_I, []),
+    "bsfp8_read_floor": (_I, [_P, _SZ, _I, _P, _P]),
     "bsfp8_config_info": (_I, [_I, ctypes.POINTER(_I)]),
     "bsfp8_plan_info": (_I, [_I64, _I64, _I64, _I64, _I, _I, ctypes.POINTER(_I)]),
     "bsfp8_workspace_bytes_config": (_SZ, [_I64, _I64, _I64, _I64, _I, _I]),
@@ -319,6 +320,22 @@ def bsfp8_gemm_mid(x, q, e, split_k=0, ws=None, out=None, out_dtype="bf16"):
 # ------------------------------------------------------------------------------------------------
 def bsfp8_num_configs():
     return int(lib().bsfp8_num_configs())
+
+
+def bsfp8_read_floor(t, nbytes=None, nwg=256, sink=None):
+    """Plain-read floor: one kernel that reads the first nbytes (default: all) of the GPU tensor t
+    once with the GEMM's load shape and computes nothing else (a measurement aid; nbytes = 0 is a
+    bare launch). sink: uint32 [nwg] on t's device (allocated when None). Returns the sink."""
+    nb = t.numel() * t.element_size() if nbytes is None else int(nbytes)
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("t must be a contiguous GPU tensor")
+    if nb > t.numel() * t.element_size():
+        raise ValueError(f"t holds {t.numel() * t.element_size()} bytes, {nb} requested")
+    if sink is None:
+        sink = torch.empty(nwg, dtype=torch.int32, device=t.device)
+    _need(sink, torch.int32, "sink", numel=nwg, device=t.device)
+    _check(lib().bsfp8_read_floor(_ptr(t), nb, nwg, _ptr(sink), _stream(t)), "bsfp8_read_floor")
+    return sink
 
 
 def bsfp8_config_info(cfg):

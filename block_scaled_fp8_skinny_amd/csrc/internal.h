@@ -88,6 +88,9 @@ int num_mx_configs();
 int mx_config_info(int cfg, int* out);
 int mx_pick(int M, int G, int N);
 
+// Plain-read floor of a weight stream (measure.hip): reads `bytes` once with the GEMM's load shape.
+int launch_read_floor(const void* p, size_t bytes, int nwg, uint32_t* sink, hipStream_t stream);
+
 inline int hip_status(hipError_t err) { return err == hipSuccess ? BSFP8_OK : BSFP8_EHIP; }
 
 }  // namespace bsfp8

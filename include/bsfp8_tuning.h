@@ -83,6 +83,22 @@ BSFP8_API int bsfp8_gemm_mx_config(const uint8_t* xq, const uint8_t* xs, int64_t
                                    int64_t N, int64_t K, const uint8_t* q, const uint8_t* e, int cfg,
                                    void* y, int out_dtype, void* stream);
 
+/* Plain-read floor, a measurement aid: one kernel that reads `bytes` of device memory at p once,
+ * with the GEMM's load shape (16 bytes per lane, one contiguous kilobyte per wave load,
+ * non-temporal, eight loads in flight per wave), on nwg workgroups of 512 threads that each read
+ * one contiguous share, and computes nothing else. Timed over the same distinct weight copies and
+ * in the same graph replay as a GEMM (the measurement protocol of page
+ * "recipes/docker-images/mia-tp4/adapter/shared_pad_k.py", MEASUREMENT: distinct weight copies so
+ * that the cache is cold, captured graphs, interleaved rounds), it gives the floor a GEMM that
+ * streams those bytes can reach on this machine; bytes = 0 times a bare launch.
+ *   p    : device memory, 16-byte aligned, at least `bytes` long (may be NULL when bytes = 0);
+ *          bytes < 2^31.
+ *   sink : device uint32_t [nwg]; written only when a workgroup's fold of the data equals a fixed
+ *          constant (it keeps the loads alive), so its contents are meaningless.
+ * Returns BSFP8_EINVAL (nwg outside 1..65536, no sink), BSFP8_ESTRIDE (misaligned p),
+ * BSFP8_ESHAPE (bytes too large), BSFP8_EHIP on a launch failure. */
+BSFP8_API int bsfp8_read_floor(const void* p, size_t bytes, int nwg, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
