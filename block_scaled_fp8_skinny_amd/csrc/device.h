@@ -16,9 +16,26 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int KCH = 128;                 // K per chunk
 constexpr int WAVE = 64;
-constexpr int MAX_LEVELS = 7;            // splits <= 64 -> at most 6 tree levels
 constexpr uint32_t OOB = 0x80000000u;    // buffer offset beyond every descriptor's range
 constexpr int RSRC_WORD3 = 0x00020000;   // raw buffer descriptor word 3 for gfx9-class GPUs
+
+// Division by a divisor fixed at launch, without the integer-division sequence (a reciprocal on the
+// vector unit and a chain of dependent scalar steps, some hundred cycles before a workgroup knows
+// its tile): q = (n * mul) >> shift with mul = ceil(2^shift / d), shift = 31 + ceil(log2 d), set
+// on the host (make_fastdiv). Exact for 0 <= n < 2^31: mul * d = 2^shift + e with 0 <= e < d, so
+// n * mul / 2^shift = n / d + n * e / (d * 2^shift) and the second term is below 1 / d.
+struct FastDiv {
+  uint32_t mul, shift;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint32_t shift = 31 + l;
+  return FastDiv{(uint32_t)(((1ull << shift) + d - 1) / d), shift};
+}
+__device__ __forceinline__ int fdiv(int n, FastDiv f) {
+  return (int)(((uint64_t)(uint32_t)n * f.mul) >> f.shift);
+}
 
 struct KParams {
   const uint16_t* x;
@@ -35,8 +52,8 @@ struct KParams {
   int M, G, N, K;
   int kchunks, cps, splits, mblocks, nblocks, out_f32;
   int nwg;                               // grid size (gridDim would be read from the dispatch packet)
-  int levels;
-  int level_base[MAX_LEVELS];            // first slot array of each tree level
+  int levels;                            // tree levels of the pairwise combine (splits > 1)
+  FastDiv dm, dn, dg;                    // division by mblocks, nblocks and G
 };
 
 __device__ __forceinline__ uint32_t bits_of(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
@@ -82,14 +99,49 @@ __device__ __forceinline__ int xcd_logical(int i, int nwg) {
   return xcd * per + min(xcd, rem) + idx;
 }
 
-// Fetch every kernel argument at entry: an empty asm that reads the fields makes the compiler
-// issue all the scalar argument loads together (one round trip) instead of in dependent rounds.
-__device__ __forceinline__ void prefetch_args(const KParams& p) {
+// Fetch every kernel argument at entry and keep it in scalar registers. The empty asm statements
+// take each field as an in-out operand, so the compiler issues all the argument loads together
+// (one round trip) instead of in dependent rounds, and - since each value is then the asm's
+// output, not a load it could repeat - it keeps the fields the epilogue needs (output pointers,
+// flags, sizes) in registers instead of loading them again from the argument segment after the
+// main loop, where each reload is a scalar memory round trip on the way to the first store.
+// (prefetch_args_only: the loads at entry without pinning, for the staged multi-pass kernel, which
+// holds enough scalar state of its own that pinning the epilogue's fields makes it spill.)
+__device__ __forceinline__ void prefetch_args_only(const KParams& p) {
   asm volatile("" ::"s"(p.x), "s"(p.q), "s"(p.e), "s"(p.y), "s"(p.slots), "s"(p.ldx));
-  asm volatile("" ::"s"(p.x_bytes), "s"(p.q_bytes), "s"(p.e_bytes), "s"(p.M), "s"(p.G), "s"(p.N),
-               "s"(p.K));
-  asm volatile("" ::"s"(p.kchunks), "s"(p.cps), "s"(p.splits), "s"(p.mblocks), "s"(p.nblocks),
-               "s"(p.out_f32), "s"(p.nwg));
+  asm volatile("" ::"s"(p.x_bytes), "s"(p.q_bytes), "s"(p.e_bytes), "s"(p.M), "s"(p.G), "s"(p.N), "s"(p.K));
+  asm volatile("" ::"s"(p.kchunks), "s"(p.cps), "s"(p.splits), "s"(p.mblocks), "s"(p.nblocks), "s"(p.out_f32),
+               "s"(p.nwg));
+  asm volatile("" ::"s"(p.dm.mul), "s"(p.dm.shift), "s"(p.dn.mul), "s"(p.dn.shift), "s"(p.dg.mul), "s"(p.dg.shift));
+}
+__device__ __forceinline__ void prefetch_args(KParams& p) {
+  asm volatile("" : "+s"(p.x), "+s"(p.q), "+s"(p.e), "+s"(p.y), "+s"(p.slots), "+s"(p.part), "+s"(p.ldx));
+  asm volatile("" : "+s"(p.yq), "+s"(p.ys), "+s"(p.x_bytes), "+s"(p.q_bytes), "+s"(p.e_bytes), "+s"(p.M),
+               "+s"(p.G), "+s"(p.N), "+s"(p.K));
+  asm volatile("" : "+s"(p.kchunks), "+s"(p.cps), "+s"(p.splits), "+s"(p.mblocks), "+s"(p.nblocks),
+               "+s"(p.out_f32), "+s"(p.nwg), "+s"(p.levels));
+  asm volatile("" : "+s"(p.dm.mul), "+s"(p.dm.shift), "+s"(p.dn.mul), "+s"(p.dn.shift), "+s"(p.dg.mul),
+               "+s"(p.dg.shift));
+}
+
+// Workgroup -> (m-block, n-block, group, split) of the plan's tile order (m-blocks fastest), from
+// the XCD-ordered logical index.
+struct Tile {
+  int mb, nb, g, s;
+};
+__device__ __forceinline__ Tile tile_of(const KParams& p) {
+  int t = xcd_logical(blockIdx.x, p.nwg);
+  Tile r;
+  int q = fdiv(t, p.dm);
+  r.mb = t - q * p.mblocks;
+  t = q;
+  q = fdiv(t, p.dn);
+  r.nb = t - q * p.nblocks;
+  t = q;
+  q = fdiv(t, p.dg);
+  r.g = t - q * p.G;
+  r.s = q;
+  return r;
 }
 
 // Pairwise-combine tree over the split index for up to NV outputs of one lane (see the header
@@ -110,10 +162,12 @@ __device__ __forceinline__ void combine_splits(const KParams& p, int s, float (&
     }
     return;
   }
-  int idx = s, cnt = p.splits;
+  // node j of a level with cnt live partials combines splits 2j and 2j + 1; its slot array follows
+  // those of the earlier levels (cnt / 2 nodes each)
+  int idx = s, cnt = p.splits, level_base = 0;
   for (int lv = 0; lv < p.levels; ++lv) {
     if ((idx ^ 1) < cnt) {
-      unsigned long long* base = p.slots + (size_t)(p.level_base[lv] + (idx >> 1)) * mgn;
+      unsigned long long* base = p.slots + (size_t)(level_base + (idx >> 1)) * mgn;
       unsigned long long old[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i)
@@ -129,6 +183,7 @@ __device__ __forceinline__ void combine_splits(const KParams& p, int s, float (&
         }
       }
     }
+    level_base += cnt >> 1;
     idx >>= 1;
     cnt = (cnt + 1) >> 1;
   }

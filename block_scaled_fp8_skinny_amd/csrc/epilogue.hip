@@ -132,6 +132,7 @@ struct DecodeMxParams {
   int64_t ldx;
   uint32_t x_bytes, q_bytes, e_bytes;
   int M, G, N, K, kchunks, mblocks, nblocks, nwg;
+  FastDiv dm, dn;                         // division by mblocks and nblocks
 };
 
 // Fused decode GEMM + MXFP8 epilogue: a workgroup computes rows m0 .. m0+7 of X against 32 weight
@@ -165,14 +166,17 @@ __global__ void __launch_bounds__(WAVE * NWK) decode_mxfp8_kernel(DecodeMxParams
   asm volatile("" ::"s"(p.x), "s"(p.q), "s"(p.e), "s"(p.yq), "s"(p.ys), "s"(p.ldx));
   asm volatile("" ::"s"(p.x_bytes), "s"(p.q_bytes), "s"(p.e_bytes), "s"(p.M), "s"(p.G), "s"(p.N), "s"(p.K));
   asm volatile("" ::"s"(p.kchunks), "s"(p.mblocks), "s"(p.nblocks), "s"(p.nwg));
+  asm volatile("" ::"s"(p.dm.mul), "s"(p.dm.shift), "s"(p.dn.mul), "s"(p.dn.shift));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wk = wave;
   const int q4 = lane >> 4, r16 = lane & 15;
   int t = xcd_logical(blockIdx.x, p.nwg);
-  const int mb = t % p.mblocks;
-  t /= p.mblocks;
-  const int nb = t % p.nblocks;
-  const int g = t / p.nblocks;
+  int tq = fdiv(t, p.dm);
+  const int mb = t - tq * p.mblocks;
+  t = tq;
+  tq = fdiv(t, p.dn);
+  const int nb = t - tq * p.nblocks;
+  const int g = tq;
   const int K = p.K, M = p.M, N = p.N, G = p.G;
   const int n0 = nb * 32, m0 = mb * XR;
   const int c_end = p.kchunks;                      // one split: chunks 0 .. kchunks-1
@@ -340,6 +344,8 @@ int launch_decode_mxfp8(const GemmShape& s, const GemmPlan& p, const uint16_t* x
   k.kchunks = p.kchunks;
   k.mblocks = (s.M + 7) / 8;
   k.nblocks = s.N / 32;
+  k.dm = make_fastdiv((uint32_t)k.mblocks);
+  k.dn = make_fastdiv((uint32_t)k.nblocks);
   const long long nwg = (long long)k.mblocks * k.nblocks * s.G;
   if (nwg <= 0 || nwg > 0x7fffffffLL) return BSFP8_ESHAPE;
   k.nwg = (int)nwg;

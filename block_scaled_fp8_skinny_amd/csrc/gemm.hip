@@ -66,19 +66,14 @@ gemm_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t x_lds[XBYTES];
   __shared__ uint8_t e_lds[EROWS * ECOLS];
 
-  prefetch_args(p);
+  prefetch_args_only(p);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave % NWN, wk = wave / NWN;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  int t = xcd_logical(blockIdx.x, p.nwg);
-  const int mb = t % p.mblocks;
-  t /= p.mblocks;
-  const int nb = t % p.nblocks;
-  t /= p.nblocks;
-  const int g = t % p.G;
-  const int s = t / p.G;
+  const Tile tl = tile_of(p);
+  const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
 
   const int K = p.K, M = p.M, N = p.N, G = p.G;
   const int n0 = nb * NB, m0 = mb * BM;
@@ -316,13 +311,8 @@ gemm_direct_kernel(KParams p) {
   const int wn = wave % NWN, wk = wave / NWN;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  int t = xcd_logical(blockIdx.x, p.nwg);
-  const int mb = t % p.mblocks;
-  t /= p.mblocks;
-  const int nb = t % p.nblocks;
-  t /= p.nblocks;
-  const int g = t % p.G;
-  const int s = t / p.G;
+  const Tile tl = tile_of(p);
+  const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
 
   const int K = p.K, M = p.M, N = p.N, G = p.G;
   const int n0 = nb * NB, m0 = mb * 16;
@@ -507,13 +497,8 @@ gemm_rows_kernel(KParams p) {
   const int q4 = lane >> 4, r16 = lane & 15;
   const int cr = lane >> 3, cp = lane & 7;          // coalesced X: row cr (+8), granule cp (+8)
 
-  int t = xcd_logical(blockIdx.x, p.nwg);
-  const int mb = t % p.mblocks;
-  t /= p.mblocks;
-  const int nb = t % p.nblocks;
-  t /= p.nblocks;
-  const int g = t % p.G;
-  const int s = t / p.G;
+  const Tile tl = tile_of(p);
+  const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
 
   const int K = p.K, M = p.M, N = p.N, G = p.G;
   const int n0 = nb * NB, m0 = mb * BM;
@@ -801,13 +786,8 @@ gemm_tile_kernel(KParams p) {
   const int wm = wave / NWN, wn = wave % NWN;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  int t = xcd_logical(blockIdx.x, p.nwg);
-  const int mb = t % p.mblocks;
-  t /= p.mblocks;
-  const int nb = t % p.nblocks;
-  t /= p.nblocks;
-  const int g = t % p.G;
-  const int s = t / p.G;
+  const Tile tl = tile_of(p);
+  const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
 
   const int K = p.K, M = p.M, N = p.N, G = p.G;
   const int n0 = nb * NB, m0 = mb * BM;
@@ -1030,13 +1010,8 @@ gemm_decode_kernel(KParams p) {
   const int wn = wave % NWN, wk = wave / NWN;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  int t = xcd_logical(blockIdx.x, p.nwg);
-  const int mb = t % p.mblocks;
-  t /= p.mblocks;
-  const int nb = t % p.nblocks;
-  t /= p.nblocks;
-  const int g = t % p.G;
-  const int s = t / p.G;
+  const Tile tl = tile_of(p);
+  const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
 
   const int K = p.K, M = p.M, N = p.N, G = p.G;
   const int n0 = nb * NB, m0 = mb * XR;
@@ -1271,13 +1246,8 @@ gemm_slab_kernel(KParams p) {
   const int wm = wmn / NWN, wn = wmn % NWN;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  int t = xcd_logical(blockIdx.x, p.nwg);
-  const int mb = t % p.mblocks;
-  t /= p.mblocks;
-  const int nb = t % p.nblocks;
-  t /= p.nblocks;
-  const int g = t % p.G;
-  const int s = t / p.G;
+  const Tile tl = tile_of(p);
+  const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
 
   const int K = p.K, M = p.M, N = p.N, G = p.G;
   const int n0 = nb * NB, m0 = mb * BM;
@@ -1487,6 +1457,199 @@ gemm_slab_kernel(KParams p) {
     if (live[i]) store_out(p, off[i], v[i]);
 }
 
+// Paired decode kernel: at most 8 rows of X and 8 weight rows per workgroup, one pass over its K
+// range, and each MFMA computing two chunks at once. In v_mfma_f32_16x16x32_bf16 the A rows
+// 0..7 carry the workgroup's 8 weight rows at the first chunk of a pair and A rows 8..15 the same
+// weight rows at the second chunk; the B columns 0..7 carry the X rows at the first chunk and
+// columns 8..15 at the second. The diagonal 8 x 8 blocks of D are the two chunks' products (the
+// off-diagonal ones mix chunks and are discarded) and a lane exchange adds them at the end. So
+// every lane dequantises codes nobody else needs, and a workgroup of 8 weight rows costs half the
+// dequant and MFMA work of a 16-row tile: the decode shapes then spread over twice as many
+// workgroups (256 at wo_a, one per CU) at the same work per code.
+//  * Wave wk owns the CW = 2 * CP consecutive chunks cw0 .. cw0 + CW - 1 of the workgroup's range
+//    (pairs (cw0, cw0 + 1), (cw0 + 2, cw0 + 3), ...), and loads everything it reads itself, into
+//    its own LDS: no barrier until the waves' sums meet.
+//  * X: each row's CW * 256 bytes are contiguous (one kilobyte per row and load at CW = 4), read
+//    with the LDS mode of the buffer loads; within each chunk's 16 granules of a row the granules
+//    are rotated by (row + 8 * (chunk & 1)), which makes the fragment reads of the 16 lanes of a
+//    quarter wave (8 rows x 2 chunks) hit 16 distinct bank groups.
+//  * Weights: one load per chunk, eight lanes per row (128 contiguous bytes per row and load),
+//    granule g of row R at slot g ^ (R / 2); chunk tiles 68 granules apart so that the two chunks
+//    of a pair sit 4 granules apart in bank space (conflict-free fragment reads of both halves).
+//  * Exponents: the wave's words of its block row (8 weight rows lie in one 32-row block).
+//  * Chunks past the range (a split's end, or K in the last pair) are loaded as out-of-range
+//    reads, which leave zeros, and take a unit factor.
+// Each output's fp32 sum: per wave, the chain of the first chunks of its pairs and the chain of
+// the second chunks, added; then the waves in ascending order. It depends on the chunk count, not
+// on K, so K zero-padded inside the same chunk count gives the same sums.
+template <int NWK, int CP, bool RG>
+__global__ void __launch_bounds__(WAVE * NWK)
+gemm_pair_kernel(KParams p) {
+  constexpr int CW = 2 * CP;                        // chunks per wave
+  constexpr int XR = 8;                             // rows of X per workgroup
+  constexpr int XS = CW * 16;                       // granules of one X row slice
+  constexpr int WT = 68;                            // granules per weight chunk tile (64 + offset)
+  constexpr int XL = XR * XS / 64;                  // X loads per wave
+  static_assert(CP == 1 || CP == 2 || CP == 4, "X row slices tile a wave load");
+  static_assert(!RG || CW + 1 <= 64, "exponent words of a ragged range");
+  __shared__ uint4 x_lds[NWK * XR * XS];
+  __shared__ uint4 w_lds[NWK * CW * WT];
+  __shared__ uint32_t e_lds[NWK * 64];
+  __shared__ f32x4_t red[NWK > 1 ? (NWK - 1) * 16 : 1];
+
+  prefetch_args(p);
+  const int lane = threadIdx.x & 63, wk = threadIdx.x >> 6;
+  const int q4 = lane >> 4, r16 = lane & 15;
+
+  const Tile tl = tile_of(p);
+  const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
+
+  const int K = p.K, M = p.M, N = p.N, G = p.G;
+  const int n0 = nb * 8, m0 = mb * XR;
+  const int c_begin = s * p.cps;
+  const int c_end = min(c_begin + p.cps, p.kchunks);
+  const int cw0 = c_begin + wk * CW;                // this wave's first chunk
+  const int KB = K / 32;
+
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, (int)p.x_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.q, 0, (int)p.q_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((void*)p.e, 0, (int)p.e_bytes, RSRC_WORD3);
+  uint4* const xw = x_lds + wk * XR * XS;
+  uint4* const ww = w_lds + wk * CW * WT;
+  uint32_t* const ew = e_lds + wk * 64;
+  const int erow = g * (N / 32) + n0 / 32;
+
+  // (1) exponent words of the wave's chunks (RG: from the aligned word below the first byte)
+  if constexpr (RG) {
+    const uint32_t first = (uint32_t)(erow * KB + cw0 * 4);
+    const uint32_t end = (uint32_t)(erow * KB + min(min(cw0 + CW, c_end) * 4, KB));
+    const uint32_t wd = (first & ~3u) + 4u * (uint32_t)lane;
+    lds_load4(re, lds_addr(ew), lane <= CW && wd < end ? wd : OOB);
+  } else {
+    const int c = cw0 + lane;
+    lds_load4(re, lds_addr(ew), lane < CW && c < c_end ? (uint32_t)(erow * KB + c * 4) : OOB);
+  }
+  // (2) X rows m0 .. m0 + 7 over the wave's chunks: load i fills slots 64i .. 64i + 63 of the rows'
+  //     slices (row-major); the lane fetches the granule that belongs in its slot. Loads whose rows
+  //     all lie at or beyond M are skipped (those rows feed only discarded columns).
+#pragma unroll
+  for (int i = 0; i < XL; ++i) {
+    const int pos = i * 64 + lane;
+    const int row = pos / XS, slot = pos % XS;
+    const int cl = slot / 16;
+    const int gr = ((slot & 15) - row - 8 * (cl & 1)) & 15;
+    const int m = m0 + row;
+    const int k = (cw0 + cl) * KCH + gr * 8;
+    const uint32_t off = (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K + k) * 2);
+    const bool ok = m < M && cw0 + cl < c_end && (!RG || k < K);
+    if (m0 + (i * 64) / XS < M) lds_load16(rx, lds_addr(xw + i * 64), ok ? off : OOB);
+  }
+  // (3) weight chunks, one load each: lane l fills row R = l / 8, slot l % 8 with granule
+  //     (l % 8) ^ (R / 2)
+  {
+    const int R = lane >> 3;
+    const int gsrc = (lane & 7) ^ (R >> 1);
+    const uint32_t qrow = (uint32_t)(g * N + n0 + R) * (uint32_t)K;
+#pragma unroll
+    for (int cl = 0; cl < CW; ++cl) {
+      const int c = cw0 + cl;
+      const uint32_t off = qrow + (uint32_t)(c * KCH + gsrc * 16);
+      const bool ok = c < c_end && (!RG || c * KCH + gsrc * 16 < K);
+      lds_load16_stream(rq, lds_addr(ww + cl * WT), ok ? off : OOB);
+    }
+  }
+
+  // (4) pairs, each once its own loads (and everything issued before them) have landed
+  const int half = r16 >> 3;                        // A rows / B columns 8..15: the pair's second chunk
+  const int R = r16 & 7;                            // weight row of this lane (A operand)
+  const int mx = r16 & 7;                           // X row of this lane (B operand)
+  const int wsw = R >> 1;
+  const uint8_t* eb = reinterpret_cast<const uint8_t*>(ew);
+  int sh = 0;
+  if constexpr (RG) sh = (int)((uint32_t)(erow * KB + cw0 * 4) & 3u);
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto pair = [&](int pp) {
+    const int cl = 2 * pp + half;
+    const bool valid = cw0 + cl < c_end;
+    const uint4* wt = ww + cl * WT + R * 8;
+    const uint4 a = wt[q4 ^ wsw], b = wt[(4 + q4) ^ wsw];
+    // the exponent bytes are read whatever the chunk (past the range they are zeros) and then
+    // replaced by a unit factor: a lane-dependent condition around the LDS read would make the
+    // compiler branch and wait on each read
+    const int kb = (cw0 + cl) * 4 + (q4 >> 1);
+    const int ei = (RG ? sh : 0) + cl * 4 + (q4 >> 1);
+    const uint32_t b0 = eb[ei], b1 = eb[ei + 2];
+    const float s0 = valid && (!RG || kb < KB) ? block_scale(b0) : 1.0f;
+    const float s1 = valid && (!RG || kb + 2 < KB) ? block_scale(b1) : 1.0f;
+    const uint4* xr = xw + mx * XS + cl * 16;
+    const int rot = mx + 8 * (cl & 1);
+    const bf16x8_t x0 = __builtin_bit_cast(bf16x8_t, xr[(2 * q4 + rot) & 15]);
+    const bf16x8_t x1 = __builtin_bit_cast(bf16x8_t, xr[(2 * q4 + 1 + rot) & 15]);
+    const bf16x8_t x2 = __builtin_bit_cast(bf16x8_t, xr[(8 + 2 * q4 + rot) & 15]);
+    const bf16x8_t x3 = __builtin_bit_cast(bf16x8_t, xr[(9 + 2 * q4 + rot) & 15]);
+    f32x4_t c = acc;
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(a.x, a.y, s0), x0, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(a.z, a.w, s0), x1, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(b.x, b.y, s1), x2, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(b.z, b.w, s1), x3, c, 0, 0, 0);
+    acc = c;
+  };
+  wait_vmcnt_le<CW - 2>();
+  pair(0);
+  if constexpr (CP > 1) { wait_vmcnt_le<(CP > 1 ? CW - 4 : 0)>(); pair(1); }
+  if constexpr (CP > 2) { wait_vmcnt_le<(CP > 2 ? CW - 6 : 0)>(); pair(2); }
+  if constexpr (CP > 3) { wait_vmcnt_le<(CP > 3 ? CW - 8 : 0)>(); pair(3); }
+  static_assert(CP <= 4, "pairs per wave");
+
+  // (5) the two halves: lane l (q4 < 2, r16 < 8) holds D[4 q4 + v][r16] of the first chunks,
+  //     lane l + 40 the matching D[8 + 4 q4 + v][8 + r16] of the second
+  f32x4_t other;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) other[v] = __shfl_down(acc[v], 40);
+  acc += other;
+  const bool useful = q4 < 2 && r16 < 8;
+  const int slot = q4 * 8 + r16;
+
+  // (6) waves along K: ascending-order sum through LDS
+  if constexpr (NWK > 1) {
+    if (wk > 0 && useful) red[(wk - 1) * 16 + slot] = acc;
+    __syncthreads();
+    if (wk != 0) return;
+#pragma unroll
+    for (int w = 1; w < NWK; ++w)
+      if (useful) acc += red[(w - 1) * 16 + slot];
+  }
+  // (7) output: X row m0 + r16, weight rows n0 + 4 q4 .. + 3
+  const int m = m0 + r16;
+  const bool live = useful && m < M;
+  const int n = n0 + 4 * q4;
+  const size_t o = ((size_t)m * G + g) * N + n;
+  if (p.splits == 1 && !p.part) {
+    if (live) {
+      if (p.out_f32) {
+        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + o) = acc;
+      } else {
+        const uint2 w2 = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + o) = w2;
+      }
+    }
+    return;
+  }
+  float v[4];
+  size_t off[4];
+  bool lv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = acc[i];
+    off[i] = o + i;
+    lv[i] = live;
+  }
+  combine_splits<4>(p, s, v, off, lv);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (lv[i]) store_out(p, off[i], v[i]);
+}
+
 // Split-K reduction for the tile kernel: Y = sum over s = 0, 1, ..., S-1 of the partials, added
 // in that order in fp32, then rounded once to the output type. Four outputs per thread.
 __global__ void __launch_bounds__(256)
@@ -1509,7 +1672,7 @@ reduce_splits_kernel(const float* __restrict__ part, void* __restrict__ y, int64
 // ---------------------------------------------------------------------------------------------
 typedef void (*KernelFn)(KParams);
 
-enum Kind { STAGED = 0, DIRECT = 1, ROWS = 2, TILE = 3, DECODE = 4, SLAB = 5 };
+enum Kind { STAGED = 0, DIRECT = 1, ROWS = 2, TILE = 3, DECODE = 4, SLAB = 5, PAIR = 6 };
 
 struct Config {
   int MT, NT, NWM, NWN, NWK, CW;         // TILE: CW = chunks in flight; SLAB: CW = ring stages;
@@ -1528,6 +1691,7 @@ struct Config {
 #define ERCFG(NT, NWN, NWK, CW, XR, TR) {XR, NT, 1, NWN, NWK, CW, gemm_decode_kernel<NT, NWN, NWK, CW, XR, 1, TR>, DECODE, 1, TR}
 #define TCFG(MT, NT, NWM, NWN, D, GI) {MT, NT, NWM, NWN, 1, D, gemm_tile_kernel<MT, NT, NWM, NWN, D, GI>, TILE}
 #define SCFG(MT, NT, NWM, NWN, NWK, S) {MT, NT, NWM, NWN, NWK, S, gemm_slab_kernel<MT, NT, NWM, NWN, NWK, S>, SLAB}
+#define PCFG(NWK, CP, RG) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, RG>, PAIR, 0, 8, RG}
 
 const Config kConfigs[] = {
     CFG(1, 1, 4, 1, 4),   // 0  small: 64 rows, one wave per 16 rows, 4 chunks per wave
@@ -1615,6 +1779,17 @@ const Config kConfigs[] = {
     // the decode shapes of 54 and 59 for K that is not a multiple of 128
     {8, 1, 1, 1, 8, 4, gemm_decode_kernel<1, 1, 8, 4, 8, 0, 16, true>, DECODE, 0, 16, 1},   // 81
     {8, 1, 1, 1, 4, 2, gemm_decode_kernel<1, 1, 4, 2, 8, 0, 16, true>, DECODE, 0, 16, 1},   // 82
+    // paired decode: 8 rows of X x 8 weight rows, each MFMA two chunks
+    PCFG(8, 2, false),        // 83 pair: 8 waves along K x 4 chunks (32 chunks in one pass)
+    PCFG(16, 1, false),       // 84 pair: 16 waves along K x 2 chunks
+    PCFG(4, 4, false),        // 85 pair: 4 waves along K x 8 chunks
+    PCFG(4, 2, false),        // 86 pair: 4 waves along K x 4 chunks
+    PCFG(8, 1, false),        // 87 pair: 8 waves along K x 2 chunks
+    PCFG(3, 1, false),        // 88 pair: 3 waves along K x 2 chunks (up to 6 chunks)
+    PCFG(8, 2, true),         // 89 pair, K not a multiple of 128
+    PCFG(3, 1, true),         // 90 pair, K not a multiple of 128, up to 6 chunks
+    PCFG(4, 1, true),         // 91 pair, K not a multiple of 128, up to 8 chunks
+    PCFG(4, 1, false),        // 92 pair: 4 waves along K x 2 chunks
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1631,7 +1806,7 @@ int num_gemm_configs() { return kNumConfigs; }
 int gemm_config_info(int cfg, int* out) {
   if (cfg < 0 || cfg >= kNumConfigs) return BSFP8_EINVAL;
   const Config& c = kConfigs[cfg];
-  out[0] = c.kind == DECODE ? c.MT : 16 * c.MT * c.NWM;
+  out[0] = c.kind == DECODE || c.kind == PAIR ? c.MT : 16 * c.MT * c.NWM;
   out[1] = c.TR * c.NT * c.NWN;
   out[2] = WAVE * c.NWM * c.NWN * c.NWK;
   out[3] = c.CW;
@@ -1660,16 +1835,16 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   const Config& c = kConfigs[cfg];
   GemmPlan p{};
   p.cfg = cfg;
-  p.BM = c.kind == DECODE ? c.MT : 16 * c.MT * c.NWM;
+  p.BM = c.kind == DECODE || c.kind == PAIR ? c.MT : 16 * c.MT * c.NWM;
   p.NB = c.TR * c.NT * c.NWN;
   if (s.N % p.NB) return BSFP8_ESHAPE;
   p.kchunks = (s.K + KCH - 1) / KCH;
   if (p.kchunks == 0) p.kchunks = 1;
   if (cps <= 0) return BSFP8_EINVAL;
   p.cps = cps < p.kchunks ? cps : p.kchunks;
-  if ((c.kind == DIRECT || c.kind == ROWS || c.kind == DECODE) && p.cps > c.NWK * c.CW)
+  if ((c.kind == DIRECT || c.kind == ROWS || c.kind == DECODE || c.kind == PAIR) && p.cps > c.NWK * c.CW)
     return BSFP8_EINVAL;                                        // one pass
-  if (c.kind == DECODE && !c.ragged && s.K % KCH != 0) return BSFP8_EINVAL;  // whole exponent words
+  if ((c.kind == DECODE || c.kind == PAIR) && !c.ragged && s.K % KCH != 0) return BSFP8_EINVAL;  // whole words
   if (c.kind == TILE && (p.cps > TILE_MAX_CPS || s.K % KCH != 0)) return BSFP8_EINVAL;
   // slab kernel: K in whole chunks, splits begin on slab boundaries, one exponent word per lane
   if (c.kind == SLAB &&
@@ -1849,11 +2024,9 @@ int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const 
   k.yq = yq;
   k.ys = ys;
   k.levels = tree_levels(p.splits);
-  int base = 0, lv = 0;
-  for (int c2 = p.splits; c2 > 1; c2 = (c2 + 1) >> 1) {
-    k.level_base[lv++] = base;
-    base += c2 >> 1;
-  }
+  k.dm = make_fastdiv((uint32_t)p.mblocks);
+  k.dn = make_fastdiv((uint32_t)p.nblocks);
+  k.dg = make_fastdiv((uint32_t)s.G);
   const Config& c = kConfigs[p.cfg];
   const long long nwg = (long long)p.splits * s.G * p.nblocks * p.mblocks;
   if (nwg <= 0 || nwg > 0x7fffffffLL) return BSFP8_ESHAPE;

@@ -108,6 +108,7 @@ struct MxParams {
   int64_t ldq;                         // row stride of xq in bytes (a multiple of 128)
   uint32_t xq_bytes, xs_bytes, q_bytes, e_bytes;
   int M, G, N, K, kchunks, mblocks, nblocks, out_f32, nwg;
+  FastDiv dm, dn;                      // division by mblocks and nblocks
 };
 
 __device__ __forceinline__ void prefetch_mx_args(const MxParams& p) {
@@ -115,6 +116,7 @@ __device__ __forceinline__ void prefetch_mx_args(const MxParams& p) {
   asm volatile("" ::"s"(p.xq_bytes), "s"(p.xs_bytes), "s"(p.q_bytes), "s"(p.e_bytes), "s"(p.M), "s"(p.G),
                "s"(p.N), "s"(p.K));
   asm volatile("" ::"s"(p.kchunks), "s"(p.mblocks), "s"(p.nblocks), "s"(p.out_f32), "s"(p.nwg));
+  asm volatile("" ::"s"(p.dm.mul), "s"(p.dm.shift), "s"(p.dn.mul), "s"(p.dn.shift));
 }
 
 // Slot swizzle of a row piece of P granules (16 bytes each): XOR with the row inside a 16-granule
@@ -164,10 +166,12 @@ gemm_mx_kernel(MxParams p) {
   const int q4 = lane >> 4, r16 = lane & 15;
 
   int t = xcd_logical(blockIdx.x, p.nwg);
-  const int mb = t % p.mblocks;
-  t /= p.mblocks;
-  const int nb = t % p.nblocks;
-  const int g = t / p.nblocks;
+  int tq = fdiv(t, p.dm);
+  const int mb = t - tq * p.mblocks;
+  t = tq;
+  tq = fdiv(t, p.dn);
+  const int nb = t - tq * p.nblocks;
+  const int g = tq;
 
   const int K = p.K, M = p.M, N = p.N, G = p.G;
   const int n0 = nb * NB, m0 = mb * BM;
@@ -443,6 +447,8 @@ int launch_gemm_mx(const uint8_t* xq, const uint8_t* xs, int64_t ldq, int M, int
   k.kchunks = K / KCH;
   k.mblocks = (M + BM - 1) / BM;
   k.nblocks = N / NB;
+  k.dm = make_fastdiv((uint32_t)k.mblocks);
+  k.dn = make_fastdiv((uint32_t)k.nblocks);
   k.out_f32 = out_f32;
   const long long nwg = (long long)k.mblocks * k.nblocks * G;
   if (nwg <= 0 || nwg > 0x7fffffffLL) return BSFP8_ESHAPE;

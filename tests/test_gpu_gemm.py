@@ -128,13 +128,13 @@ def test_every_kernel_configuration():
         info = B.bsfp8_config_info(cfg)
         if info["row_scales"]:              # these read [G][N][K/32] exponents: test_gpu_row32.py
             continue
-        K = 768 if info["kind"] in (3, 4, 5) else 800
-        if info["kind"] == 4 and _takes_ragged_k(cfg):
+        K = 768 if info["kind"] in (3, 4, 5, 6) else 800
+        if info["kind"] in (4, 6) and _takes_ragged_k(cfg):
             K = 800                         # a decode instance built for a ragged last chunk
         M = min(2 * info["BM"] - 3, 256)
         x, q, e = _inputs(400 + cfg, M, G, N, K)
         exact = oracle.gemm_exact_f64(x, G, N, K, q, e)
-        if info["kind"] in (1, 2, 4):       # one pass: chunks per split <= CW * NWK
+        if info["kind"] in (1, 2, 4, 6):    # one pass: chunks per split <= CW * NWK
             cps_list = sorted({1, 2, info["CW"] * info["NWK"]})
         elif info["kind"] == 5:             # splits on 4-chunk slab boundaries, a partial last slab
             cps_list = (4, (K + 127) // 128)
