@@ -72,9 +72,10 @@ def test_workspace_and_plans(lib):
     assert len(maps) == 1
     for cfg in range(B.bsfp8_num_configs()):
         info = B.bsfp8_config_info(cfg)
-        # weight tiles are whole 16-row MFMA tiles, or half tiles (8 rows) for row-scale twins
+        # weight tiles are whole 16-row MFMA tiles, or 8 rows: half tiles for row-scale twins, and
+        # the paired decode kernel (kind 6), whose MFMA rows 8..15 carry the same rows' next chunk
         assert info["BM"] % 8 == 0 and info["threads"] % 64 == 0
-        assert info["NB"] % 16 == 0 or (info["row_scales"] and info["NB"] % 8 == 0)
+        assert info["NB"] % 16 == 0 or ((info["row_scales"] or info["kind"] == 6) and info["NB"] % 8 == 0)
 
 
 def test_plan_is_valid_for_every_shape_class(lib):
