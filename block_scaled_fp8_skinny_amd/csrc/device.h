@@ -99,33 +99,33 @@ __device__ __forceinline__ int xcd_logical(int i, int nwg) {
   return xcd * per + min(xcd, rem) + idx;
 }
 
-// Fetch every kernel argument at entry and keep it in scalar registers. The empty asm statements
-// take each field as an in-out operand, so the compiler issues all the argument loads together
-// (one round trip) instead of in dependent rounds, and - since each value is then the asm's
-// output, not a load it could repeat - it keeps the fields the epilogue needs (output pointers,
-// flags, sizes) in registers instead of loading them again from the argument segment after the
-// main loop, where each reload is a scalar memory round trip on the way to the first store.
-// (prefetch_args_only: the loads at entry without pinning, for the staged multi-pass kernel, which
-// holds enough scalar state of its own that pinning the epilogue's fields makes it spill.)
+// Kernel arguments, in two steps. At entry, prefetch_args takes the fields the first loads' addresses
+// need as inputs of empty asm statements: the compiler then issues their loads together (one round
+// trip) instead of in dependent rounds, and waits for no other field. Once the kernel's loads are
+// issued, pin_epilogue_args passes the fields the epilogue reads (output pointers, flags, sizes)
+// through an empty asm as in-out operands: each is then the asm's output, not a load the compiler
+// could repeat, so it stays in a register instead of being loaded again from the argument segment
+// after the main loop (each such reload is a scalar memory round trip on the way to the stores).
+__device__ __forceinline__ void prefetch_args(const KParams& p) {
+  asm volatile("" ::"s"(p.x), "s"(p.q), "s"(p.e), "s"(p.ldx), "s"(p.x_bytes), "s"(p.q_bytes), "s"(p.e_bytes));
+  asm volatile("" ::"s"(p.M), "s"(p.G), "s"(p.N), "s"(p.K), "s"(p.kchunks), "s"(p.cps), "s"(p.mblocks),
+               "s"(p.nblocks), "s"(p.nwg));
+}
+__device__ __forceinline__ void pin_epilogue_args(KParams& p) {
+  asm volatile("" : "+s"(p.y), "+s"(p.part), "+s"(p.yq), "+s"(p.ys), "+s"(p.slots));
+  asm volatile("" : "+s"(p.splits), "+s"(p.out_f32), "+s"(p.M), "+s"(p.G), "+s"(p.N), "+s"(p.levels));
+}
+// (prefetch_args_only: the same loads at entry, for the staged multi-pass kernel, which keeps
+// enough scalar state of its own that pinning the epilogue's fields makes it spill.)
 __device__ __forceinline__ void prefetch_args_only(const KParams& p) {
   asm volatile("" ::"s"(p.x), "s"(p.q), "s"(p.e), "s"(p.y), "s"(p.slots), "s"(p.ldx));
   asm volatile("" ::"s"(p.x_bytes), "s"(p.q_bytes), "s"(p.e_bytes), "s"(p.M), "s"(p.G), "s"(p.N), "s"(p.K));
   asm volatile("" ::"s"(p.kchunks), "s"(p.cps), "s"(p.splits), "s"(p.mblocks), "s"(p.nblocks), "s"(p.out_f32),
                "s"(p.nwg));
-  asm volatile("" ::"s"(p.dm.mul), "s"(p.dm.shift), "s"(p.dn.mul), "s"(p.dn.shift), "s"(p.dg.mul), "s"(p.dg.shift));
-}
-__device__ __forceinline__ void prefetch_args(KParams& p) {
-  asm volatile("" : "+s"(p.x), "+s"(p.q), "+s"(p.e), "+s"(p.y), "+s"(p.slots), "+s"(p.part), "+s"(p.ldx));
-  asm volatile("" : "+s"(p.yq), "+s"(p.ys), "+s"(p.x_bytes), "+s"(p.q_bytes), "+s"(p.e_bytes), "+s"(p.M),
-               "+s"(p.G), "+s"(p.N), "+s"(p.K));
-  asm volatile("" : "+s"(p.kchunks), "+s"(p.cps), "+s"(p.splits), "+s"(p.mblocks), "+s"(p.nblocks),
-               "+s"(p.out_f32), "+s"(p.nwg), "+s"(p.levels));
-  asm volatile("" : "+s"(p.dm.mul), "+s"(p.dm.shift), "+s"(p.dn.mul), "+s"(p.dn.shift), "+s"(p.dg.mul),
-               "+s"(p.dg.shift));
 }
 
 // Workgroup -> (m-block, n-block, group, split) of the plan's tile order (m-blocks fastest), from
-// the XCD-ordered logical index.
+// the XCD-ordered logical index of a one-dimensional grid.
 struct Tile {
   int mb, nb, g, s;
 };
@@ -141,6 +141,24 @@ __device__ __forceinline__ Tile tile_of(const KParams& p) {
   q = fdiv(t, p.dg);
   r.g = t - q * p.G;
   r.s = q;
+  return r;
+}
+// The same for a three-dimensional grid (x = n-block, y = group, z = split * mblocks + m-block),
+// which the decode kernels use: the hardware hands each workgroup its indices, so nothing stands
+// between the arguments and the first loads (a decode workgroup reads its own weight rows and the
+// shared activations, which every L2 holds after its first miss, so the XCD order buys nothing).
+__device__ __forceinline__ Tile tile_of_grid(const KParams& p) {
+  Tile r;
+  r.nb = blockIdx.x;
+  r.g = blockIdx.y;
+  const int z = blockIdx.z;
+  if (p.mblocks == 1) {
+    r.mb = 0;
+    r.s = z;
+  } else {
+    r.s = fdiv(z, p.dm);
+    r.mb = z - r.s * p.mblocks;
+  }
   return r;
 }
 

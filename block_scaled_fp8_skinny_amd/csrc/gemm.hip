@@ -370,6 +370,7 @@ gemm_direct_kernel(KParams p) {
   }
   __builtin_amdgcn_sched_barrier(0);
   // (3) stage X and the exponents in LDS
+  pin_epilogue_args(p);                             // the loads are issued
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const int f = tid + i * NTHR;
@@ -627,6 +628,7 @@ gemm_rows_kernel(KParams p) {
   Buf ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) load(j, ring[j]);
+  pin_epilogue_args(p);                             // the first loads are issued
   __builtin_amdgcn_sched_barrier(0);
   if (tid < EROWS * ECOLS) e_lds[tid] = (uint8_t)ev;
   __syncthreads();
@@ -851,6 +853,7 @@ gemm_tile_kernel(KParams p) {
 
 #pragma unroll
   for (int j = 0; j < D - GI; ++j) issue(j);
+  pin_epilogue_args(p);                             // the first loads are issued
 
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -1010,7 +1013,7 @@ gemm_decode_kernel(KParams p) {
   const int wn = wave % NWN, wk = wave / NWN;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  const Tile tl = tile_of(p);
+  const Tile tl = tile_of_grid(p);
   const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
 
   const int K = p.K, M = p.M, N = p.N, G = p.G;
@@ -1076,6 +1079,7 @@ gemm_decode_kernel(KParams p) {
         }
     }
   }
+  pin_epilogue_args(p);                             // every load is issued
   wait_vmcnt_le<WPW>();                             // this wave's exponent and X loads
   lds_barrier();                                    // ... everyone's
 
@@ -1151,10 +1155,15 @@ gemm_decode_kernel(KParams p) {
     }
     __syncthreads();
     if (wk != 0) return;
+    f32x4_t part[NWK - 1][NT];                      // all reads issued before the first add
 #pragma unroll
     for (int w = 1; w < NWK; ++w)
 #pragma unroll
-      for (int ts = 0; ts < NT; ++ts) acc[ts] += red[(((w - 1) * NWN + wn) * NT + ts) * WAVE + lane];
+      for (int ts = 0; ts < NT; ++ts) part[w - 1][ts] = red[(((w - 1) * NWN + wn) * NT + ts) * WAVE + lane];
+#pragma unroll
+    for (int w = 1; w < NWK; ++w)
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) acc[ts] += part[w - 1][ts];
   }
   // (6) output
   const int m = m0 + r16;
@@ -1306,6 +1315,7 @@ gemm_slab_kernel(KParams p) {
 
 #pragma unroll
   for (int j = 0; j < S - 1; ++j) issue(j);
+  pin_epilogue_args(p);                             // the first loads are issued
 
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -1482,7 +1492,11 @@ gemm_slab_kernel(KParams p) {
 // Each output's fp32 sum: per wave, the chain of the first chunks of its pairs and the chain of
 // the second chunks, added; then the waves in ascending order. It depends on the chunk count, not
 // on K, so K zero-padded inside the same chunk count gives the same sums.
-template <int NWK, int CP, bool RG>
+// FULL instances serve the plans whose one split covers exactly the workgroup's NWK * CW chunks
+// (K = 128 * NWK * CW): every chunk is then in range and no load, factor or output needs a range
+// test, which shortens the path from the arguments to the first loads (each instruction there
+// delays the whole stream) and the epilogue. Their sums are those of the general instance.
+template <int NWK, int CP, bool RG, bool FULL = false>
 __global__ void __launch_bounds__(WAVE * NWK)
 gemm_pair_kernel(KParams p) {
   constexpr int CW = 2 * CP;                        // chunks per wave
@@ -1492,6 +1506,7 @@ gemm_pair_kernel(KParams p) {
   constexpr int XL = XR * XS / 64;                  // X loads per wave
   static_assert(CP == 1 || CP == 2 || CP == 4, "X row slices tile a wave load");
   static_assert(!RG || CW + 1 <= 64, "exponent words of a ragged range");
+  static_assert(!(RG && FULL), "a whole range has no ragged chunk");
   __shared__ uint4 x_lds[NWK * XR * XS];
   __shared__ uint4 w_lds[NWK * CW * WT];
   __shared__ uint32_t e_lds[NWK * 64];
@@ -1501,13 +1516,13 @@ gemm_pair_kernel(KParams p) {
   const int lane = threadIdx.x & 63, wk = threadIdx.x >> 6;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  const Tile tl = tile_of(p);
+  const Tile tl = tile_of_grid(p);
   const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
 
   const int K = p.K, M = p.M, N = p.N, G = p.G;
   const int n0 = nb * 8, m0 = mb * XR;
-  const int c_begin = s * p.cps;
-  const int c_end = min(c_begin + p.cps, p.kchunks);
+  const int c_begin = FULL ? 0 : s * p.cps;
+  const int c_end = FULL ? NWK * CW : min(c_begin + p.cps, p.kchunks);
   const int cw0 = c_begin + wk * CW;                // this wave's first chunk
   const int KB = K / 32;
 
@@ -1527,7 +1542,7 @@ gemm_pair_kernel(KParams p) {
     lds_load4(re, lds_addr(ew), lane <= CW && wd < end ? wd : OOB);
   } else {
     const int c = cw0 + lane;
-    lds_load4(re, lds_addr(ew), lane < CW && c < c_end ? (uint32_t)(erow * KB + c * 4) : OOB);
+    lds_load4(re, lds_addr(ew), lane < CW && (FULL || c < c_end) ? (uint32_t)(erow * KB + c * 4) : OOB);
   }
   // (2) X rows m0 .. m0 + 7 over the wave's chunks: load i fills slots 64i .. 64i + 63 of the rows'
   //     slices (row-major); the lane fetches the granule that belongs in its slot. Loads whose rows
@@ -1541,7 +1556,7 @@ gemm_pair_kernel(KParams p) {
     const int m = m0 + row;
     const int k = (cw0 + cl) * KCH + gr * 8;
     const uint32_t off = (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K + k) * 2);
-    const bool ok = m < M && cw0 + cl < c_end && (!RG || k < K);
+    const bool ok = m < M && (FULL || cw0 + cl < c_end) && (!RG || k < K);
     if (m0 + (i * 64) / XS < M) lds_load16(rx, lds_addr(xw + i * 64), ok ? off : OOB);
   }
   // (3) weight chunks, one load each: lane l fills row R = l / 8, slot l % 8 with granule
@@ -1554,12 +1569,13 @@ gemm_pair_kernel(KParams p) {
     for (int cl = 0; cl < CW; ++cl) {
       const int c = cw0 + cl;
       const uint32_t off = qrow + (uint32_t)(c * KCH + gsrc * 16);
-      const bool ok = c < c_end && (!RG || c * KCH + gsrc * 16 < K);
+      const bool ok = (FULL || c < c_end) && (!RG || c * KCH + gsrc * 16 < K);
       lds_load16_stream(rq, lds_addr(ww + cl * WT), ok ? off : OOB);
     }
   }
 
   // (4) pairs, each once its own loads (and everything issued before them) have landed
+  pin_epilogue_args(p);                             // every load is issued
   const int half = r16 >> 3;                        // A rows / B columns 8..15: the pair's second chunk
   const int R = r16 & 7;                            // weight row of this lane (A operand)
   const int mx = r16 & 7;                           // X row of this lane (B operand)
@@ -1570,7 +1586,7 @@ gemm_pair_kernel(KParams p) {
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto pair = [&](int pp) {
     const int cl = 2 * pp + half;
-    const bool valid = cw0 + cl < c_end;
+    const bool valid = FULL || cw0 + cl < c_end;
     const uint4* wt = ww + cl * WT + R * 8;
     const uint4 a = wt[q4 ^ wsw], b = wt[(4 + q4) ^ wsw];
     // the exponent bytes are read whatever the chunk (past the range they are zeros) and then
@@ -1608,24 +1624,27 @@ gemm_pair_kernel(KParams p) {
   for (int v = 0; v < 4; ++v) other[v] = __shfl_down(acc[v], 40);
   acc += other;
   const bool useful = q4 < 2 && r16 < 8;
-  const int slot = q4 * 8 + r16;
+  const int slot = useful ? q4 * 8 + r16 : 0;
 
-  // (6) waves along K: ascending-order sum through LDS
+  // (6) waves along K: ascending-order sum through LDS. Wave 0 issues all its reads before the
+  //     first add (a condition inside the loop would make each read a separate round trip).
   if constexpr (NWK > 1) {
     if (wk > 0 && useful) red[(wk - 1) * 16 + slot] = acc;
     __syncthreads();
     if (wk != 0) return;
+    f32x4_t part[NWK - 1];
 #pragma unroll
-    for (int w = 1; w < NWK; ++w)
-      if (useful) acc += red[(w - 1) * 16 + slot];
+    for (int w = 1; w < NWK; ++w) part[w - 1] = red[(w - 1) * 16 + slot];
+#pragma unroll
+    for (int w = 1; w < NWK; ++w) acc += part[w - 1];
   }
   // (7) output: X row m0 + r16, weight rows n0 + 4 q4 .. + 3
   const int m = m0 + r16;
   const bool live = useful && m < M;
   const int n = n0 + 4 * q4;
   const size_t o = ((size_t)m * G + g) * N + n;
-  if (p.splits == 1 && !p.part) {
-    if (live) {
+  if (FULL || (p.splits == 1 && !p.part)) {             // (FULL: one split; partials mode then
+    if (live) {                                         // passes the workspace as an fp32 y)
       if (p.out_f32) {
         *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + o) = acc;
       } else {
@@ -1672,7 +1691,7 @@ reduce_splits_kernel(const float* __restrict__ part, void* __restrict__ y, int64
 // ---------------------------------------------------------------------------------------------
 typedef void (*KernelFn)(KParams);
 
-enum Kind { STAGED = 0, DIRECT = 1, ROWS = 2, TILE = 3, DECODE = 4, SLAB = 5, PAIR = 6 };
+enum Kind { STAGED = 0, DIRECT = 1, ROWS = 2, TILE = 3, DECODE = 4, SLAB = 5, PAIR = 6, PAIR_FULL = 7 };
 
 struct Config {
   int MT, NT, NWM, NWN, NWK, CW;         // TILE: CW = chunks in flight; SLAB: CW = ring stages;
@@ -1692,6 +1711,7 @@ struct Config {
 #define TCFG(MT, NT, NWM, NWN, D, GI) {MT, NT, NWM, NWN, 1, D, gemm_tile_kernel<MT, NT, NWM, NWN, D, GI>, TILE}
 #define SCFG(MT, NT, NWM, NWN, NWK, S) {MT, NT, NWM, NWN, NWK, S, gemm_slab_kernel<MT, NT, NWM, NWN, NWK, S>, SLAB}
 #define PCFG(NWK, CP, RG) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, RG>, PAIR, 0, 8, RG}
+#define PFCFG(NWK, CP) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, false, true>, PAIR_FULL, 0, 8, 0}
 
 const Config kConfigs[] = {
     CFG(1, 1, 4, 1, 4),   // 0  small: 64 rows, one wave per 16 rows, 4 chunks per wave
@@ -1790,6 +1810,10 @@ const Config kConfigs[] = {
     PCFG(3, 1, true),         // 90 pair, K not a multiple of 128, up to 6 chunks
     PCFG(4, 1, true),         // 91 pair, K not a multiple of 128, up to 8 chunks
     PCFG(4, 1, false),        // 92 pair: 4 waves along K x 2 chunks
+    // paired decode over exactly the workgroup's chunks (K = 128 * NWK * CW, one split)
+    PFCFG(8, 2),              // 93 pair, whole range: 8 waves x 4 chunks (K = 4096)
+    PFCFG(4, 4),              // 94 pair, whole range: 4 waves x 8 chunks (K = 4096)
+    PFCFG(3, 1),              // 95 pair, whole range: 3 waves x 2 chunks (K = 768)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1806,7 +1830,7 @@ int num_gemm_configs() { return kNumConfigs; }
 int gemm_config_info(int cfg, int* out) {
   if (cfg < 0 || cfg >= kNumConfigs) return BSFP8_EINVAL;
   const Config& c = kConfigs[cfg];
-  out[0] = c.kind == DECODE || c.kind == PAIR ? c.MT : 16 * c.MT * c.NWM;
+  out[0] = c.kind == DECODE || c.kind == PAIR || c.kind == PAIR_FULL ? c.MT : 16 * c.MT * c.NWM;
   out[1] = c.TR * c.NT * c.NWN;
   out[2] = WAVE * c.NWM * c.NWN * c.NWK;
   out[3] = c.CW;
@@ -1835,13 +1859,15 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   const Config& c = kConfigs[cfg];
   GemmPlan p{};
   p.cfg = cfg;
-  p.BM = c.kind == DECODE || c.kind == PAIR ? c.MT : 16 * c.MT * c.NWM;
+  p.BM = c.kind == DECODE || c.kind == PAIR || c.kind == PAIR_FULL ? c.MT : 16 * c.MT * c.NWM;
   p.NB = c.TR * c.NT * c.NWN;
   if (s.N % p.NB) return BSFP8_ESHAPE;
   p.kchunks = (s.K + KCH - 1) / KCH;
   if (p.kchunks == 0) p.kchunks = 1;
   if (cps <= 0) return BSFP8_EINVAL;
   p.cps = cps < p.kchunks ? cps : p.kchunks;
+  if (c.kind == PAIR_FULL && (p.kchunks != c.NWK * c.CW || p.cps != p.kchunks || s.K % KCH != 0))
+    return BSFP8_EINVAL;                                        // exactly the workgroup's chunks
   if ((c.kind == DIRECT || c.kind == ROWS || c.kind == DECODE || c.kind == PAIR) && p.cps > c.NWK * c.CW)
     return BSFP8_EINVAL;                                        // one pass
   if ((c.kind == DECODE || c.kind == PAIR) && !c.ragged && s.K % KCH != 0) return BSFP8_EINVAL;  // whole words
@@ -1875,16 +1901,17 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
 //    kernel, one split, for every row count. Each output's fp32 sum is then the same ascending
 //    chain of chunks and MFMAs whatever the tile, so a row's result does not depend on how many
 //    rows share the call.
-//  * Decode rows (at most 8, or 16 with a long K): the decode kernel (everything streamed into
-//    LDS, 8 rows of X per workgroup) when K is whole
-//    128-wide chunks; otherwise the one-pass kernel with X rows in LDS and the same waves and
-//    chunks, whose fp32 chains are the same, so K zero-padded to whole chunks (576 -> 640) gives
-//    bitwise the same Y on the faster kernel.
+//  * Decode rows (at most 8) over exactly 32 chunks on at most 256 eight-row tiles (wo_a at G = 2):
+//    the paired decode kernel on the whole range, one workgroup per CU.
+//  * Other decode rows (at most 8, or 16 with a long K): the decode kernel (everything streamed
+//    into LDS, 8 rows of X per workgroup); when K is not whole 128-wide chunks its ragged
+//    instances, which read zeros past K, so K zero-padded to whole chunks (576 -> 640) gives
+//    bitwise the same Y.
 //  * Few rows (at most 32): the one-pass register kernel with X rows in LDS, one 16-row block of X
 //    per workgroup.
 //  * More rows: the register kernel with both operands in registers and 16-48 rows of X per
 //    workgroup (no split while the K range fits one pass of 32 chunks).
-int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
+int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool allow_pair) {
   const int kchunks = (s.K + KCH - 1) / KCH > 0 ? (s.K + KCH - 1) / KCH : 1;
   const bool n64 = (s.N % 64) == 0;
   const bool tile_ok = s.K % KCH == 0 && kchunks <= TILE_MAX_CPS && s.N % 128 == 0;
@@ -1896,6 +1923,11 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
     else if (path == PATH_SMALL || s.M <= 16) cfg = n64 ? 0 : 3;
     else if (s.M <= 32) cfg = n64 ? 9 : 15;
     else cfg = n64 ? 10 : 16;
+  } else if (allow_pair && s.M <= 8 && s.K == 32 * KCH && split_k <= 1 && (long long)s.G * s.N / 8 <= 256) {
+    // decode rows on at most 256 eight-row tiles over exactly 32 chunks: the paired kernel on the
+    // whole range (one workgroup per CU, every MFMA computing two chunks)
+    cfg = 93;
+    cps = kchunks;
   } else if (s.M <= 8 || (s.M <= 16 && kchunks > 8)) {
     // decode kernel (8 rows of X per workgroup); for K that is not whole chunks its ragged
     // instance, whose last chunk reads zeros past K: K zero-padded to whole chunks gives bitwise
@@ -1939,7 +1971,9 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan) {
 // The MXFP8-epilogue GEMM runs the plan bsfp8_gemm would pick for the same arguments, so its
 // codes quantise exactly the fp32 outputs of that call.
 int plan_gemm_mxfp8(const GemmShape& s, int split_k, GemmPlan* plan) {
-  return plan_gemm(s, s.M <= 8 ? PATH_SMALL : PATH_MID, split_k, plan);
+  // not the paired kernel: its 8-row tiles hold a quarter of an MX block, while the 16-row
+  // decode plan has a fused form that quantises whole blocks in the kernel
+  return plan_gemm(s, s.M <= 8 ? PATH_SMALL : PATH_MID, split_k, plan, false);
 }
 
 // Built-in choice for weights with one exponent per row and 32 columns (a GEMV for up to 16
@@ -2031,7 +2065,12 @@ int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const 
   const long long nwg = (long long)p.splits * s.G * p.nblocks * p.mblocks;
   if (nwg <= 0 || nwg > 0x7fffffffLL) return BSFP8_ESHAPE;
   k.nwg = (int)nwg;
-  hipLaunchKernelGGL(c.fn, dim3((unsigned)nwg), dim3(WAVE * c.NWM * c.NWN * c.NWK), 0, stream, k);
+  // the decode kernels take their tile from a three-dimensional grid (x = n-block, y = group,
+  // z = split * mblocks + m-block); the others from the XCD-ordered index of a flat one
+  const bool grid3 = c.kind == DECODE || c.kind == PAIR || c.kind == PAIR_FULL;
+  const dim3 grid = grid3 ? dim3((unsigned)p.nblocks, (unsigned)s.G, (unsigned)(p.splits * p.mblocks))
+                          : dim3((unsigned)nwg);
+  hipLaunchKernelGGL(c.fn, grid, dim3(WAVE * c.NWM * c.NWN * c.NWK), 0, stream, k);
   if (c.kind == TILE && p.splits > 1 && !partials) {
     const int64_t n4 = (int64_t)s.M * s.G * s.N / 4;
     hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,

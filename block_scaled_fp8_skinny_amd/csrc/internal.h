@@ -29,8 +29,9 @@ struct GemmPlan {
 
 enum Path { PATH_SMALL = 0, PATH_MID = 1 };
 
-// Picks the kernel configuration and split for a shape; returns a bsfp8_status.
-int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan);
+// Picks the kernel configuration and split for a shape; returns a bsfp8_status. allow_pair = false
+// leaves out the paired decode kernel (the MXFP8-epilogue GEMM quantises whole 32-row blocks).
+int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool allow_pair = true);
 // Plan for an explicit configuration index and chunks per split.
 int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan);
 // Plan of the MXFP8-epilogue GEMM (bsfp8_gemm_mxfp8).

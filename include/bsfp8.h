@@ -259,11 +259,14 @@ BSFP8_API int bsfp8_reduce_quantize_mx(const float* part, int64_t S, int64_t M, 
  * workspace must not be used by two calls that can run at the same time. */
 BSFP8_API size_t bsfp8_workspace_bytes_mxfp8(int64_t M, int64_t G, int64_t N, int64_t K, int split_k);
 
-/* The GEMM of bsfp8_gemm with the MXFP8 epilogue: the fp32 results of the GEMM's plan for
- * (M, G, N, K, split_k) - the sum itself with one split, else each split's partial - go to ws,
- * and the epilogue adds the partials in the order of that plan's own combine (pairwise for the
- * one-pass kernels, ascending for the tile kernel), so the quantised values are exactly the fp32
- * outputs bsfp8_gemm returns for the same arguments with out_dtype = BSFP8_OUT_F32.
+/* The GEMM of bsfp8_gemm with the MXFP8 epilogue: the fp32 results of the plan that
+ * bsfp8_plan_info(..., path 3) reports for (M, G, N, K, split_k) - the sum itself with one split,
+ * else each split's partial - go to ws, and the epilogue adds the partials in the order of that
+ * plan's own combine (pairwise for the one-pass kernels, ascending for the tile kernel), so the
+ * quantised values are exactly the fp32 outputs of bsfp8_gemm_config with that configuration and
+ * chunks per split (out_dtype = BSFP8_OUT_F32). That is bsfp8_gemm's own plan, except on the
+ * decode shapes where bsfp8_gemm takes the paired kernel: its 8-row tiles hold a quarter of an MX
+ * block, so this call keeps the 16-row decode plan, whose fused form quantises whole blocks.
  *   x, ldx, M, G, N, K, q, e, split_k : as bsfp8_gemm (1 <= M <= 256).
  *   ws    : >= bsfp8_workspace_bytes_mxfp8(M, G, N, K, split_k) bytes (device, 16-byte aligned).
  *   yq    : uint8_t e4m3 codes [M][G*N] (device, contiguous, 16-byte aligned).

@@ -73,9 +73,9 @@ def test_workspace_and_plans(lib):
     for cfg in range(B.bsfp8_num_configs()):
         info = B.bsfp8_config_info(cfg)
         # weight tiles are whole 16-row MFMA tiles, or 8 rows: half tiles for row-scale twins, and
-        # the paired decode kernel (kind 6), whose MFMA rows 8..15 carry the same rows' next chunk
+        # the paired decode kernel (kinds 6, 7), whose MFMA rows 8..15 carry the same rows' next chunk
         assert info["BM"] % 8 == 0 and info["threads"] % 64 == 0
-        assert info["NB"] % 16 == 0 or ((info["row_scales"] or info["kind"] == 6) and info["NB"] % 8 == 0)
+        assert info["NB"] % 16 == 0 or ((info["row_scales"] or info["kind"] in (6, 7)) and info["NB"] % 8 == 0)
 
 
 def test_plan_is_valid_for_every_shape_class(lib):
@@ -208,11 +208,17 @@ def test_mxfp8_epilogue_checks_and_plans(lib):
     assert R(null, 1, 2, 64, 1, fake, fake, null) == B.EINVAL
     assert R(ctypes.c_void_p(4100), 1, 2, 64, 1, fake, fake, null) == B.ESTRIDE
     assert R(fake, 1, 2, 64, 1, ctypes.c_void_p(4100), fake, null) == B.ESTRIDE
-    # the epilogue GEMM runs bsfp8_gemm's plan; its workspace holds one fp32 copy per split
+    # the epilogue GEMM runs bsfp8_gemm's plan, except where that is the paired decode kernel
+    # (8-row tiles, a quarter of an MX block): there it keeps the 16-row decode plan, whose fused
+    # form quantises whole blocks; its workspace holds one fp32 copy per split
     for M, G, N, K, sk in ((6, 2, 1024, 4096, 0), (6, 2, 1024, 4096, 4), (64, 2, 1024, 4096, 0),
                            (16, 1, 32768, 5120, 0), (16, 1, 32768, 5120, 2), (6, 1, 5120, 576, 0)):
         p3 = B.bsfp8_plan_info(M, G, N, K, split_k=sk, path=3)
-        assert p3 == B.bsfp8_plan_info(M, G, N, K, split_k=sk, path=2)
+        p2 = B.bsfp8_plan_info(M, G, N, K, split_k=sk, path=2)
+        if B.bsfp8_config_info(p2["cfg"])["kind"] in (6, 7):
+            assert B.bsfp8_config_info(p3["cfg"])["kind"] == 4 and p3["splits"] == p2["splits"]
+        else:
+            assert p3 == p2
         assert B.bsfp8_workspace_bytes_mxfp8(M, G, N, K, sk) == p3["splits"] * M * G * N * 4
         assert B.bsfp8_workspace_bytes_mxfp8_config(M, G, N, K, p3["cfg"], p3["cps"]) == p3["splits"] * M * G * N * 4
     assert B.bsfp8_workspace_bytes_mxfp8(0, 2, 1024, 4096, 0) == 0

@@ -132,7 +132,7 @@ def test_gemm_mxfp8_wo_a_full_size(wo_a_weight, M, sk):
     xt = to_gpu_bf16(x)
     yq, ys = B.bsfp8_gemm_mxfp8(xt, qt, et, split_k=sk)
     # the same plan's fp32 output, quantised by the stand-alone epilogue with one partial
-    y32 = B.bsfp8_gemm(xt, qt, et, split_k=sk, out_dtype="f32")
+    y32 = B.bsfp8_gemm_config(xt, qt, et, plan["cfg"], plan["cps"], out_dtype="f32")
     q2, s2 = B.bsfp8_reduce_quantize_mx(y32.reshape(1, M, G * N), B.SUM_ASCENDING)
     torch.cuda.synchronize()
     assert torch.equal(yq, q2) and torch.equal(ys, s2)

@@ -131,11 +131,15 @@ def test_every_kernel_configuration():
         K = 768 if info["kind"] in (3, 4, 5, 6) else 800
         if info["kind"] in (4, 6) and _takes_ragged_k(cfg):
             K = 800                         # a decode instance built for a ragged last chunk
+        if info["kind"] == 7:               # exactly the workgroup's chunks, one split
+            K = 128 * info["CW"] * info["NWK"]
         M = min(2 * info["BM"] - 3, 256)
         x, q, e = _inputs(400 + cfg, M, G, N, K)
         exact = oracle.gemm_exact_f64(x, G, N, K, q, e)
         if info["kind"] in (1, 2, 4, 6):    # one pass: chunks per split <= CW * NWK
             cps_list = sorted({1, 2, info["CW"] * info["NWK"]})
+        elif info["kind"] == 7:
+            cps_list = (K // 128,)
         elif info["kind"] == 5:             # splits on 4-chunk slab boundaries, a partial last slab
             cps_list = (4, (K + 127) // 128)
         else:                               # several splits, and one split over all the chunks

@@ -77,7 +77,7 @@ def test_random_gemm_mxfp8(case):
     print(f"case {case}: M={M} G={G} N={N} K={K} split={split} plan {plan}", flush=True)
     xt, qt, et = _x_gpu(x, G, K), to_gpu_u8(q), to_gpu_u8(e)
     yq, ys = B.bsfp8_gemm_mxfp8(xt, qt, et, split_k=split)
-    y32 = B.bsfp8_gemm(xt, qt, et, split_k=split, out_dtype="f32")
+    y32 = B.bsfp8_gemm_config(xt, qt, et, plan["cfg"], plan["cps"], out_dtype="f32")   # the same plan
     q2, s2 = B.bsfp8_reduce_quantize_mx(y32.reshape(1, M, G * N), B.SUM_ASCENDING)
     torch.cuda.synchronize()
     assert torch.equal(yq, q2) and torch.equal(ys, s2)
