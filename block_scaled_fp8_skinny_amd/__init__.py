@@ -37,6 +37,7 @@ _SIGS = {
     "bsfp8_gemm_small": (_I, _GEMM_ARGS),
     "bsfp8_gemm_mid": (_I, _GEMM_ARGS),
     "bsfp8_gemm": (_I, _GEMM_ARGS),
+    "bsfp8_gemm_no_alloc": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _P, _I, _P]),
     "bsfp8_num_configs": (_I, []),
     "bsfp8_read_floor": (_I, [_P, _SZ, _I, _P, _P]),
     "bsfp8_config_info": (_I, [_I, ctypes.POINTER(_I)]),
@@ -305,6 +306,20 @@ def _gemm(entry, x, q, e, split_k, ws, out, out_dtype):
 def bsfp8_gemm(x, q, e, split_k=0, ws=None, out=None, out_dtype="bf16"):
     """Y [M, G, N] = per group X[:, g*K:(g+1)*K] @ W_g^T, W_g rebuilt from the twin (q, e)."""
     return _gemm("bsfp8_gemm", x, q, e, split_k, ws, out, out_dtype)
+
+
+NO_ALLOC_SCRATCH_BYTES = 16 << 20   # BSFP8_NO_ALLOC_SCRATCH_BYTES of include/bsfp8.h
+
+
+def bsfp8_gemm_no_alloc(x, q, e, split_k=0, out=None, out_dtype="bf16"):
+    """bsfp8_gemm without a workspace: a split plan uses the library's static per-GPU scratch
+    (calls that can overlap on one GPU must not be made)."""
+    x, M, ldx, q, G, N, K = _operands(x, q, e, _block_exps)
+    od = _out_dtype(out_dtype)
+    out = _out(out, M, G, N, od, x.device)
+    _check(lib().bsfp8_gemm_no_alloc(_ptr(x), ldx, M, G, N, K, _ptr(q), _ptr(e), split_k, _ptr(out), od,
+                                     _stream(x)), "bsfp8_gemm_no_alloc")
+    return out
 
 
 def bsfp8_gemm_small(x, q, e, split_k=0, ws=None, out=None, out_dtype="bf16"):

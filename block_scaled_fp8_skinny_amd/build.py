@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbsfp8.so")
-SOURCES = ["api.cpp", "gemm.hip", "prep.hip", "mx.hip", "epilogue.hip", "measure.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "prep.hip", "mx.hip", "epilogue.hip", "measure.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled for every device pass.

@@ -323,6 +323,30 @@ int bsfp8_gemm(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, 
   return run_gemm(path, 256, x, ldx, M, G, N, K, q, e, split_k, ws, ws_bytes, y, out_dtype, stream);
 }
 
+int bsfp8_gemm_no_alloc(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                        const uint8_t* q, const uint8_t* e, int split_k, void* y, int out_dtype, void* stream) {
+  GemmShape s;
+  int st = check_gemm(x, ldx, M, G, N, K, q, e, y, out_dtype, split_k, 256, &s);
+  if (st != BSFP8_OK || M == 0) return st;
+  GemmPlan p;
+  st = plan_gemm(s, M <= 8 ? PATH_SMALL : PATH_MID, split_k, &p);
+  if (st != BSFP8_OK) return st;
+  hipStream_t hs = as_stream(stream);
+  void* ws = nullptr;
+  if (p.ws_bytes > 0) {
+    if (p.ws_bytes > BSFP8_NO_ALLOC_SCRATCH_BYTES) return BSFP8_EWORKSPACE;
+    st = scratch_for_stream(hs, &ws);
+    if (st != BSFP8_OK) return st;
+  }
+  st = check_gemm_alias(s, x, q, e, false, ws, p.ws_bytes, y, out_dtype);
+  if (st != BSFP8_OK) return st;
+  if (gemm_ws_needs_zero(p)) {
+    st = launch_clear(ws, p.ws_bytes, hs);
+    if (st != BSFP8_OK) return st;
+  }
+  return launch_gemm(s, p, x, q, e, ws, y, out_dtype == BSFP8_OUT_F32, hs);
+}
+
 size_t bsfp8_workspace_bytes_row32(int64_t M, int64_t G, int64_t N, int64_t K, int split_k) {
   if (M <= 0 || M > 16 || G < 1 || N < 32 || K < 128 || N % 32 || K % 128 || split_k < 0 || split_k > 64) return 0;
   if (G > 4096 || N > (1 << 24) || K > (1 << 24)) return 0;

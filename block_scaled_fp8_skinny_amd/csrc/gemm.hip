@@ -1849,6 +1849,8 @@ int gemm_partials_order(const GemmPlan& p) {
   return kConfigs[p.cfg].kind == TILE ? BSFP8_SUM_ASCENDING : BSFP8_SUM_PAIRWISE;
 }
 
+int gemm_ws_needs_zero(const GemmPlan& p) { return p.splits > 1 && kConfigs[p.cfg].kind != TILE; }
+
 size_t gemm_partials_bytes(const GemmShape& s, const GemmPlan& p) {
   return (size_t)p.splits * s.M * s.G * s.N * 4;
 }

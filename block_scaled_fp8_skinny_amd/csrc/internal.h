@@ -55,6 +55,9 @@ int launch_gemm(const GemmShape& s, const GemmPlan& p, const uint16_t* x, const 
 // Order in which a plan's own combine adds its split partials: BSFP8_SUM_ASCENDING (tile kernel
 // and its reduce kernel) or BSFP8_SUM_PAIRWISE (the one-pass kernels' exchange tree).
 int gemm_partials_order(const GemmPlan& p);
+// 1 when the plan's workspace must hold zeros before the launch (the one-pass kernels' exchange
+// slots; the tile kernel's partials are written whole).
+int gemm_ws_needs_zero(const GemmPlan& p);
 // Workspace of launch_gemm with partials: splits * M * G * N fp32 values.
 size_t gemm_partials_bytes(const GemmShape& s, const GemmPlan& p);
 
@@ -91,6 +94,12 @@ int mx_pick(int M, int G, int N);
 
 // Plain-read floor of a weight stream (measure.hip): reads `bytes` once with the GEMM's load shape.
 int launch_read_floor(const void* p, size_t bytes, int nwg, uint32_t* sink, hipStream_t stream);
+
+// Static scratch of bsfp8_gemm_no_alloc (scratch.hip): the array's address on the device of
+// `stream` (the current device for a null stream), looked up once per device.
+int scratch_for_stream(hipStream_t stream, void** out);
+// Zero-fills `bytes` (a multiple of 16) at p with a kernel on `stream`.
+int launch_clear(void* p, size_t bytes, hipStream_t stream);
 
 inline int hip_status(hipError_t err) { return err == hipSuccess ? BSFP8_OK : BSFP8_EHIP; }
 

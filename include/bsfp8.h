@@ -170,6 +170,22 @@ BSFP8_API int bsfp8_gemm(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, i
                const uint8_t* q, const uint8_t* e, int split_k, void* ws, size_t ws_bytes,
                void* y, int out_dtype, void* stream);
 
+/* bsfp8_gemm without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Arguments,
+ * plans, kernels, summation order and results are those of bsfp8_gemm with the same split_k
+ * (bitwise the same Y). A plan that needs a workspace uses a fixed array in the library's own
+ * device memory instead: BSFP8_NO_ALLOC_SCRATCH_BYTES bytes, of which each GPU the library runs
+ * on holds its own copy until the process ends. The call allocates nothing; it enqueues a small zero-fill
+ * kernel before a plan whose exchange slots must start at zero. Errors as bsfp8_gemm, plus
+ * BSFP8_EWORKSPACE (nothing enqueued) when the plan's workspace (bsfp8_workspace_bytes) exceeds
+ * BSFP8_NO_ALLOC_SCRATCH_BYTES, and BSFP8_EHIP when the array's address cannot be looked up.
+ * Every call on one GPU shares that GPU's array: calls that can overlap on one GPU (two streams,
+ * two threads) race and must not be made; calls ordered on one stream are safe. */
+#define BSFP8_NO_ALLOC_SCRATCH_BYTES (16u << 20)
+BSFP8_API int bsfp8_gemm_no_alloc(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int64_t N, int64_t K,
+                                  const uint8_t* q, const uint8_t* e, int split_k, void* y, int out_dtype,
+                                  void* stream);
+
 /* The GEMM on a twin with one exponent per row and 32 columns (bsfp8_make_twin_row32): the GEMV
  * of page "recipes/docker-images/mia-tp4/docs/tp4-adapters.md", row draft_main_proj, for up to
  * 16 rows. W[g][n][k] = bf16(e4m3(q[g][n][k]) * 2^(e[g][n][k/32] - 127)); otherwise arguments,

@@ -137,6 +137,19 @@ def test_argument_checks_return_before_gpu_work(lib):
     assert lib.bsfp8_dequant(qa, ea, 1, 64, 64, ctypes.c_void_p((2 << 32) + 16), null) == B.EINVAL
     assert lib.bsfp8_pad_k_input(xa, 64, 2, 1, 64, 128, ctypes.c_void_p((1 << 32) + 64), null) == B.EINVAL
     assert lib.bsfp8_pad_k_weight(qa, ea, 1, 64, 64, 128, ya, ctypes.c_void_p((3 << 32) + 2), null) == B.EINVAL
+    # the entry point without a workspace: the same host checks, and a plan beyond its static
+    # scratch is refused before the scratch is looked up or anything is enqueued
+    NA = lib.bsfp8_gemm_no_alloc
+    assert NA(null, 64, 1, 1, 64, 64, null, null, 0, null, 7, null) == B.EINVAL
+    assert NA(null, 64, 300, 1, 64, 64, null, null, 0, null, 0, null) == B.ESHAPE
+    assert NA(null, 64, 0, 1, 64, 64, null, null, 0, null, 0, null) == B.OK
+    assert NA(fake, 60, 1, 1, 64, 64, fake, fake, 0, fake, 0, null) == B.ESTRIDE
+    assert NA(xa, 4096, 256, 1, 8192, 4096, qa, ea, 8, ya, 0, null) == B.EWORKSPACE
+    assert B.bsfp8_workspace_bytes(256, 1, 8192, 4096, 8) > B.NO_ALLOC_SCRATCH_BYTES
+    assert NA(xa, 8192, 6, 2, 1024, 4096, qa, ea, 0, ctypes.c_void_p((1 << 32) + 4096), 0, null) == B.EINVAL
+    hdr = open(os.path.join(ROOT, "include", "bsfp8.h")).read()
+    m = re.search(r"#define BSFP8_NO_ALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NO_ALLOC_SCRATCH_BYTES
     bad = ctypes.c_int64(0)
     assert lib.bsfp8_make_twin(null, 1, 33, 32, null, null, null, ctypes.byref(bad), null) == B.ESHAPE
     assert lib.bsfp8_pad_k_weight(null, null, 1, 32, 64, 48, null, null, null) == B.ESHAPE
