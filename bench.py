@@ -520,7 +520,8 @@ def run(args):
 
     # step graphs
     timed, meta = [], []
-    keep = []                                       # buffers the graphs address
+    keep = []                                       # buffers the graphs address (a graph does not keep
+                                                    # them alive, and every capture empties the cache)
     for (label, name, M, split_k) in configs:
         G, N, K, _ = shape_of(name)
         ws_set = sets[WEIGHT_SET[name]]
@@ -536,7 +537,7 @@ def run(args):
         reps = args.steps if (label, name, M, split_k) == headline else args.reps
         timed.append(Timed((label, name, M, split_k), g, C, reps))
         meta.append((label, name, M, split_k, plan, ws_set))
-        keep.append((x, out))
+        keep.append((x, out, fn))                   # fn holds the workspace the graph writes
     # plain-read floors and a bare launch over each weight set's copies
     floors = {}
     sink = torch.empty(FLOOR_WGS, dtype=torch.int32, device="cuda")
