@@ -459,6 +459,115 @@ gemm_direct_kernel(KParams p) {
     if (live[i]) store_out(p, off[i], v[i]);
 }
 
+// Epilogue of the register kernels (rows_kernel, rows_dma_kernel): the NWK waves along K each hold
+// a partial of the whole BM x NB tile. They meet in LDS (`red`, WS f32x4 slots per wave, which
+// alias each wave's own staging area, so no barrier is needed before the writes) and are added in
+// ascending wave order; the tile then goes out as bf16/fp32, as MXFP8 codes, or into the
+// pairwise-exchange tree of the splits.
+template <int MT, int NT, int NWK, int WS>
+__device__ __forceinline__ void rows_epilogue(KParams& p, f32x4_t (&acc)[MT][NT], f32x4_t* red, int wk, int lane,
+                                              int m0, int n0, int g, int s) {
+  constexpr int TILES = MT * NT;
+  constexpr int TPW = (TILES + NWK - 1) / NWK;      // tiles summed and stored per wave
+  static_assert(TILES * WAVE <= WS, "a wave's partial tiles fit in its area");
+  const int q4 = lane >> 4, r16 = lane & 15;
+  const int M = p.M, N = p.N, G = p.G;
+  // Sum the NWK partial tiles in ascending wave order; wave w finishes tiles w, w + NWK, ...
+  f32x4_t v4[TPW];
+  int tix[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    tix[i] = NWK > 1 ? wk + i * NWK : i;
+    v4[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  if constexpr (NWK > 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ts = 0; ts < NT; ++ts) red[wk * WS + (mt * NT + ts) * WAVE + lane] = acc[mt][ts];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      if (tix[i] < TILES) {
+        f32x4_t a = red[tix[i] * WAVE + lane];
+#pragma unroll
+        for (int w = 1; w < NWK; ++w) a += red[w * WS + tix[i] * WAVE + lane];
+        v4[i] = a;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) v4[i] = acc[i / NT][i % NT];
+  }
+
+  // MXFP8 output (one split): wave w finishes the 32-column blocks of strips w, w + NWK, ...,
+  // adding each tile's wave partials in the same ascending order as above, and quantises them
+  if (p.yq) {
+    if constexpr (NT % 2 == 0) {
+      constexpr int NBLK = NT / 2;
+      for (int j = wk; j < MT * NBLK; j += NWK) {
+        const int mt = j / NBLK, bk = j % NBLK;
+        f32x4_t half[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int tt = mt * NT + 2 * bk + h;
+          if constexpr (NWK > 1) {
+            f32x4_t v = red[tt * WAVE + lane];
+#pragma unroll
+            for (int w = 1; w < NWK; ++w) v += red[w * WS + tt * WAVE + lane];
+            half[h] = v;
+          } else {
+            half[h] = acc[mt][2 * bk + h];
+          }
+        }
+        uint32_t c_lo, c_hi;
+        const uint8_t sb = mx_block_codes(half[0], half[1], c_lo, c_hi);
+        const int m = m0 + mt * 16 + r16;
+        if (m < M) store_mx_block(p.yq, p.ys, m, g, G, N, n0 + 32 * bk, q4, c_lo, c_hi, sb);
+      }
+    }
+    return;
+  }
+
+  if (p.splits == 1) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int mt = tix[i] / NT, ts = tix[i] % NT;
+      const int m = m0 + mt * 16 + r16;
+      if (tix[i] < TILES && m < M) {
+        const size_t o = ((size_t)m * G + g) * N + n0 + ts * 16 + q4 * 4;
+        const f32x4_t v = v4[i];
+        if (p.out_f32) {
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + o) = v;
+        } else {
+          const uint2 w2 = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + o) = w2;
+        }
+      }
+    }
+    return;
+  }
+  constexpr int NV = TPW * 4;
+  float v[NV];
+  size_t off[NV];
+  bool live[NV];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int mt = tix[i] / NT, ts = tix[i] % NT;
+    const int m = m0 + mt * 16 + r16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[i * 4 + r] = v4[i][r];
+      off[i * 4 + r] = ((size_t)m * G + g) * N + n0 + ts * 16 + q4 * 4 + r;
+      live[i * 4 + r] = tix[i] < TILES && m < M;
+    }
+  }
+  combine_splits<NV>(p, s, v, off, live);
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (live[i]) store_out(p, off[i], v[i]);
+}
+
 // Register kernel for mid row counts: BM = 16*MT rows of X and NB = 16*NT weight rows per
 // workgroup, NWK waves along K, one pass over the workgroup's K range. The waves of a workgroup
 // share nothing (each owns the chunks wk, wk + NWK, ...), so there is no LDS limit on the tile's
@@ -482,12 +591,9 @@ gemm_rows_kernel(KParams p) {
   constexpr int PCH = NWK * CW;                     // chunks of the workgroup
   constexpr int EROWS = NB >= 32 ? NB / 32 : 1;
   constexpr int ECOLS = PCH * 4;
-  constexpr int TILES = MT * NT;
-  constexpr int TPW = (TILES + NWK - 1) / NWK;      // tiles summed and stored per wave
   constexpr int XG = MT * 256;                      // 16-byte granules of one wave's X chunk
   static_assert(EROWS * ECOLS <= NTHR, "one exponent byte per thread");
   static_assert(D >= 1 && D <= CW, "ring depth");
-  static_assert(TILES * WAVE <= XG, "a wave's partial tiles fit in its X area");
   __shared__ uint8_t e_lds[EROWS * ECOLS];
   __shared__ uint4 xs[NWK * XG];
   __shared__ uint4 wsm[NWK * NT * 128];            // each wave's weight chunk, 16 rows x 8 granules per tile
@@ -501,7 +607,7 @@ gemm_rows_kernel(KParams p) {
   const Tile tl = tile_of(p);
   const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
 
-  const int K = p.K, M = p.M, N = p.N, G = p.G;
+  const int K = p.K, M = p.M, N = p.N;
   const int n0 = nb * NB, m0 = mb * BM;
   const int c_begin = s * p.cps;
   const int c_end = min(c_begin + p.cps, p.kchunks);
@@ -642,102 +748,167 @@ gemm_rows_kernel(KParams p) {
     }
   }
 
-  // Sum the NWK partial tiles in ascending wave order; wave w finishes tiles w, w + NWK, ...
-  f32x4_t v4[TPW];
-  int tix[TPW];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    tix[i] = NWK > 1 ? wk + i * NWK : i;
-    v4[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  rows_epilogue<MT, NT, NWK, XG>(p, acc, reinterpret_cast<f32x4_t*>(xs), wk, lane, m0, n0, g, s);
+}
+
+// Register kernel with LDS-mode staging: the tiles, waves, chunk order, MFMA order and epilogue of
+// gemm_rows_kernel (so the two give bitwise the same results for the same MT, NT, NWK and CW),
+// but each wave streams its chunks straight from memory into a private ring of D LDS buffers with
+// the buffer loads' LDS mode instead of passing them through VGPRs and LDS stores:
+//  * an X chunk (BM rows x 256 bytes) is BM/4 wave loads of four 256-byte row pieces, sixteen
+//    lanes per row, each lane fetching the granule that belongs in its slot (granule g of row r at
+//    slot g ^ (r % 16)); a weight chunk (NB rows x 128 bytes) is NB/8 wave loads of eight 128-byte
+//    row pieces (granule g of row R at slot g ^ (R/2 % 8)). Both layouts are the ones the rows
+//    kernel writes, so the fragment reads are the same and conflict-free;
+//  * a wave only ever reads its own buffers, so it needs no barrier: it waits for its own loads
+//    (every chunk issues the same PC loads, chunks past the split's range at out-of-range
+//    offsets, so the counts stay exact) and refills a buffer once its reads of it are done;
+//  * chunks past the range are not computed (the accumulators start at +0 and can never hold -0,
+//    so adding their zero products would change nothing).
+// K must be whole 128-wide chunks.
+template <int MT, int NT, int NWK, int CW, int D>
+__global__ void __launch_bounds__(WAVE * NWK)
+gemm_rows_dma_kernel(KParams p) {
+  constexpr int BM = 16 * MT;
+  constexpr int NB = 16 * NT;
+  constexpr int PCH = NWK * CW;                     // chunks of the workgroup
+  constexpr int EROWS = NB >= 32 ? NB / 32 : 1;
+  constexpr int ECOLS = PCH * 4;
+  constexpr int XGR = BM * 16;                      // 16-byte granules of an X chunk
+  constexpr int BUF = XGR + NB * 8;                 // ... of a chunk buffer (X, then weights)
+  constexpr int WS = D * BUF;                       // ... of a wave's ring
+  constexpr int PCX = BM / 4, PCW = NB / 8;
+  constexpr int PC = PCX + PCW;                     // loads per chunk
+  static_assert(EROWS * PCH <= WAVE, "one exponent word (a chunk of a block row) per lane of wave 0");
+  static_assert(D >= 1 && D <= CW && D * PC <= 63, "ring depth, counter range");
+  __shared__ uint32_t e_words[WAVE];                // every lane of the load writes its word
+  const uint8_t* const e_lds = reinterpret_cast<const uint8_t*>(e_words);
+  __shared__ uint4 ring[NWK * WS];
+
+  prefetch_args(p);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wk = tid >> 6;
+  const int q4 = lane >> 4, r16 = lane & 15;
+
+  const Tile tl = tile_of(p);
+  const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
+
+  const int K = p.K, M = p.M, N = p.N;
+  const int n0 = nb * NB, m0 = mb * BM;
+  const int c_begin = s * p.cps;
+  const int c_end = min(c_begin + p.cps, p.kchunks);
+  const int KB = K / 32;
+
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, (int)p.x_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.q, 0, (int)p.q_bytes, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((void*)p.e, 0, (int)p.e_bytes, RSRC_WORD3);
+
+  // exponent words (one 4-byte word = the four K blocks of a chunk), EROWS block rows x the
+  // workgroup's chunks, straight into LDS by wave 0 before its chunk loads (K is whole chunks, so
+  // every word is aligned)
+  if (wk == 0) {
+    const int er = lane / PCH, cl = lane % PCH;
+    const bool ok = lane < EROWS * PCH && c_begin + cl < c_end;
+    const uint32_t off = (uint32_t)((g * (N / 32) + n0 / 32 + er) * KB + (c_begin + cl) * 4);
+    lds_load4(re, lds_addr(e_words), ok ? off : OOB);
   }
-  if constexpr (NWK > 1) {
-    f32x4_t* red = reinterpret_cast<f32x4_t*>(xs);  // wave w, tile tt: red[w*XG + tt*WAVE + lane]
+
+  // This lane's share of a chunk's loads (the chunk index only adds c*128 to the offsets).
+  //  X load i: rows 4i .. 4i+3; the lane fills row 4i + q4, slot r16 with granule r16 ^ (row % 16).
+  uint32_t xoff[PCX];
+  bool xok[PCX];
+#pragma unroll
+  for (int i = 0; i < PCX; ++i) {
+    const int row = 4 * i + q4;
+    const int m = m0 + row;
+    xok[i] = m < M;
+    xoff[i] = xok[i] ? (uint32_t)(((int64_t)m * p.ldx + (int64_t)g * K + (r16 ^ (row & 15)) * 8) * 2) : 0u;
+  }
+  //  weight load i: rows 8i .. 8i+7; the lane fills row R = 8i + lane/8, slot lane%8 with granule
+  //  (lane%8) ^ (R/2 % 8).
+  uint32_t woff[PCW];
+#pragma unroll
+  for (int i = 0; i < PCW; ++i) {
+    const int R = 8 * i + (lane >> 3);
+    woff[i] = (uint32_t)(g * N + n0 + R) * (uint32_t)K + 16 * ((lane & 7) ^ ((R >> 1) & 7));
+  }
+  uint4* const area = ring + wk * WS;
+  // chunk j of this wave is chunk c = c_begin + wk + j*NWK, into buffer j % D
+  auto issue = [&](int j) {
+    const int c = c_begin + wk + j * NWK;
+    const bool cok = c < c_end;
+    uint4* const b = area + (j % D) * BUF;
+#pragma unroll
+    for (int i = 0; i < PCX; ++i)
+      lds_load16(rx, lds_addr(b + 64 * i), cok && xok[i] ? xoff[i] + (uint32_t)(c * KCH * 2) : OOB);
+#pragma unroll
+    for (int i = 0; i < PCW; ++i)
+      lds_load16_stream(rq, lds_addr(b + XGR + 64 * i), cok ? woff[i] + (uint32_t)(c * KCH) : OOB);
+  };
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) acc[mt][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int wsw = (r16 >> 1) & 7;
+  auto compute = [&](int j) {
+    const int cl = wk + j * NWK;                    // chunk index inside the workgroup
+    const uint4* const b = area + (j % D) * BUF;
+    // lane (r16, q4) takes the k values 64h + 16*q4 + 8u + [0, 8) of row r16 for MFMA 2h + u
+    bf16x8_t xf[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ts = 0; ts < NT; ++ts) red[wk * XG + (mt * NT + ts) * WAVE + lane] = acc[mt][ts];
-    __syncthreads();
+      for (int f = 0; f < 4; ++f) {
+        const int gr = 8 * (f >> 1) + 2 * q4 + (f & 1);
+        xf[mt][f] = __builtin_bit_cast(bf16x8_t, b[(mt * 16 + r16) * 16 + (gr ^ r16)]);
+      }
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      if (tix[i] < TILES) {
-        f32x4_t a = red[tix[i] * WAVE + lane];
+    for (int ts = 0; ts < NT; ++ts) {
+      const int er = (n0 + ts * 16 + r16) / 32 - n0 / 32;
+      const float sc0 = block_scale(e_lds[er * ECOLS + cl * 4 + (q4 >> 1)]);
+      const float sc1 = block_scale(e_lds[er * ECOLS + cl * 4 + 2 + (q4 >> 1)]);
+      const uint4 wa = b[XGR + (ts * 16 + r16) * 8 + (q4 ^ wsw)];
+      const uint4 wb = b[XGR + (ts * 16 + r16) * 8 + ((4 + q4) ^ wsw)];
+      const bf16x8_t w0 = dequant8(wa.x, wa.y, sc0);
+      const bf16x8_t w1 = dequant8(wa.z, wa.w, sc0);
+      const bf16x8_t w2 = dequant8(wb.x, wb.y, sc1);
+      const bf16x8_t w3 = dequant8(wb.z, wb.w, sc1);
 #pragma unroll
-        for (int w = 1; w < NWK; ++w) a += red[w * XG + tix[i] * WAVE + lane];
-        v4[i] = a;
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4_t c = acc[mt][ts];
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, xf[mt][0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, xf[mt][1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2, xf[mt][2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w3, xf[mt][3], c, 0, 0, 0);
+        acc[mt][ts] = c;
       }
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) v4[i] = acc[i / NT][i % NT];
-  }
+  };
 
-  // MXFP8 output (one split): wave w finishes the 32-column blocks of strips w, w + NWK, ...,
-  // adding each tile's wave partials in the same ascending order as above, and quantises them
-  if (p.yq) {
-    if constexpr (NT % 2 == 0) {
-      constexpr int NBLK = NT / 2;
-      for (int j = wk; j < MT * NBLK; j += NWK) {
-        const int mt = j / NBLK, bk = j % NBLK;
-        f32x4_t half[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int tt = mt * NT + 2 * bk + h;
-          if constexpr (NWK > 1) {
-            const f32x4_t* red = reinterpret_cast<const f32x4_t*>(xs);
-            f32x4_t v = red[tt * WAVE + lane];
+  for (int j = 0; j < D; ++j) issue(j);
+  pin_epilogue_args(p);                             // the first loads are issued
+  if (wk == 0) wait_vmcnt_le<D * PC>();             // wave 0's exponent words are in
+  __syncthreads();
 #pragma unroll
-            for (int w = 1; w < NWK; ++w) v += red[w * XG + tt * WAVE + lane];
-            half[h] = v;
-          } else {
-            half[h] = acc[mt][2 * bk + h];
-          }
-        }
-        uint32_t c_lo, c_hi;
-        const uint8_t sb = mx_block_codes(half[0], half[1], c_lo, c_hi);
-        const int m = m0 + mt * 16 + r16;
-        if (m < M) store_mx_block(p.yq, p.ys, m, g, G, N, n0 + 32 * bk, q4, c_lo, c_hi, sb);
-      }
+  for (int j = 0; j < CW; ++j) {
+    // this wave's loads of chunk j (those of the later chunks in flight may still be outstanding)
+    if (j + D - 1 < CW) {
+      wait_vmcnt_le<(D - 1) * PC>();
+    } else {
+      wait_vmcnt_le<0>();
     }
-    return;
-  }
-
-  if (p.splits == 1) {
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int mt = tix[i] / NT, ts = tix[i] % NT;
-      const int m = m0 + mt * 16 + r16;
-      if (tix[i] < TILES && m < M) {
-        const size_t o = ((size_t)m * G + g) * N + n0 + ts * 16 + q4 * 4;
-        const f32x4_t v = v4[i];
-        if (p.out_f32) {
-          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.y) + o) = v;
-        } else {
-          const uint2 w2 = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + o) = w2;
-        }
-      }
-    }
-    return;
-  }
-  constexpr int NV = TPW * 4;
-  float v[NV];
-  size_t off[NV];
-  bool live[NV];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int mt = tix[i] / NT, ts = tix[i] % NT;
-    const int m = m0 + mt * 16 + r16;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      v[i * 4 + r] = v4[i][r];
-      off[i * 4 + r] = ((size_t)m * G + g) * N + n0 + ts * 16 + q4 * 4 + r;
-      live[i * 4 + r] = tix[i] < TILES && m < M;
+    if (c_begin + wk + j * NWK < c_end) compute(j);
+    if (j + D < CW) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's reads of the buffer are done
+      issue(j + D);
     }
   }
-  combine_splits<NV>(p, s, v, off, live);
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if (live[i]) store_out(p, off[i], v[i]);
+  wait_vmcnt_le<0>();                               // no load may still be writing LDS
+  rows_epilogue<MT, NT, NWK, WS>(p, acc, reinterpret_cast<f32x4_t*>(ring), wk, lane, m0, n0, g, s);
 }
 
 // Tile kernel for many rows or wide weights: a BM x NB output tile per workgroup, BM = 16*MT*NWM
@@ -1691,7 +1862,7 @@ reduce_splits_kernel(const float* __restrict__ part, void* __restrict__ y, int64
 // ---------------------------------------------------------------------------------------------
 typedef void (*KernelFn)(KParams);
 
-enum Kind { STAGED = 0, DIRECT = 1, ROWS = 2, TILE = 3, DECODE = 4, SLAB = 5, PAIR = 6, PAIR_FULL = 7 };
+enum Kind { STAGED = 0, DIRECT = 1, ROWS = 2, TILE = 3, DECODE = 4, SLAB = 5, PAIR = 6, PAIR_FULL = 7, ROWS_DMA = 8 };
 
 struct Config {
   int MT, NT, NWM, NWN, NWK, CW;         // TILE: CW = chunks in flight; SLAB: CW = ring stages;
@@ -1712,6 +1883,7 @@ struct Config {
 #define SCFG(MT, NT, NWM, NWN, NWK, S) {MT, NT, NWM, NWN, NWK, S, gemm_slab_kernel<MT, NT, NWM, NWN, NWK, S>, SLAB}
 #define PCFG(NWK, CP, RG) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, RG>, PAIR, 0, 8, RG}
 #define PFCFG(NWK, CP) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, false, true>, PAIR_FULL, 0, 8, 0}
+#define RDCFG(MT, NT, NWK, CW, D) {MT, NT, 1, 1, NWK, CW, gemm_rows_dma_kernel<MT, NT, NWK, CW, D>, ROWS_DMA}
 
 const Config kConfigs[] = {
     CFG(1, 1, 4, 1, 4),   // 0  small: 64 rows, one wave per 16 rows, 4 chunks per wave
@@ -1814,6 +1986,14 @@ const Config kConfigs[] = {
     PFCFG(8, 2),              // 93 pair, whole range: 8 waves x 4 chunks (K = 4096)
     PFCFG(4, 4),              // 94 pair, whole range: 4 waves x 8 chunks (K = 4096)
     PFCFG(3, 1),              // 95 pair, whole range: 3 waves x 2 chunks (K = 768)
+    // register kernels with LDS-mode staging (bitwise the same sums as the ROWS entries alike)
+    RDCFG(3, 2, 4, 8, 2),     // 96 rows, LDS-mode: 48 x 32 tile, 4 waves along K x 8 chunks, 2 in flight
+    RDCFG(2, 2, 4, 8, 2),     // 97 rows, LDS-mode: 32 x 32 tile
+    RDCFG(2, 2, 4, 8, 3),     // 98 rows, LDS-mode: 32 x 32 tile, 3 in flight
+    RDCFG(3, 2, 8, 4, 1),     // 99 rows, LDS-mode: 48 x 32 tile, 8 waves along K x 4 chunks, 1 in flight
+    RDCFG(2, 2, 8, 4, 1),     // 100 rows, LDS-mode: 32 x 32 tile, 8 waves along K
+    RDCFG(1, 2, 8, 4, 2),     // 101 rows, LDS-mode: 16 x 32 tile, 8 waves along K, 2 in flight
+    RDCFG(1, 2, 4, 8, 4),     // 102 rows, LDS-mode: 16 x 32 tile, 4 waves along K, 4 in flight
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1870,8 +2050,10 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   p.cps = cps < p.kchunks ? cps : p.kchunks;
   if (c.kind == PAIR_FULL && (p.kchunks != c.NWK * c.CW || p.cps != p.kchunks || s.K % KCH != 0))
     return BSFP8_EINVAL;                                        // exactly the workgroup's chunks
-  if ((c.kind == DIRECT || c.kind == ROWS || c.kind == DECODE || c.kind == PAIR) && p.cps > c.NWK * c.CW)
+  if ((c.kind == DIRECT || c.kind == ROWS || c.kind == ROWS_DMA || c.kind == DECODE || c.kind == PAIR) &&
+      p.cps > c.NWK * c.CW)
     return BSFP8_EINVAL;                                        // one pass
+  if (c.kind == ROWS_DMA && s.K % KCH != 0) return BSFP8_EINVAL;  // whole chunks
   if ((c.kind == DECODE || c.kind == PAIR) && !c.ragged && s.K % KCH != 0) return BSFP8_EINVAL;  // whole words
   if (c.kind == TILE && (p.cps > TILE_MAX_CPS || s.K % KCH != 0)) return BSFP8_EINVAL;
   // slab kernel: K in whole chunks, splits begin on slab boundaries, one exponent word per lane
@@ -1911,8 +2093,9 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
 //    bitwise the same Y.
 //  * Few rows (at most 32): the one-pass register kernel with X rows in LDS, one 16-row block of X
 //    per workgroup.
-//  * More rows: the register kernel with both operands in registers and 16-48 rows of X per
-//    workgroup (no split while the K range fits one pass of 32 chunks).
+//  * More rows: the register kernel with 16-48 rows of X per workgroup, its chunks streamed
+//    straight into LDS when K is whole chunks (no split while the K range fits one pass of 32
+//    chunks).
 int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool allow_pair) {
   const int kchunks = (s.K + KCH - 1) / KCH > 0 ? (s.K + KCH - 1) / KCH : 1;
   const bool n64 = (s.N % 64) == 0;
@@ -1951,10 +2134,18 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool al
       cps = 32;
     }
   } else {
-    // up to 64 rows with K in whole chunks: the slab kernel (16 x 32 tiles, X rows read a
-    // kilobyte at a time), one split. Otherwise the rows kernel: 16 x 32 tiles, 8 waves along K
-    // (M <= 64); 32 x 32 (<= 128), 48 x 32 (<= 192) and 64 x 32 tiles, 4 waves along K x 8 chunks
-    if (s.M <= 64 && s.K % KCH == 0 && kchunks <= TILE_MAX_CPS) {
+    // K in whole chunks, at most 32 of them, up to 192 rows: the register kernel with LDS-mode
+    // staging, 16 x 32 tiles with 8 waves along K x 4 chunks (M <= 64), 32 x 32 (<= 128) and
+    // 48 x 32 (<= 192) with 4 waves along K x 8 chunks (the last two bitwise equal to the rows
+    // kernel's 37 and 62). Up to 64 rows with a longer K: the slab kernel (16 x 32 tiles, X rows
+    // read a kilobyte at a time), one split. Otherwise the rows kernel: 16 x 32 tiles, 8 waves
+    // along K (M <= 64); 32 x 32 (<= 128), 48 x 32 (<= 192) and 64 x 32 tiles, 4 waves along K x 8
+    // chunks.
+    const bool whole = s.K % KCH == 0;
+    if (whole && kchunks <= 32 && s.M <= 192) {
+      cfg = s.M <= 64 ? 101 : s.M <= 128 ? 97 : 96;
+      cps = kchunks;
+    } else if (s.M <= 64 && whole && kchunks <= TILE_MAX_CPS) {
       cfg = 69;
       cps = kchunks;
     } else {
@@ -2006,6 +2197,7 @@ bool mx_fusable(const Config& c) {
   switch (c.kind) {
     case TILE:
     case ROWS:
+    case ROWS_DMA:
       return c.NT % 2 == 0;
     case SLAB: {
       const int BM = 16 * c.MT * c.NWM, XG = BM * 64, WGR = NB * 32;

@@ -97,7 +97,7 @@ def test_plan_is_valid_for_every_shape_class(lib):
                         assert (p["splits"] - 1) * p["cps"] < kch <= p["splits"] * p["cps"], (M, G, N, K, split_k, p)
                         assert p["mblocks"] * p["BM"] >= M and N % p["NB"] == 0
                         info = B.bsfp8_config_info(p["cfg"])
-                        if info["kind"] in (3, 5) or (info["kind"] == 4 and info["row_scales"]):
+                        if info["kind"] in (3, 5, 8) or (info["kind"] == 4 and info["row_scales"]):
                             assert K % 128 == 0     # the decode kernel takes a ragged last chunk
                         if info["kind"] == 5 and p["splits"] > 1:
                             assert p["cps"] % 4 == 0

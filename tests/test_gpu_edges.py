@@ -89,12 +89,12 @@ def test_extreme_exponent_bytes_every_kernel(kind):
     G, N = 2, 256
     for cfg in _kinds():
         info = B.bsfp8_config_info(cfg)
-        K = 768 if info["kind"] in (3, 4, 5, 6) and not _takes_ragged_k(cfg) else 800
+        K = 768 if info["kind"] in (3, 4, 5, 6, 8) and not _takes_ragged_k(cfg) else 800
         if info["kind"] == 7:                          # exactly the workgroup's chunks
             K = 128 * info["CW"] * info["NWK"]
         M = min(2 * info["BM"] - 3, 256)
         x, q, e, _ = _edge_inputs(9100 + cfg + (0 if kind == "tiny" else 500), M, G, N, K, kind)
-        cps = info["CW"] * info["NWK"] if info["kind"] in (1, 2, 4, 6, 7) else (K + 127) // 128
+        cps = info["CW"] * info["NWK"] if info["kind"] in (1, 2, 4, 6, 7, 8) else (K + 127) // 128
         print(f"{kind} cfg {cfg} {info} M {M} K {K} cps {cps}", flush=True)
         xt, qt, et = to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e)
         y = B.bsfp8_gemm_config(xt, qt, et, cfg, cps)

@@ -189,11 +189,14 @@ def test_fused_decode_equals_the_two_kernel_form(M, G, N, K):
 
 
 # plans whose own kernel quantises its output (one split, 32-column blocks per wave or per
-# workgroup): the slab kernel (33..64 rows), the rows kernel (65..256 rows) and the tile kernel
-# (wide weights); the explicit configuration call takes the two-kernel form of the same plan
-IN_KERNEL_CASES = [(33, 2, 1024, 4096, 5), (64, 1, 256, 2048, 5), (65, 2, 1024, 4096, 2), (128, 1, 512, 1024, 2),
-                   (200, 1, 256, 1152, 2), (256, 1, 64, 256, 2), (16, 1, 16384, 1024, 3), (64, 1, 16384, 512, 3),
-                   (100, 1, 16384, 256, 3)]
+# workgroup): the LDS-staged register kernel (33..192 rows, K of at most 32 whole chunks), the
+# slab kernel (33..64 rows, longer K), the rows kernel (ragged K, or more than 192 rows) and the
+# tile kernel (wide weights); the explicit configuration call takes the two-kernel form of the
+# same plan
+IN_KERNEL_CASES = [(33, 2, 1024, 4096, 8), (64, 1, 256, 2048, 8), (65, 2, 1024, 4096, 8), (128, 1, 512, 1024, 8),
+                   (160, 1, 256, 2048, 8), (33, 1, 256, 5120, 5), (64, 1, 256, 8192, 5), (65, 2, 1024, 4000, 2),
+                   (128, 1, 512, 1056, 2), (200, 1, 256, 1152, 2), (256, 1, 64, 256, 2), (16, 1, 16384, 1024, 3),
+                   (64, 1, 16384, 512, 3), (100, 1, 16384, 256, 3)]
 
 
 @pytest.mark.parametrize("M,G,N,K,kind", IN_KERNEL_CASES)

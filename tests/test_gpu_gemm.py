@@ -121,14 +121,14 @@ def test_ragged_k_decode_equals_the_register_kernel_and_the_padded_k(M, K):
 
 def test_every_kernel_configuration():
     """Each compiled configuration, with a few chunks-per-split values, on a shape with several
-    m-blocks (where the tile is smaller than M), a ragged K tail (the tile, slab and aligned
-    decode kernels take K in whole 128-wide chunks) and every N tile width."""
+    m-blocks (where the tile is smaller than M), a ragged K tail (the tile, slab, LDS-staged
+    register and aligned decode kernels take K in whole 128-wide chunks) and every N tile width."""
     G, N = 2, 256
     for cfg in range(B.bsfp8_num_configs()):
         info = B.bsfp8_config_info(cfg)
         if info["row_scales"]:              # these read [G][N][K/32] exponents: test_gpu_row32.py
             continue
-        K = 768 if info["kind"] in (3, 4, 5, 6) else 800
+        K = 768 if info["kind"] in (3, 4, 5, 6, 8) else 800
         if info["kind"] in (4, 6) and _takes_ragged_k(cfg):
             K = 800                         # a decode instance built for a ragged last chunk
         if info["kind"] == 7:               # exactly the workgroup's chunks, one split
@@ -136,7 +136,7 @@ def test_every_kernel_configuration():
         M = min(2 * info["BM"] - 3, 256)
         x, q, e = _inputs(400 + cfg, M, G, N, K)
         exact = oracle.gemm_exact_f64(x, G, N, K, q, e)
-        if info["kind"] in (1, 2, 4, 6):    # one pass: chunks per split <= CW * NWK
+        if info["kind"] in (1, 2, 4, 6, 8):  # one pass: chunks per split <= CW * NWK
             cps_list = sorted({1, 2, info["CW"] * info["NWK"]})
         elif info["kind"] == 7:
             cps_list = (K // 128,)
