@@ -148,6 +148,9 @@ BSFP8_API size_t bsfp8_workspace_bytes(int64_t M, int64_t G, int64_t N, int64_t 
  *             ldx >= G*K and ldx % 8 == 0.
  *   q, e    : twin codes [G][N][K] and exponent bytes [G][N/32][K/32] (device; q 16-byte, e 4-byte aligned);
  *             N and K multiples of 32. Exponent byte 255 and e4m3 NaN codes give NaN outputs.
+ *             The kernels read e in aligned 4-byte words: when its size is not a multiple of 4,
+ *             up to 3 bytes past its end are read (within the same word, hence the same page);
+ *             they never reach a result.
  *   split_k : number of workgroups that share one output tile's K range (fixed-order reduction);
  *             0 = the built-in table for this shape; otherwise 1..64.
  *   ws      : workspace of ws_bytes >= bsfp8_workspace_bytes(M,G,N,K,split_k) (may be NULL when
