@@ -13,8 +13,9 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless stated "host". bf16 values are passed as their 16-bit
- *     patterns (uint16_t). The caller owns every buffer; the library keeps no state between
- *     calls and allocates nothing in the per-call functions.
+ *     patterns (uint16_t). The caller owns every buffer; the library allocates nothing in the
+ *     per-call functions and keeps no state between calls, apart from the static scratch array
+ *     of bsfp8_gemm_no_alloc (and its address, looked up once per device).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Per-call functions
  *     only enqueue work: they never synchronise or allocate, so they can be captured in a HIP
  *     graph. The "prepare" functions are synchronous: they enqueue, wait for the stream and
