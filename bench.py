@@ -16,7 +16,8 @@ weight copies so that the cache is cold, captured graphs, interleaved rounds):
     rounds;
   * the plain-read floor of each weight set: the same graph with the GEMM replaced by a kernel
     that only reads the copy's bytes with the GEMM's load shape (bsfp8_read_floor), and a bare
-    launch (the same kernel reading nothing).
+    launch (the same kernel reading nothing); and per configuration the read + write floor, the
+    same reads followed by a write of that configuration's output bytes.
 
 Per call: us_per_call = step time / C (gaps between launches included, as a graph replays them).
 value = weight-stream GB/s = (e4m3 bytes + exponent bytes) / us_per_call. roofline.achieved =
@@ -330,7 +331,7 @@ def make_call(torch, B, ws_set, name, M, split_k, path, x, out):
                                    out_dtype=od)), plan
 
 
-def entry_for(label, name, M, split_k, path, plan, t, ws_set, floor_t, launch_t):
+def entry_for(label, name, M, split_k, path, plan, t, ws_set, floor_t, launch_t, floor_rw_t=None):
     G, N, K, erows = shape_of(name)
     w, e, x, y = algorithmic_bytes(name, M, path)
     us = t.us
@@ -355,6 +356,9 @@ def entry_for(label, name, M, split_k, path, plan, t, ws_set, floor_t, launch_t)
         ent["floor_us_per_call"] = round(floor_t.us, 3)
         ent["floor_frac"] = round(floor_t.us / us, 4)
         ent["launch_us_per_call"] = round(launch_t.us, 3)
+    if floor_rw_t is not None:
+        ent["floor_rw_us_per_call"] = round(floor_rw_t.us, 3)
+        ent["floor_rw_frac"] = round(floor_rw_t.us / us, 4)
     return ent
 
 
@@ -547,7 +551,21 @@ def run(args):
         gf = capture(torch, lambda i, s=ws_set: B.bsfp8_read_floor(s.bufs[i], nwg=FLOOR_WGS, sink=sink), C)
         gl = capture(torch, lambda i, s=ws_set: B.bsfp8_read_floor(s.bufs[i], nbytes=0, nwg=FLOOR_WGS, sink=sink), C)
         floors[ws_name] = (Timed(("floor", ws_name), gf, C, args.reps), Timed(("launch", ws_name), gl, C, args.reps))
-    every = timed + [t for pair in floors.values() for t in pair]
+    # read + write floors: the same reads, then a configuration's output bytes written (a kernel
+    # that stores pays for its writes and their completion at its end)
+    rw_floors = {}
+    for (label, name, M, split_k) in configs:
+        ws_name = WEIGHT_SET[name]
+        ob = (algorithmic_bytes(name, M, path)[3] + 15) // 16 * 16
+        if (ws_name, ob) in rw_floors:
+            continue
+        ws_set = sets[ws_name]
+        yb = torch.empty(ob, dtype=torch.uint8, device="cuda")
+        keep.append(yb)
+        g = capture(torch, lambda i, s=ws_set, yb=yb: B.bsfp8_read_floor(s.bufs[i], nwg=FLOOR_WGS, sink=sink, out=yb),
+                    len(ws_set))
+        rw_floors[(ws_name, ob)] = Timed(("floor_rw", ws_name, ob), g, len(ws_set), args.reps)
+    every = timed + [t for pair in floors.values() for t in pair] + list(rw_floors.values())
 
     # warm-up replays, then interleaved rounds
     for t in every:
@@ -563,7 +581,8 @@ def run(args):
     entries = []
     for t, (label, name, M, split_k, plan, ws_set) in zip(timed, meta):
         ft, lt = floors[WEIGHT_SET[name]]
-        entries.append(entry_for(label, name, M, split_k, path, plan, t, ws_set, ft, lt))
+        rwt = rw_floors[(WEIGHT_SET[name], (algorithmic_bytes(name, M, path)[3] + 15) // 16 * 16)]
+        entries.append(entry_for(label, name, M, split_k, path, plan, t, ws_set, ft, lt, rwt))
     floor_summary = {k: {"copy_bytes": sets[k].copy_bytes, "copies": len(sets[k]),
                          "read_us_per_call": round(f.us, 3), "read_gbs": round(sets[k].copy_bytes / (f.us * 1e3), 1),
                          "launch_us_per_call": round(l.us, 3), "workgroups": FLOOR_WGS}
@@ -610,6 +629,8 @@ def run(args):
         "pct_hbm_peak": round(100 * head["weight_stream_gbs"] / HBM_PEAK_GBS, 1),
         "floor_us_per_call": head.get("floor_us_per_call"),
         "floor_frac": head.get("floor_frac"),
+        "floor_rw_us_per_call": head.get("floor_rw_us_per_call"),
+        "floor_rw_frac": head.get("floor_rw_frac"),
         "roofline": dict(head["roofline"], traffic=traffic_from_profile(name, M) if path == "bf16" else None,
                          algorithmic_bytes_per_launch=head["algorithmic_bytes"]),
         "baseline_ref": "pages (GB10, other hardware): twin path 2.20 ms / 43 layers = 51.2 us/call at M=6",

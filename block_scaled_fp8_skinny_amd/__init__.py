@@ -39,7 +39,7 @@ _SIGS = {
     "bsfp8_gemm": (_I, _GEMM_ARGS),
     "bsfp8_gemm_no_alloc": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _P, _I, _P]),
     "bsfp8_num_configs": (_I, []),
-    "bsfp8_read_floor": (_I, [_P, _SZ, _I, _P, _P]),
+    "bsfp8_read_floor": (_I, [_P, _SZ, _I, _P, _P, _SZ, _P]),
     "bsfp8_config_info": (_I, [_I, ctypes.POINTER(_I)]),
     "bsfp8_plan_info": (_I, [_I64, _I64, _I64, _I64, _I, _I, ctypes.POINTER(_I)]),
     "bsfp8_workspace_bytes_config": (_SZ, [_I64, _I64, _I64, _I64, _I, _I]),
@@ -337,10 +337,12 @@ def bsfp8_num_configs():
     return int(lib().bsfp8_num_configs())
 
 
-def bsfp8_read_floor(t, nbytes=None, nwg=256, sink=None):
+def bsfp8_read_floor(t, nbytes=None, nwg=256, sink=None, out=None):
     """Plain-read floor: one kernel that reads the first nbytes (default: all) of the GPU tensor t
     once with the GEMM's load shape and computes nothing else (a measurement aid; nbytes = 0 is a
-    bare launch). sink: uint32 [nwg] on t's device (allocated when None). Returns the sink."""
+    bare launch). sink: uint32 [nwg] on t's device (allocated when None). out: a contiguous GPU
+    tensor of a multiple of 16 bytes that the kernel also writes whole (the read + write floor of
+    a GEMM storing that many output bytes), or None. Returns the sink."""
     nb = t.numel() * t.element_size() if nbytes is None else int(nbytes)
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError("t must be a contiguous GPU tensor")
@@ -349,7 +351,12 @@ def bsfp8_read_floor(t, nbytes=None, nwg=256, sink=None):
     if sink is None:
         sink = torch.empty(nwg, dtype=torch.int32, device=t.device)
     _need(sink, torch.int32, "sink", numel=nwg, device=t.device)
-    _check(lib().bsfp8_read_floor(_ptr(t), nb, nwg, _ptr(sink), _stream(t)), "bsfp8_read_floor")
+    ob = 0
+    if out is not None:
+        if not out.is_cuda or not out.is_contiguous() or out.device != t.device:
+            raise ValueError("out must be a contiguous GPU tensor on t's device")
+        ob = out.numel() * out.element_size()
+    _check(lib().bsfp8_read_floor(_ptr(t), nb, nwg, _ptr(sink), _ptr(out), ob, _stream(t)), "bsfp8_read_floor")
     return sink
 
 

@@ -90,14 +90,20 @@ BSFP8_API int bsfp8_gemm_mx_config(const uint8_t* xq, const uint8_t* xs, int64_t
  * in the same graph replay as a GEMM (the measurement protocol of page
  * "recipes/docker-images/mia-tp4/adapter/shared_pad_k.py", MEASUREMENT: distinct weight copies so
  * that the cache is cold, captured graphs, interleaved rounds), it gives the floor a GEMM that
- * streams those bytes can reach on this machine; bytes = 0 times a bare launch.
+ * streams those bytes can reach on this machine; bytes = 0 times a bare launch. With out_bytes > 0
+ * each workgroup then also writes its contiguous share of `out` (16 bytes per lane): the floor of
+ * a GEMM that reads those bytes and stores that many output bytes.
  *   p    : device memory, 16-byte aligned, at least `bytes` long (may be NULL when bytes = 0);
  *          bytes < 2^31.
  *   sink : device uint32_t [nwg]; written only when a workgroup's fold of the data equals a fixed
  *          constant (it keeps the loads alive), so its contents are meaningless.
- * Returns BSFP8_EINVAL (nwg outside 1..65536, no sink), BSFP8_ESTRIDE (misaligned p),
- * BSFP8_ESHAPE (bytes too large), BSFP8_EHIP on a launch failure. */
-BSFP8_API int bsfp8_read_floor(const void* p, size_t bytes, int nwg, uint32_t* sink, void* stream);
+ *   out  : device memory, 16-byte aligned, out_bytes long (NULL when out_bytes = 0); out_bytes a
+ *          multiple of 16 below 2^31; receives the workgroups' folds (meaningless contents).
+ * Returns BSFP8_EINVAL (nwg outside 1..65536, no sink, out missing, out or sink overlapping p),
+ * BSFP8_ESTRIDE (misaligned p or out, out_bytes not a multiple of 16), BSFP8_ESHAPE (bytes or
+ * out_bytes too large), BSFP8_EHIP on a launch failure. */
+BSFP8_API int bsfp8_read_floor(const void* p, size_t bytes, int nwg, uint32_t* sink, void* out, size_t out_bytes,
+                               void* stream);
 
 #ifdef __cplusplus
 }

@@ -150,6 +150,17 @@ def test_argument_checks_return_before_gpu_work(lib):
     hdr = open(os.path.join(ROOT, "include", "bsfp8.h")).read()
     m = re.search(r"#define BSFP8_NO_ALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
     assert m and int(m.group(1)) << int(m.group(2)) == B.NO_ALLOC_SCRATCH_BYTES
+    # the floor kernel's checks: a sink, an output buffer when output bytes are asked for, 16-byte
+    # alignment and a multiple of 16 bytes, and no overlap with what it reads
+    F = lib.bsfp8_read_floor
+    assert F(xa, 1024, 0, ya, null, 0, null) == B.EINVAL
+    assert F(xa, 1024, 4, null, null, 0, null) == B.EINVAL
+    assert F(xa, 1024, 4, ya, null, 64, null) == B.EINVAL
+    assert F(ctypes.c_void_p((1 << 32) + 8), 1024, 4, ya, null, 0, null) == B.ESTRIDE
+    assert F(xa, 1024, 4, ya, ctypes.c_void_p((4 << 32) + 4096 + 8), 64, null) == B.ESTRIDE
+    assert F(xa, 1024, 4, ya, ctypes.c_void_p((4 << 32) + 4096), 40, null) == B.ESTRIDE
+    assert F(xa, 1 << 31, 4, ya, null, 0, null) == B.ESHAPE
+    assert F(xa, 1024, 4, ya, ctypes.c_void_p((1 << 32) + 512), 64, null) == B.EINVAL
     bad = ctypes.c_int64(0)
     assert lib.bsfp8_make_twin(null, 1, 33, 32, null, null, null, ctypes.byref(bad), null) == B.ESHAPE
     assert lib.bsfp8_pad_k_weight(null, null, 1, 32, 64, 48, null, null, null) == B.ESHAPE
