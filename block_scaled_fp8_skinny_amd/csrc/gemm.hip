@@ -1994,6 +1994,7 @@ const Config kConfigs[] = {
     RDCFG(2, 2, 8, 4, 1),     // 100 rows, LDS-mode: 32 x 32 tile, 8 waves along K
     RDCFG(1, 2, 8, 4, 2),     // 101 rows, LDS-mode: 16 x 32 tile, 8 waves along K, 2 in flight
     RDCFG(1, 2, 4, 8, 4),     // 102 rows, LDS-mode: 16 x 32 tile, 4 waves along K, 4 in flight
+    TCFG(2, 2, 4, 4, 3, 1),   // 103 tile: 128 x 128, 16 waves of 32 x 32, 3 stages
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2082,7 +2083,8 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
 // the fp32 chain of every output stays the same, so K and K zero-padded inside the same chunk
 // count give the same sums.
 //  * Wide weights (at least 1024 tiles of 16 rows, e.g. an LM-head vocabulary shard): the tile
-//    kernel, one split, for every row count. Each output's fp32 sum is then the same ascending
+//    kernel, one split, for every row count (16 x 128 tiles up to 16 rows, 64 x 128 up to 64, then
+//    128 x 128 on 16 waves, four per SIMD, which hide each other's fragment reads better than 8). Each output's fp32 sum is then the same ascending
 //    chain of chunks and MFMAs whatever the tile, so a row's result does not depend on how many
 //    rows share the call.
 //  * Decode rows (at most 8) over exactly 32 chunks on at most 256 eight-row tiles (wo_a at G = 2):
@@ -2104,7 +2106,7 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool al
   int cfg, cps;
   if (tiles16 >= 1024) {
     cps = kchunks;
-    if (tile_ok) cfg = s.M <= 16 ? 51 : s.M <= 64 ? 53 : 43;
+    if (tile_ok) cfg = s.M <= 16 ? 51 : s.M <= 64 ? 53 : 103;
     else if (path == PATH_SMALL || s.M <= 16) cfg = n64 ? 0 : 3;
     else if (s.M <= 32) cfg = n64 ? 9 : 15;
     else cfg = n64 ? 10 : 16;
