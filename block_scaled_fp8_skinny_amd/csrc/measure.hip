@@ -3,9 +3,10 @@
 // The GEMM's cost at decode row counts is the time to stream its weight bytes from HBM plus a
 // fixed launch and first-byte latency. This kernel does only the first part of that work: it
 // reads `bytes` of a buffer once, with the GEMM's load shape (16 bytes per lane, one contiguous
-// kilobyte per wave load, non-temporal, several loads in flight per wave), and folds what it read
-// into one word per lane, which it stores only if it matches a constant no realistic data hits
-// (the store keeps the loads alive; the sink is written at most once per workgroup in practice).
+// kilobyte per wave load, non-temporal, every load of a workgroup's share in flight at once, up to
+// twelve per wave), and folds what it read into one word per lane, which it stores only if it
+// matches a constant no realistic data hits (the store keeps every lane's loads alive; the sink is
+// written at most once per workgroup in practice).
 // Timed on the same distinct weight copies as the GEMM, it is the floor a GEMM of that size can
 // approach on this machine; with bytes = 0 it is the cost of a launch. With an output buffer it
 // also writes `out_bytes` there (16 bytes per lane, each workgroup one contiguous share, after
@@ -17,27 +18,38 @@ namespace bsfp8 {
 namespace {
 
 constexpr int FLOOR_WAVES = 8;
-constexpr int FLOOR_INFLIGHT = 8;                   // loads in flight per wave per step
+constexpr int FLOOR_MAX_L = 12;                     // loads per wave per step, at most
 constexpr uint32_t FLOOR_MAGIC = 0x9E3779B9u;
 
+// L loads per wave per step: a workgroup's share is walked in steps of L * 8 KB, each wave's load u
+// of a step at kilobyte u * 8 + wave, every load of a step issued before any is used. The launch
+// picks the smallest L that covers a share in one step (every decode size), else L = 12 and several
+// steps. Loads past the share (the last step's tail) read at the out-of-range offset.
+template <int L>
 __global__ void __launch_bounds__(WAVE * FLOOR_WAVES)
-read_floor_kernel(const uint8_t* p, uint32_t bytes, uint32_t per_wg, uint32_t* sink, uint4* out, uint32_t out16,
-                  uint32_t out_per_wg16) {
+read_floor_kernel(const uint8_t* p, uint32_t bytes, uint32_t per_wg, uint32_t steps, uint32_t* sink, uint4* out,
+                  uint32_t out16, uint32_t out_per_wg16) {
+  // every argument the loads need, fetched in one batch (left to itself the compiler fetched the
+  // buffer pointer only after a bounds test: a second dependent round trip), and the ones the end
+  // needs held in registers rather than fetched after the reads
+  asm volatile("" ::"s"(p), "s"(bytes), "s"(per_wg), "s"(steps));
+  asm volatile("" : "+s"(sink), "+s"(out), "+s"(out16), "+s"(out_per_wg16));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, (int)bytes, RSRC_WORD3);
   const uint32_t begin = blockIdx.x * per_wg;
   const uint32_t end = min(begin + per_wg, bytes);
+  const uint32_t first = begin + (uint32_t)wave * 1024u + (uint32_t)lane * 16u;
   uint32_t acc = 0;
-  for (uint32_t base = begin + (uint32_t)wave * 1024u; base < end;
-       base += (uint32_t)(FLOOR_WAVES * FLOOR_INFLIGHT) * 1024u) {
-    uint4 v[FLOOR_INFLIGHT];
+  for (uint32_t st = 0; st < steps; ++st) {
+    uint4 v[L];
 #pragma unroll
-    for (int u = 0; u < FLOOR_INFLIGHT; ++u) {
-      const uint32_t off = base + (uint32_t)u * FLOOR_WAVES * 1024u + (uint32_t)lane * 16u;
+    for (int u = 0; u < L; ++u) {
+      const uint32_t off = first + (st * L + (uint32_t)u) * FLOOR_WAVES * 1024u;
       v[u] = load16_stream(r, off < end ? off : OOB);
     }
+    __builtin_amdgcn_sched_barrier(0);             // every load of the step in flight before any is used
 #pragma unroll
-    for (int u = 0; u < FLOOR_INFLIGHT; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < L; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   if (out) {
     const uint32_t b = blockIdx.x * out_per_wg16, e = min(b + out_per_wg16, out16);
@@ -47,15 +59,27 @@ read_floor_kernel(const uint8_t* p, uint32_t bytes, uint32_t per_wg, uint32_t* s
   }
 }
 
+typedef void (*FloorFn)(const uint8_t*, uint32_t, uint32_t, uint32_t, uint32_t*, uint4*, uint32_t, uint32_t);
+const FloorFn kFloor[FLOOR_MAX_L] = {read_floor_kernel<1>, read_floor_kernel<2>,  read_floor_kernel<3>,
+                                     read_floor_kernel<4>, read_floor_kernel<5>,  read_floor_kernel<6>,
+                                     read_floor_kernel<7>, read_floor_kernel<8>,  read_floor_kernel<9>,
+                                     read_floor_kernel<10>, read_floor_kernel<11>, read_floor_kernel<12>};
+
 }  // namespace
 
 int launch_read_floor(const void* p, size_t bytes, int nwg, uint32_t* sink, void* out, size_t out_bytes,
                       hipStream_t stream) {
-  const uint32_t per = (uint32_t)((bytes + (size_t)nwg * 1024 - 1) / ((size_t)nwg * 1024)) * 1024u;
+  // each workgroup's share in whole 16-byte pieces; one wave load covers 1 KB of it, a step of the
+  // 8 waves L KB apiece
+  const uint32_t per = (uint32_t)((bytes + (size_t)nwg * 16 - 1) / ((size_t)nwg * 16)) * 16u;
+  const uint32_t kb = (per + 1023) / 1024;                       // wave loads a share needs
+  const uint32_t loads = (kb + FLOOR_WAVES - 1) / FLOOR_WAVES;   // ... per wave
+  const int L = loads == 0 ? 1 : loads < (uint32_t)FLOOR_MAX_L ? (int)loads : FLOOR_MAX_L;
+  const uint32_t steps = (loads + (uint32_t)L - 1) / (uint32_t)L;
   const uint32_t out16 = (uint32_t)(out_bytes / 16);
   const uint32_t out_per = (out16 + (uint32_t)nwg - 1) / (uint32_t)nwg;
-  hipLaunchKernelGGL(read_floor_kernel, dim3((unsigned)nwg), dim3(WAVE * FLOOR_WAVES), 0, stream,
-                     reinterpret_cast<const uint8_t*>(p), (uint32_t)bytes, per, sink,
+  hipLaunchKernelGGL(kFloor[L - 1], dim3((unsigned)nwg), dim3(WAVE * FLOOR_WAVES), 0, stream,
+                     reinterpret_cast<const uint8_t*>(p), (uint32_t)bytes, per, steps, sink,
                      out_bytes ? reinterpret_cast<uint4*>(out) : nullptr, out16, out_per);
   return hip_status(hipGetLastError());
 }
