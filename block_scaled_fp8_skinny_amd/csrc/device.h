@@ -162,15 +162,24 @@ __device__ __forceinline__ Tile tile_of_grid(const KParams& p) {
   return r;
 }
 
+// Exchange slot of output (m, c), c = g * N + n, inside one tree node's array of
+// mp16 * 16 * G * N slots (mp16 = M rounded up to whole 16s, in 16s). The slots of one 16 x 16
+// MFMA output block lie together, ordered (c / 16, m / 16, c % 4, c / 4 % 4, m % 16): the lanes
+// of a wave exchanging one value of their accumulator (16 rows x four column groups) touch 64
+// consecutive slots, four cache lines, where the element index would touch one line per row.
+__device__ __forceinline__ size_t exch_slot(int m, int c, int mp16) {
+  return ((((size_t)(c >> 4) * mp16 + (m >> 4)) * 4 + (c & 3)) << 6) + (((c >> 2) & 3) << 4) + (m & 15);
+}
+
 // Pairwise-combine tree over the split index for up to NV outputs of one lane (see the header
-// comment). v[i] is this split's partial of output i, off[i] its element index, live[i] whether
-// the lane owns it. All exchanges of one tree level are issued before any result is used, so a
-// level costs one round trip to memory. On return live[i] says whether this lane finished output
-// i (its total is then in v[i]). With p.part set the tree is left to a later kernel: split s
-// stores its partials and finishes nothing.
+// comment). v[i] is this split's partial of output i, off[i] its element index (m * G * N + c) and
+// mr[i] its row m, live[i] whether the lane owns it. All exchanges of one tree level are issued before any result
+// is used, so a level costs one round trip to memory. On return live[i] says whether this lane
+// finished output i (its total is then in v[i]). With p.part set the tree is left to a later
+// kernel: split s stores its partials and finishes nothing.
 template <int NV>
 __device__ __forceinline__ void combine_splits(const KParams& p, int s, float (&v)[NV],
-                                               const size_t (&off)[NV], bool (&live)[NV]) {
+                                               const size_t (&off)[NV], const int (&mr)[NV], bool (&live)[NV]) {
   const size_t mgn = (size_t)p.M * p.G * p.N;
   if (p.part) {
 #pragma unroll
@@ -182,14 +191,19 @@ __device__ __forceinline__ void combine_splits(const KParams& p, int s, float (&
   }
   // node j of a level with cnt live partials combines splits 2j and 2j + 1; its slot array follows
   // those of the earlier levels (cnt / 2 nodes each)
+  const int gn = p.G * p.N, mp16 = (p.M + 15) >> 4;
+  const size_t node = (size_t)mp16 * 16 * gn;
+  size_t slot[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) slot[i] = exch_slot(mr[i], (int)(off[i] - (size_t)mr[i] * gn), mp16);
   int idx = s, cnt = p.splits, level_base = 0;
   for (int lv = 0; lv < p.levels; ++lv) {
     if ((idx ^ 1) < cnt) {
-      unsigned long long* base = p.slots + (size_t)(level_base + (idx >> 1)) * mgn;
+      unsigned long long* base = p.slots + (size_t)(level_base + (idx >> 1)) * node;
       unsigned long long old[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i)
-        old[i] = live[i] ? atomicExch(base + off[i], (1ull << 32) | __float_as_uint(v[i])) : 0ull;
+        old[i] = live[i] ? atomicExch(base + slot[i], (1ull << 32) | __float_as_uint(v[i])) : 0ull;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         if (!live[i]) continue;
@@ -197,7 +211,7 @@ __device__ __forceinline__ void combine_splits(const KParams& p, int s, float (&
           live[i] = false;                          // the partner finishes this node
         } else {
           v[i] = __uint_as_float((uint32_t)old[i]) + v[i];
-          __hip_atomic_store(base + off[i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(base + slot[i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }

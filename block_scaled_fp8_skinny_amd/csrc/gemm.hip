@@ -259,6 +259,7 @@ gemm_kernel(KParams p) {
   constexpr int NV = MT * NT * 4;
   float v[NV];
   size_t off[NV];
+  int mr[NV];
   bool live[NV];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -271,9 +272,10 @@ gemm_kernel(KParams p) {
         const int n = n0 + wn * 16 * NT + ts * 16 + q4 * 4 + r;
         v[i] = acc[mt][ts][r];
         off[i] = ((size_t)m * G + g) * N + n;
+        mr[i] = m;
         live[i] = m < M;
       }
-  combine_splits<NV>(p, s, v, off, live);
+  combine_splits<NV>(p, s, v, off, mr, live);
 #pragma unroll
   for (int i = 0; i < NV; ++i)
     if (live[i]) store_out(p, off[i], v[i]);
@@ -444,6 +446,7 @@ gemm_direct_kernel(KParams p) {
   constexpr int NV = NT * 4;
   float v[NV];
   size_t off[NV];
+  int mr[NV];
   bool live[NV];
 #pragma unroll
   for (int ts = 0; ts < NT; ++ts)
@@ -451,9 +454,10 @@ gemm_direct_kernel(KParams p) {
     for (int r = 0; r < 4; ++r) {
       v[ts * 4 + r] = acc[ts][r];
       off[ts * 4 + r] = ((size_t)m * G + g) * N + n0 + wn * 16 * NT + ts * 16 + q4 * 4 + r;
+      mr[ts * 4 + r] = m;
       live[ts * 4 + r] = mrow;
     }
-  combine_splits<NV>(p, s, v, off, live);
+  combine_splits<NV>(p, s, v, off, mr, live);
 #pragma unroll
   for (int i = 0; i < NV; ++i)
     if (live[i]) store_out(p, off[i], v[i]);
@@ -550,6 +554,7 @@ __device__ __forceinline__ void rows_epilogue(KParams& p, f32x4_t (&acc)[MT][NT]
   constexpr int NV = TPW * 4;
   float v[NV];
   size_t off[NV];
+  int mr[NV];
   bool live[NV];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
@@ -559,10 +564,11 @@ __device__ __forceinline__ void rows_epilogue(KParams& p, f32x4_t (&acc)[MT][NT]
     for (int r = 0; r < 4; ++r) {
       v[i * 4 + r] = v4[i][r];
       off[i * 4 + r] = ((size_t)m * G + g) * N + n0 + ts * 16 + q4 * 4 + r;
+      mr[i * 4 + r] = m;
       live[i * 4 + r] = tix[i] < TILES && m < M;
     }
   }
-  combine_splits<NV>(p, s, v, off, live);
+  combine_splits<NV>(p, s, v, off, mr, live);
 #pragma unroll
   for (int i = 0; i < NV; ++i)
     if (live[i]) store_out(p, off[i], v[i]);
@@ -1359,6 +1365,7 @@ gemm_decode_kernel(KParams p) {
   constexpr int NV = NT * 4;
   float v[NV];
   size_t off[NV];
+  int mr[NV];
   bool live[NV];
 #pragma unroll
   for (int ts = 0; ts < NT; ++ts)
@@ -1366,9 +1373,10 @@ gemm_decode_kernel(KParams p) {
     for (int r = 0; r < 4; ++r) {
       v[ts * 4 + r] = acc[ts][r];
       off[ts * 4 + r] = ((size_t)m * G + g) * N + n0 + wn * TR * NT + ts * TR + q4 * 4 + r;
+      mr[ts * 4 + r] = m;
       live[ts * 4 + r] = mrow;
     }
-  combine_splits<NV>(p, s, v, off, live);
+  combine_splits<NV>(p, s, v, off, mr, live);
 #pragma unroll
   for (int i = 0; i < NV; ++i)
     if (live[i]) store_out(p, off[i], v[i]);
@@ -1619,6 +1627,7 @@ gemm_slab_kernel(KParams p) {
   constexpr int NV = TILES * 4;
   float v[NV];
   size_t off[NV];
+  int mr[NV];
   bool live[NV];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -1630,9 +1639,10 @@ gemm_slab_kernel(KParams p) {
         const int m = m0 + wm * 16 * MT + mt * 16 + r16;
         v[i] = acc[mt][ts][r];
         off[i] = ((size_t)m * G + g) * N + n0 + wn * 16 * NT + ts * 16 + q4 * 4 + r;
+        mr[i] = m;
         live[i] = m < M;
       }
-  combine_splits<NV>(p, s, v, off, live);
+  combine_splits<NV>(p, s, v, off, mr, live);
 #pragma unroll
   for (int i = 0; i < NV; ++i)
     if (live[i]) store_out(p, off[i], v[i]);
@@ -1827,14 +1837,16 @@ gemm_pair_kernel(KParams p) {
   }
   float v[4];
   size_t off[4];
+  int mr[4];
   bool lv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[i] = acc[i];
     off[i] = o + i;
+    mr[i] = m;
     lv[i] = live;
   }
-  combine_splits<4>(p, s, v, off, lv);
+  combine_splits<4>(p, s, v, off, mr, lv);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (lv[i]) store_out(p, off[i], v[i]);
@@ -1995,6 +2007,9 @@ const Config kConfigs[] = {
     RDCFG(1, 2, 8, 4, 2),     // 101 rows, LDS-mode: 16 x 32 tile, 8 waves along K, 2 in flight
     RDCFG(1, 2, 4, 8, 4),     // 102 rows, LDS-mode: 16 x 32 tile, 4 waves along K, 4 in flight
     TCFG(2, 2, 4, 4, 3, 1),   // 103 tile: 128 x 128, 16 waves of 32 x 32, 3 stages
+    // decode workgroups for splits of few chunks (small LDS: several workgroups per CU)
+    ECFG(1, 1, 4, 1, 8),      // 104 decode: 16 weight rows, 4 waves along K x 1 chunk
+    ECFG(1, 1, 8, 1, 8),      // 105 decode: 16 weight rows, 8 waves along K x 1 chunk
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2069,10 +2084,11 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
     // fp32 partials [splits][M][G][N], summed by the reduce kernel
     if (p.splits > 1) p.ws_bytes = (size_t)p.splits * s.M * s.G * s.N * 4;
   } else if (p.splits > 1) {
-    // one 64-bit slot per output element and tree node
+    // one 64-bit slot per output element and tree node, the rows rounded up to whole 16s (the
+    // slot layout groups each 16 x 16 output block)
     size_t nodes = 0;
     for (int c2 = p.splits; c2 > 1; c2 = (c2 + 1) >> 1) nodes += (size_t)(c2 >> 1);
-    p.ws_bytes = nodes * (size_t)s.M * s.G * s.N * 8;
+    p.ws_bytes = nodes * (size_t)((s.M + 15) / 16 * 16) * s.G * s.N * 8;
   }
   *plan = p;
   return BSFP8_OK;
@@ -2155,7 +2171,14 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool al
       cps = kchunks < 32 ? kchunks : 32;
     }
   }
-  if (split_k > 0) cps = (kchunks + split_k - 1) / split_k;
+  if (split_k > 0) {
+    cps = (kchunks + split_k - 1) / split_k;
+    // An explicit split leaves each workgroup a few chunks: a workgroup sized for them (fewer
+    // waves and chunk buffers, so several fit on a CU) instead of one sized for the whole range,
+    // most of whose waves would sit idle while its LDS keeps the CU to one workgroup at a time.
+    if (cfg == 54 || cfg == 59) cfg = cps <= 4 ? 104 : cps <= 8 ? 59 : cps <= 16 ? 60 : cfg;
+    else if (cfg == 20) cfg = cps <= 8 ? 21 : cps <= 16 ? 19 : cfg;
+  }
   const int st = plan_with(s, cfg, cps, plan);
   if (st != BSFP8_EINVAL) return st;
   // The one-pass choice cannot take this many chunks per split (an explicit split_k with a long
