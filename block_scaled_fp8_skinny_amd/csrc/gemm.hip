@@ -859,11 +859,16 @@ gemm_rows_dma_kernel(KParams p) {
     for (int ts = 0; ts < NT; ++ts) acc[mt][ts] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int wsw = (r16 >> 1) & 7;
-  auto compute = [&](int j) {
+  // A chunk's fragments (X, raw weight codes, block exponents) are read from its buffer first;
+  // the buffer is then refilled at once and the dequant and MFMAs run from registers while the
+  // next loads stream in.
+  bf16x8_t xf[MT][4];
+  uint4 wa[NT], wb[NT];
+  uint32_t eb0[NT], eb1[NT];
+  auto fetch = [&](int j) {
     const int cl = wk + j * NWK;                    // chunk index inside the workgroup
     const uint4* const b = area + (j % D) * BUF;
     // lane (r16, q4) takes the k values 64h + 16*q4 + 8u + [0, 8) of row r16 for MFMA 2h + u
-    bf16x8_t xf[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -874,14 +879,21 @@ gemm_rows_dma_kernel(KParams p) {
 #pragma unroll
     for (int ts = 0; ts < NT; ++ts) {
       const int er = (n0 + ts * 16 + r16) / 32 - n0 / 32;
-      const float sc0 = block_scale(e_lds[er * ECOLS + cl * 4 + (q4 >> 1)]);
-      const float sc1 = block_scale(e_lds[er * ECOLS + cl * 4 + 2 + (q4 >> 1)]);
-      const uint4 wa = b[XGR + (ts * 16 + r16) * 8 + (q4 ^ wsw)];
-      const uint4 wb = b[XGR + (ts * 16 + r16) * 8 + ((4 + q4) ^ wsw)];
-      const bf16x8_t w0 = dequant8(wa.x, wa.y, sc0);
-      const bf16x8_t w1 = dequant8(wa.z, wa.w, sc0);
-      const bf16x8_t w2 = dequant8(wb.x, wb.y, sc1);
-      const bf16x8_t w3 = dequant8(wb.z, wb.w, sc1);
+      eb0[ts] = e_lds[er * ECOLS + cl * 4 + (q4 >> 1)];
+      eb1[ts] = e_lds[er * ECOLS + cl * 4 + 2 + (q4 >> 1)];
+      wa[ts] = b[XGR + (ts * 16 + r16) * 8 + (q4 ^ wsw)];
+      wb[ts] = b[XGR + (ts * 16 + r16) * 8 + ((4 + q4) ^ wsw)];
+    }
+  };
+  auto math = [&]() {
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts) {
+      const float sc0 = block_scale(eb0[ts]);
+      const float sc1 = block_scale(eb1[ts]);
+      const bf16x8_t w0 = dequant8(wa[ts].x, wa[ts].y, sc0);
+      const bf16x8_t w1 = dequant8(wa[ts].z, wa[ts].w, sc0);
+      const bf16x8_t w2 = dequant8(wb[ts].x, wb[ts].y, sc1);
+      const bf16x8_t w3 = dequant8(wb[ts].z, wb[ts].w, sc1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x4_t c = acc[mt][ts];
@@ -907,11 +919,16 @@ gemm_rows_dma_kernel(KParams p) {
     } else {
       wait_vmcnt_le<0>();
     }
-    if (c_begin + wk + j * NWK < c_end) compute(j);
+    const bool live = c_begin + wk + j * NWK < c_end;
+    if (live) fetch(j);
     if (j + D < CW) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's reads of the buffer are done
+      // this wave's reads of the buffer are done (the compiler sees the wait, so the MFMAs below
+      // need none of their own)
+      __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue(j + D);
     }
+    if (live) math();
   }
   wait_vmcnt_le<0>();                               // no load may still be writing LDS
   rows_epilogue<MT, NT, NWK, WS>(p, acc, reinterpret_cast<f32x4_t*>(ring), wk, lane, m0, n0, g, s);
