@@ -17,7 +17,9 @@ weight copies so that the cache is cold, captured graphs, interleaved rounds):
   * the plain-read floor of each weight set: the same graph with the GEMM replaced by a kernel
     that only reads the copy's bytes with the GEMM's load shape (bsfp8_read_floor), and a bare
     launch (the same kernel reading nothing); and per configuration the read + write floor, the
-    same reads followed by a write of that configuration's output bytes.
+    same reads followed by a write of that configuration's output bytes; for the unsplit rows up
+    to M = 8, whose workgroups each read all the activation rows of their group, also the same
+    with every floor workgroup first reading an M x K bf16 slab of its group (floor_xrw).
 
 Per call: us_per_call = step time / C (gaps between launches included, as a graph replays them).
 value = weight-stream GB/s = (e4m3 bytes + exponent bytes) / us_per_call. roofline.achieved =
@@ -331,7 +333,7 @@ def make_call(torch, B, ws_set, name, M, split_k, path, x, out):
                                    out_dtype=od)), plan
 
 
-def entry_for(label, name, M, split_k, path, plan, t, ws_set, floor_t, launch_t, floor_rw_t=None):
+def entry_for(label, name, M, split_k, path, plan, t, ws_set, floor_t, launch_t, floor_rw_t=None, floor_xrw_t=None):
     G, N, K, erows = shape_of(name)
     w, e, x, y = algorithmic_bytes(name, M, path)
     us = t.us
@@ -359,6 +361,9 @@ def entry_for(label, name, M, split_k, path, plan, t, ws_set, floor_t, launch_t,
     if floor_rw_t is not None:
         ent["floor_rw_us_per_call"] = round(floor_rw_t.us, 3)
         ent["floor_rw_frac"] = round(floor_rw_t.us / us, 4)
+    if floor_xrw_t is not None:
+        ent["floor_xrw_us_per_call"] = round(floor_xrw_t.us, 3)
+        ent["floor_xrw_frac"] = round(floor_xrw_t.us / us, 4)
     return ent
 
 
@@ -565,7 +570,28 @@ def run(args):
         g = capture(torch, lambda i, s=ws_set, yb=yb: B.bsfp8_read_floor(s.bufs[i], nwg=FLOOR_WGS, sink=sink, out=yb),
                     len(ws_set))
         rw_floors[(ws_name, ob)] = Timed(("floor_rw", ws_name, ob), g, len(ws_set), args.reps)
-    every = timed + [t for pair in floors.values() for t in pair] + list(rw_floors.values())
+    # ... and, for the unsplit decode rows (M <= 8), where every workgroup also reads all the
+    # activation rows of its group, the same with each floor workgroup first reading its group's
+    # slab of M x K bf16 (cache-resident after the first reads, as the activations are)
+    xrw_floors = {}
+    for (label, name, M, split_k) in configs:
+        if M > 8 or split_k or path != "bf16" or name in ROW_SCALE_WORKLOADS:
+            continue
+        G, N, K, _ = shape_of(name)
+        ws_name = WEIGHT_SET[name]
+        ob = (algorithmic_bytes(name, M, path)[3] + 15) // 16 * 16
+        sb = (M * K * 2 + 15) // 16 * 16
+        if (ws_name, ob, sb, G) in xrw_floors:
+            continue
+        ws_set = sets[ws_name]
+        yb = torch.empty(ob, dtype=torch.uint8, device="cuda")
+        slab = torch.zeros(G * sb, dtype=torch.uint8, device="cuda")
+        keep.extend([yb, slab])
+        g = capture(torch, lambda i, s=ws_set, yb=yb, slab=slab, G=G: B.bsfp8_read_floor(
+            s.bufs[i], nwg=FLOOR_WGS, sink=sink, out=yb, slab=slab, slab_groups=G), len(ws_set))
+        xrw_floors[(ws_name, ob, sb, G)] = Timed(("floor_xrw", ws_name, ob, sb, G), g, len(ws_set), args.reps)
+    every = (timed + [t for pair in floors.values() for t in pair] + list(rw_floors.values()) +
+             list(xrw_floors.values()))
 
     # warm-up replays, then interleaved rounds
     for t in every:
@@ -581,8 +607,11 @@ def run(args):
     entries = []
     for t, (label, name, M, split_k, plan, ws_set) in zip(timed, meta):
         ft, lt = floors[WEIGHT_SET[name]]
-        rwt = rw_floors[(WEIGHT_SET[name], (algorithmic_bytes(name, M, path)[3] + 15) // 16 * 16)]
-        entries.append(entry_for(label, name, M, split_k, path, plan, t, ws_set, ft, lt, rwt))
+        ob = (algorithmic_bytes(name, M, path)[3] + 15) // 16 * 16
+        rwt = rw_floors[(WEIGHT_SET[name], ob)]
+        xkey = (WEIGHT_SET[name], ob, (M * shape_of(name)[2] * 2 + 15) // 16 * 16, shape_of(name)[0])
+        xrwt = xrw_floors.get(xkey) if not split_k else None
+        entries.append(entry_for(label, name, M, split_k, path, plan, t, ws_set, ft, lt, rwt, xrwt))
     floor_summary = {k: {"copy_bytes": sets[k].copy_bytes, "copies": len(sets[k]),
                          "read_us_per_call": round(f.us, 3), "read_gbs": round(sets[k].copy_bytes / (f.us * 1e3), 1),
                          "launch_us_per_call": round(l.us, 3), "workgroups": FLOOR_WGS}
@@ -631,6 +660,8 @@ def run(args):
         "floor_frac": head.get("floor_frac"),
         "floor_rw_us_per_call": head.get("floor_rw_us_per_call"),
         "floor_rw_frac": head.get("floor_rw_frac"),
+        "floor_xrw_us_per_call": head.get("floor_xrw_us_per_call"),
+        "floor_xrw_frac": head.get("floor_xrw_frac"),
         "roofline": dict(head["roofline"], traffic=traffic_from_profile(name, M) if path == "bf16" else None,
                          algorithmic_bytes_per_launch=head["algorithmic_bytes"]),
         "baseline_ref": "pages (GB10, other hardware): twin path 2.20 ms / 43 layers = 51.2 us/call at M=6",

@@ -386,14 +386,20 @@ int bsfp8_gemm_row32_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G
   return launch_gemm(s, p, x, q, e, ws, y, out_dtype == BSFP8_OUT_F32, as_stream(stream));
 }
 
-int bsfp8_read_floor(const void* p, size_t bytes, int nwg, uint32_t* sink, void* out, size_t out_bytes,
-                     void* stream) {
+int bsfp8_read_floor(const void* p, size_t bytes, int nwg, const void* slab, size_t slab_bytes, int slab_groups,
+                     uint32_t* sink, void* out, size_t out_bytes, void* stream) {
   if (nwg < 1 || nwg > 65536 || !sink || (out_bytes && !out)) return BSFP8_EINVAL;
+  if (slab_bytes && (!slab || slab_groups < 1 || slab_groups > nwg)) return BSFP8_EINVAL;
   if (bytes && (!p || !aligned16(p))) return BSFP8_ESTRIDE;
   if (out_bytes && (!aligned16(out) || out_bytes % 16)) return BSFP8_ESTRIDE;
+  if (slab_bytes && (!aligned16(slab) || slab_bytes % 16)) return BSFP8_ESTRIDE;
   if (bytes >= ((size_t)1 << 31) || out_bytes >= ((size_t)1 << 31)) return BSFP8_ESHAPE;
-  if (outputs_alias({{out, out_bytes}, {sink, (size_t)nwg * 4}}, {{p, bytes}})) return BSFP8_EINVAL;
-  return launch_read_floor(p, bytes, nwg, sink, out, out_bytes, as_stream(stream));
+  if (slab_bytes && slab_bytes * (size_t)slab_groups >= ((size_t)1 << 31)) return BSFP8_ESHAPE;
+  const size_t slab_span = slab_bytes ? slab_bytes * (size_t)slab_groups : 0;
+  if (outputs_alias({{out, out_bytes}, {sink, (size_t)nwg * 4}}, {{p, bytes}, {slab, slab_span}}))
+    return BSFP8_EINVAL;
+  return launch_read_floor(p, bytes, nwg, slab, slab_bytes, slab_bytes ? slab_groups : 1, sink, out, out_bytes,
+                           as_stream(stream));
 }
 
 int bsfp8_num_configs(void) { return num_gemm_configs(); }

@@ -11,7 +11,10 @@
 // approach on this machine; with bytes = 0 it is the cost of a launch. With an output buffer it
 // also writes `out_bytes` there (16 bytes per lane, each workgroup one contiguous share, after
 // its reads): the read + write floor of a GEMM that streams those bytes and stores that many
-// output bytes (a kernel that stores pays for its writes and their completion at its end).
+// output bytes (a kernel that stores pays for its writes and their completion at its end). With a
+// slab, every workgroup first reads its group's slab whole (one kilobyte per wave load, straight
+// into LDS, as the decode GEMMs read the activation rows of their group): the floor of a GEMM
+// whose workgroups each also read those shared, cache-resident bytes.
 #include "device.h"
 
 namespace bsfp8 {
@@ -27,14 +30,28 @@ constexpr uint32_t FLOOR_MAGIC = 0x9E3779B9u;
 // steps. Loads past the share (the last step's tail) read at the out-of-range offset.
 template <int L>
 __global__ void __launch_bounds__(WAVE * FLOOR_WAVES)
-read_floor_kernel(const uint8_t* p, uint32_t bytes, uint32_t per_wg, uint32_t steps, uint32_t* sink, uint4* out,
-                  uint32_t out16, uint32_t out_per_wg16) {
+read_floor_kernel(const uint8_t* p, uint32_t bytes, uint32_t per_wg, uint32_t steps, const uint8_t* slab,
+                  uint32_t slab_bytes, uint32_t slab_groups, uint32_t* sink, uint4* out, uint32_t out16,
+                  uint32_t out_per_wg16) {
   // every argument the loads need, fetched in one batch (left to itself the compiler fetched the
   // buffer pointer only after a bounds test: a second dependent round trip), and the ones the end
   // needs held in registers rather than fetched after the reads
-  asm volatile("" ::"s"(p), "s"(bytes), "s"(per_wg), "s"(steps));
+  asm volatile("" ::"s"(p), "s"(bytes), "s"(per_wg), "s"(steps), "s"(slab), "s"(slab_bytes), "s"(slab_groups));
   asm volatile("" : "+s"(sink), "+s"(out), "+s"(out16), "+s"(out_per_wg16));
+  __shared__ uint4 slab_lds[FLOOR_WAVES * WAVE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (slab_bytes) {
+    // the group's slab, wave w taking kilobytes w, w + 8, ... (every load lands in this wave's
+    // kilobyte of LDS; the contents are never read)
+    const uint32_t grp = (uint32_t)(((uint64_t)blockIdx.x * slab_groups) / gridDim.x);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)slab, 0, (int)(slab_bytes * slab_groups), RSRC_WORD3);
+    const lds_addr_t dst = lds_addr(slab_lds + wave * WAVE);
+    for (uint32_t o = (uint32_t)wave * 1024u; o < slab_bytes; o += FLOOR_WAVES * 1024u) {
+      const uint32_t off = o + (uint32_t)lane * 16u;
+      lds_load16(rs, dst, off < slab_bytes ? grp * slab_bytes + off : OOB);
+    }
+  }
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, (int)bytes, RSRC_WORD3);
   const uint32_t begin = blockIdx.x * per_wg;
   const uint32_t end = min(begin + per_wg, bytes);
@@ -51,6 +68,8 @@ read_floor_kernel(const uint8_t* p, uint32_t bytes, uint32_t per_wg, uint32_t st
 #pragma unroll
     for (int u = 0; u < L; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
+  // the slab loads write LDS: none may still be in flight when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (out) {
     const uint32_t b = blockIdx.x * out_per_wg16, e = min(b + out_per_wg16, out16);
     for (uint32_t i = b + threadIdx.x; i < e; i += WAVE * FLOOR_WAVES) out[i] = make_uint4(acc, acc, acc, acc);
@@ -59,7 +78,8 @@ read_floor_kernel(const uint8_t* p, uint32_t bytes, uint32_t per_wg, uint32_t st
   }
 }
 
-typedef void (*FloorFn)(const uint8_t*, uint32_t, uint32_t, uint32_t, uint32_t*, uint4*, uint32_t, uint32_t);
+typedef void (*FloorFn)(const uint8_t*, uint32_t, uint32_t, uint32_t, const uint8_t*, uint32_t, uint32_t, uint32_t*,
+                        uint4*, uint32_t, uint32_t);
 const FloorFn kFloor[FLOOR_MAX_L] = {read_floor_kernel<1>, read_floor_kernel<2>,  read_floor_kernel<3>,
                                      read_floor_kernel<4>, read_floor_kernel<5>,  read_floor_kernel<6>,
                                      read_floor_kernel<7>, read_floor_kernel<8>,  read_floor_kernel<9>,
@@ -67,8 +87,8 @@ const FloorFn kFloor[FLOOR_MAX_L] = {read_floor_kernel<1>, read_floor_kernel<2>,
 
 }  // namespace
 
-int launch_read_floor(const void* p, size_t bytes, int nwg, uint32_t* sink, void* out, size_t out_bytes,
-                      hipStream_t stream) {
+int launch_read_floor(const void* p, size_t bytes, int nwg, const void* slab, size_t slab_bytes, int slab_groups,
+                      uint32_t* sink, void* out, size_t out_bytes, hipStream_t stream) {
   // each workgroup's share in whole 16-byte pieces; one wave load covers 1 KB of it, a step of the
   // 8 waves L KB apiece
   const uint32_t per = (uint32_t)((bytes + (size_t)nwg * 16 - 1) / ((size_t)nwg * 16)) * 16u;
@@ -79,7 +99,8 @@ int launch_read_floor(const void* p, size_t bytes, int nwg, uint32_t* sink, void
   const uint32_t out16 = (uint32_t)(out_bytes / 16);
   const uint32_t out_per = (out16 + (uint32_t)nwg - 1) / (uint32_t)nwg;
   hipLaunchKernelGGL(kFloor[L - 1], dim3((unsigned)nwg), dim3(WAVE * FLOOR_WAVES), 0, stream,
-                     reinterpret_cast<const uint8_t*>(p), (uint32_t)bytes, per, steps, sink,
+                     reinterpret_cast<const uint8_t*>(p), (uint32_t)bytes, per, steps,
+                     reinterpret_cast<const uint8_t*>(slab), (uint32_t)slab_bytes, (uint32_t)slab_groups, sink,
                      out_bytes ? reinterpret_cast<uint4*>(out) : nullptr, out16, out_per);
   return hip_status(hipGetLastError());
 }

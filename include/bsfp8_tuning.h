@@ -85,25 +85,31 @@ BSFP8_API int bsfp8_gemm_mx_config(const uint8_t* xq, const uint8_t* xs, int64_t
 
 /* Plain-read floor, a measurement aid: one kernel that reads `bytes` of device memory at p once,
  * with the GEMM's load shape (16 bytes per lane, one contiguous kilobyte per wave load,
- * non-temporal, eight loads in flight per wave), on nwg workgroups of 512 threads that each read
- * one contiguous share, and computes nothing else. Timed over the same distinct weight copies and
- * in the same graph replay as a GEMM (the measurement protocol of page
- * "recipes/docker-images/mia-tp4/adapter/shared_pad_k.py", MEASUREMENT: distinct weight copies so
- * that the cache is cold, captured graphs, interleaved rounds), it gives the floor a GEMM that
- * streams those bytes can reach on this machine; bytes = 0 times a bare launch. With out_bytes > 0
- * each workgroup then also writes its contiguous share of `out` (16 bytes per lane): the floor of
- * a GEMM that reads those bytes and stores that many output bytes.
+ * non-temporal, every load of a workgroup's share issued before any is used), on nwg workgroups
+ * of 512 threads that each read one contiguous share, and computes nothing else. Timed over the
+ * same distinct weight copies and in the same graph replay as a GEMM (the measurement protocol of
+ * page "recipes/docker-images/mia-tp4/adapter/shared_pad_k.py", MEASUREMENT: distinct weight
+ * copies so that the cache is cold, captured graphs, interleaved rounds), it gives the floor a
+ * GEMM that streams those bytes can reach on this machine; bytes = 0 times a bare launch.
+ * With slab_bytes > 0 every workgroup first reads the whole slab of its group (workgroup b takes
+ * group b * slab_groups / nwg; LDS-mode loads of one kilobyte per wave): the floor of a GEMM
+ * whose workgroups also each read the activation rows of their group, as the decode GEMMs do.
+ * With out_bytes > 0 each workgroup then also writes its contiguous share of `out` (16 bytes per
+ * lane): the floor of a GEMM that reads those bytes and stores that many output bytes.
  *   p    : device memory, 16-byte aligned, at least `bytes` long (may be NULL when bytes = 0);
  *          bytes < 2^31.
+ *   slab : device memory, 16-byte aligned, slab_groups x slab_bytes long (NULL when slab_bytes
+ *          = 0); slab_bytes a multiple of 16, 1 <= slab_groups <= nwg, the whole below 2^31.
  *   sink : device uint32_t [nwg]; written only when a workgroup's fold of the data equals a fixed
  *          constant (it keeps the loads alive), so its contents are meaningless.
  *   out  : device memory, 16-byte aligned, out_bytes long (NULL when out_bytes = 0); out_bytes a
  *          multiple of 16 below 2^31; receives the workgroups' folds (meaningless contents).
- * Returns BSFP8_EINVAL (nwg outside 1..65536, no sink, out missing, out or sink overlapping p),
- * BSFP8_ESTRIDE (misaligned p or out, out_bytes not a multiple of 16), BSFP8_ESHAPE (bytes or
- * out_bytes too large), BSFP8_EHIP on a launch failure. */
-BSFP8_API int bsfp8_read_floor(const void* p, size_t bytes, int nwg, uint32_t* sink, void* out, size_t out_bytes,
-                               void* stream);
+ * Returns BSFP8_EINVAL (nwg outside 1..65536, no sink, out or slab missing, slab_groups out of
+ * range, out or sink overlapping p, the slab or each other), BSFP8_ESTRIDE (misaligned p, slab or
+ * out, slab_bytes or out_bytes not a multiple of 16), BSFP8_ESHAPE (bytes, the slab or out_bytes
+ * too large), BSFP8_EHIP on a launch failure. */
+BSFP8_API int bsfp8_read_floor(const void* p, size_t bytes, int nwg, const void* slab, size_t slab_bytes,
+                               int slab_groups, uint32_t* sink, void* out, size_t out_bytes, void* stream);
 
 #ifdef __cplusplus
 }

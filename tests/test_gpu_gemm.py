@@ -373,16 +373,22 @@ def test_binding_refuses_short_or_misplaced_buffers():
 
 
 def test_read_floor_reads_and_writes_in_bounds():
-    """The measurement aid of the bench: the plain-read floor kernel reads the bytes it is given,
-    touches the sink only on its fixed constant, and with an output buffer writes every byte of it
-    and nothing else (all-zero data fold to zero, so the written bytes are known)."""
+    """The measurement aid of the bench: the plain-read floor kernel reads the bytes it is given
+    (and, with a slab, every workgroup its group's part of the slab), touches the sink only on its
+    fixed constant, and with an output buffer writes every byte of it and nothing else (all-zero
+    data fold to zero, so the written bytes are known)."""
     t = torch.zeros(8 * 1024 * 1024 + 4096, dtype=torch.uint8, device="cuda")
     sink = torch.full((256,), 7, dtype=torch.int32, device="cuda")
     guard = torch.full((24576 + 4096,), 0xAB, dtype=torch.uint8, device="cuda")
     out = guard[:24576]
+    slab = torch.zeros(2 * 49152, dtype=torch.uint8, device="cuda")
     B.bsfp8_read_floor(t, nwg=256, sink=sink)
     B.bsfp8_read_floor(t, nbytes=0, nwg=256, sink=sink)
     B.bsfp8_read_floor(t, nwg=256, sink=sink, out=out)
+    B.bsfp8_read_floor(t, nwg=256, sink=sink, slab=slab, slab_groups=2)        # 48 KB per group
+    B.bsfp8_read_floor(t, nbytes=0, nwg=256, sink=sink, slab=slab[:6912], slab_groups=1)
+    guard[:24576].fill_(0xAB)
+    B.bsfp8_read_floor(t, nwg=256, sink=sink, out=out, slab=slab, slab_groups=2)
     torch.cuda.synchronize()
     assert bool((sink == 7).all())
     assert bool((out == 0).all())
