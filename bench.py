@@ -17,9 +17,10 @@ weight copies so that the cache is cold, captured graphs, interleaved rounds):
   * the plain-read floor of each weight set: the same graph with the GEMM replaced by a kernel
     that only reads the copy's bytes with the GEMM's load shape (bsfp8_read_floor), and a bare
     launch (the same kernel reading nothing); and per configuration the read + write floor, the
-    same reads followed by a write of that configuration's output bytes; for the unsplit rows up
-    to M = 8, whose workgroups each read all the activation rows of their group, also the same
-    with every floor workgroup first reading an M x K bf16 slab of its group (floor_xrw).
+    same reads followed by a write of that configuration's output bytes; for the unsplit rows
+    below the LM head also the data-movement floor (floor_xrw): the same, with every floor
+    workgroup first reading a slab of the bytes a workgroup of the plan reads beyond its share of
+    the weights (its activation rows, K wide, and the weight rows other m-blocks read again).
 
 Per call: us_per_call = step time / C (gaps between launches included, as a graph replays them).
 value = weight-stream GB/s = (e4m3 bytes + exponent bytes) / us_per_call. roofline.achieved =
@@ -570,26 +571,33 @@ def run(args):
         g = capture(torch, lambda i, s=ws_set, yb=yb: B.bsfp8_read_floor(s.bufs[i], nwg=FLOOR_WGS, sink=sink, out=yb),
                     len(ws_set))
         rw_floors[(ws_name, ob)] = Timed(("floor_rw", ws_name, ob), g, len(ws_set), args.reps)
-    # ... and, for the unsplit decode rows (M <= 8), where every workgroup also reads all the
-    # activation rows of its group, the same with each floor workgroup first reading its group's
-    # slab of M x K bf16 (cache-resident after the first reads, as the activations are)
-    xrw_floors = {}
-    for (label, name, M, split_k) in configs:
-        if M > 8 or split_k or path != "bf16" or name in ROW_SCALE_WORKLOADS:
-            continue
+    # ... and, for the unsplit rows below the LM head, the data-movement floor: the same, with each
+    # floor workgroup first reading a slab of the bytes a workgroup of the plan reads beyond its
+    # share of the weights (the activation rows of its m-block, K wide, and the weight rows that
+    # the plan's other m-blocks read again), spread over the 256 floor workgroups; those bytes are
+    # cache-resident after their first reads, as the activations and re-read weights are
+    def slab_of(name, M, plan):
         G, N, K, _ = shape_of(name)
-        ws_name = WEIGHT_SET[name]
-        ob = (algorithmic_bytes(name, M, path)[3] + 15) // 16 * 16
-        sb = (M * K * 2 + 15) // 16 * 16
-        if (ws_name, ob, sb, G) in xrw_floors:
+        rows = min(plan["BM"], M) if plan["mblocks"] == 1 else plan["BM"]
+        per = (rows * K * 2 * plan["workgroups"] + (plan["mblocks"] - 1) * G * N * K) // FLOOR_WGS
+        return (per + 15) // 16 * 16, G * plan["mblocks"]
+    xrw_floors, xkeys = {}, []
+    for (label, name, M, split_k, plan, ws_set) in meta:
+        xkeys.append(None)
+        if split_k or path != "bf16" or name in ROW_SCALE_WORKLOADS or name == "lm_head" or "BM" not in plan:
             continue
-        ws_set = sets[ws_name]
+        ob = (algorithmic_bytes(name, M, path)[3] + 15) // 16 * 16
+        sb, groups = slab_of(name, M, plan)
+        key = (WEIGHT_SET[name], ob, sb, groups)
+        xkeys[-1] = key
+        if key in xrw_floors:
+            continue
         yb = torch.empty(ob, dtype=torch.uint8, device="cuda")
-        slab = torch.zeros(G * sb, dtype=torch.uint8, device="cuda")
+        slab = torch.zeros(groups * sb, dtype=torch.uint8, device="cuda")
         keep.extend([yb, slab])
-        g = capture(torch, lambda i, s=ws_set, yb=yb, slab=slab, G=G: B.bsfp8_read_floor(
-            s.bufs[i], nwg=FLOOR_WGS, sink=sink, out=yb, slab=slab, slab_groups=G), len(ws_set))
-        xrw_floors[(ws_name, ob, sb, G)] = Timed(("floor_xrw", ws_name, ob, sb, G), g, len(ws_set), args.reps)
+        g = capture(torch, lambda i, s=ws_set, yb=yb, slab=slab, gr=groups: B.bsfp8_read_floor(
+            s.bufs[i], nwg=FLOOR_WGS, sink=sink, out=yb, slab=slab, slab_groups=gr), len(ws_set))
+        xrw_floors[key] = Timed(("floor_xrw",) + key, g, len(ws_set), args.reps)
     every = (timed + [t for pair in floors.values() for t in pair] + list(rw_floors.values()) +
              list(xrw_floors.values()))
 
@@ -605,12 +613,11 @@ def run(args):
     gpu_s = time.perf_counter() - t_start
 
     entries = []
-    for t, (label, name, M, split_k, plan, ws_set) in zip(timed, meta):
+    for t, (label, name, M, split_k, plan, ws_set), xkey in zip(timed, meta, xkeys):
         ft, lt = floors[WEIGHT_SET[name]]
         ob = (algorithmic_bytes(name, M, path)[3] + 15) // 16 * 16
         rwt = rw_floors[(WEIGHT_SET[name], ob)]
-        xkey = (WEIGHT_SET[name], ob, (M * shape_of(name)[2] * 2 + 15) // 16 * 16, shape_of(name)[0])
-        xrwt = xrw_floors.get(xkey) if not split_k else None
+        xrwt = xrw_floors.get(xkey) if xkey else None
         entries.append(entry_for(label, name, M, split_k, path, plan, t, ws_set, ft, lt, rwt, xrwt))
     floor_summary = {k: {"copy_bytes": sets[k].copy_bytes, "copies": len(sets[k]),
                          "read_us_per_call": round(f.us, 3), "read_gbs": round(sets[k].copy_bytes / (f.us * 1e3), 1),
