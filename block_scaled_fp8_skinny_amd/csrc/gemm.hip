@@ -2027,6 +2027,9 @@ const Config kConfigs[] = {
     // decode workgroups for splits of few chunks (small LDS: several workgroups per CU)
     ECFG(1, 1, 4, 1, 8),      // 104 decode: 16 weight rows, 4 waves along K x 1 chunk
     ECFG(1, 1, 8, 1, 8),      // 105 decode: 16 weight rows, 8 waves along K x 1 chunk
+    RDCFG(1, 1, 8, 4, 2),     // 106 rows, LDS-mode: 16 x 16 tile, 8 waves along K x 4 chunks
+    RDCFG(1, 1, 4, 8, 2),     // 107 rows, LDS-mode: 16 x 16 tile, 4 waves along K x 8 chunks
+    RDCFG(2, 1, 4, 8, 2),     // 108 rows, LDS-mode: 32 x 16 tile, 4 waves along K x 8 chunks
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2164,6 +2167,9 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool al
     if (s.M <= 16 && kchunks <= 8) {
       cfg = 25;                      // short K: 32 weight rows, 2 waves along K, no split
       cps = kchunks;
+    } else if (s.M > 16 && s.K % KCH == 0 && kchunks <= 32) {
+      cfg = 106;                     // 16 x 16 tiles staged through LDS, 8 waves along K x 4
+      cps = kchunks;                 // chunks (bitwise the sums of the register kernel 20)
     } else {
       cfg = 20;                      // 16 weight rows, 8 waves along K x 4 chunks
       cps = 32;
@@ -2194,7 +2200,7 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool al
     // waves and chunk buffers, so several fit on a CU) instead of one sized for the whole range,
     // most of whose waves would sit idle while its LDS keeps the CU to one workgroup at a time.
     if (cfg == 54 || cfg == 59) cfg = cps <= 4 ? 104 : cps <= 8 ? 59 : cps <= 16 ? 60 : cfg;
-    else if (cfg == 20) cfg = cps <= 8 ? 21 : cps <= 16 ? 19 : cfg;
+    else if (cfg == 20 || cfg == 106) cfg = cps <= 8 ? 21 : cps <= 16 ? 19 : cfg;
   }
   const int st = plan_with(s, cfg, cps, plan);
   if (st != BSFP8_EINVAL) return st;
