@@ -26,7 +26,9 @@ Per call: us_per_call = step time / C (gaps between launches included, as a grap
 value = weight-stream GB/s = (e4m3 bytes + exponent bytes) / us_per_call. roofline.achieved =
 algorithmic bytes (weights + exponents + X + Y) / us_per_call, as a fraction of 8 TB/s.
 Every configuration named by the workloads gets such an entry in "configs", with the floor, the
-roofline fraction, the MFMA rate and the CPU oracle's time (all host threads and one thread).
+roofline fraction, the MFMA rate and the CPU oracle's time (all host threads and one thread);
+so do the twin encoder (make_twin) and the standalone dequantisation (bsfp8_dequant) per
+[4, 1024, 4096] layer.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--rounds R] [--no-cpu-baseline]
        [--headline-only] [--workload NAME --m M [--path P] [--split-k S]] [--extra FILE]
@@ -220,6 +222,47 @@ def twin_weight_set(torch, B, seed, n_layers=TWIN_LAYERS, reps=5):
     same = all(torch.equal(t.q, q0) and torch.equal(t.e, e0) for t, q0, e0 in zip(twins, src.q, src.e))
     nbytes = G * N * K * 2 + G * N * K + 2 * G * (N // 32) * (K // 32)   # read bf16; write codes, exps, ok
     us = statistics.median(round_means)
+    # the standalone dequantisation (the twin back to bf16, into the layers' own buffers, so every
+    # call reads and writes its own cold copy): one graph of n_layers calls, `reps` timed replays
+    g = capture(torch, lambda i: B.bsfp8_dequant(twins[i].q, twins[i].e, out=layers[i]), n_layers)
+    g.replay()
+    torch.cuda.synchronize()
+    dq_rounds = []
+    for rd in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        dq_rounds.append(1e3 * a.elapsed_time(b) / n_layers)
+    dq_bytes = G * N * K + G * (N // 32) * (K // 32) + G * N * K * 2     # read codes, exps; write bf16
+    dq_us = statistics.median(dq_rounds)
+    # its read + write floor: the floor kernel reading each twin copy and writing the layer's bytes
+    sink = torch.empty(FLOOR_WGS, dtype=torch.int32, device="cuda")
+    gf = capture(torch, lambda i: B.bsfp8_read_floor(bufs[i], nwg=FLOOR_WGS, sink=sink,
+                                                     out=layers[i].view(torch.uint8).reshape(-1)), n_layers)
+    gf.replay()
+    torch.cuda.synchronize()
+    fl_rounds = []
+    for rd in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        gf.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        fl_rounds.append(1e3 * a.elapsed_time(b) / n_layers)
+    fl_us = statistics.median(fl_rounds)
+    dequant_entry = {
+        "label": "f1 dequant", "workload": "wo_a_tp3", "path": "dequant",
+        "desc": f"bsfp8_dequant of {n_layers} twins [{G},{N},{K}] to bf16, each into its own layer buffer "
+                f"(one graph of {n_layers} calls)",
+        "layers": n_layers, "us_per_layer": round(dq_us, 3),
+        "us_per_layer_rounds": [round(v, 3) for v in dq_rounds], "bytes_per_layer": dq_bytes,
+        "floor_rw_us_per_layer": round(fl_us, 3), "floor_rw_frac": round(fl_us / dq_us, 4),
+        "roofline": {"bound": "hbm", "achieved": round(dq_bytes / (dq_us * 1e3), 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dq_bytes / (dq_us * 1e3) / HBM_PEAK_GBS, 4)},
+    }
+    del g, gf
     twin_entry = {
         "label": "d4 make_twin", "workload": "wo_a_tp3", "path": "make_twin",
         "desc": f"make_twin of {n_layers} exact bf16 layers [{G},{N},{K}] (synchronous prepare call: "
@@ -231,7 +274,7 @@ def twin_weight_set(torch, B, seed, n_layers=TWIN_LAYERS, reps=5):
                      "unit": "GB/s", "frac": round(nbytes / (us * 1e3) / HBM_PEAK_GBS, 4)},
     }
     del layers, src
-    return WeightSet(torch, name, bufs), twin_entry
+    return WeightSet(torch, name, bufs), [twin_entry, dequant_entry]
 
 
 def activations(torch, M, G, K, seed):
@@ -469,6 +512,18 @@ def cpu_twin_baseline(seconds):
                       f"scaled by 4 to the [4,1024,4096] layer (NumPy elementwise work, one thread)"}
 
 
+def cpu_dequant_baseline(seconds):
+    """oracle.dequant_bf16 on one group [1, 1024, 4096] of the padded-TP3 layer, scaled to the layer."""
+    import oracle
+    import synthetic as S
+    src = S.twin_source(7700, G=1, R=1024, D=4096)
+    calls, t = _oracle_leg(lambda: oracle.dequant_bf16(src["q"], src["e"]), seconds)
+    us = 1e6 * t / calls * 4
+    return {"us_per_layer": round(us, 1), "kind": "oracle", "threads": 1,
+            "sample": f"{calls} oracle.dequant_bf16 calls on one group [1,1024,4096] of a layer, {t:.2f} s, "
+                      f"scaled by 4 to the [4,1024,4096] layer (NumPy elementwise work)"}
+
+
 # ------------------------------------------------------------------------------------------------
 def gemm_source_sha256():
     """Hash of the sources the bf16 GEMM kernels are built from (gemm.hip and device.h)."""
@@ -512,14 +567,14 @@ def run(args):
         path = "bf16"
 
     # weight sets
-    sets, twin_entry = {}, None
+    sets, prep_entries = {}, None
     needed = {WEIGHT_SET[c[1]] for c in configs}
     seeds = {"wo_a": 7000, "shared_down": 7200, "lm_head": 7300, "main_proj": 7400}
     for ws_name in sorted(needed):
         if ws_name == "shared_down_pad":
             continue
         if ws_name == "wo_a_tp3":
-            sets[ws_name], twin_entry = twin_weight_set(torch, B, 7500, reps=max(3, args.rounds))
+            sets[ws_name], prep_entries = twin_weight_set(torch, B, 7500, reps=max(3, args.rounds))
         else:
             sets[ws_name] = random_weight_set(torch, ws_name, seeds[ws_name])
     if "shared_down_pad" in needed:
@@ -636,8 +691,9 @@ def run(args):
             if split_k and not is_head:             # same oracle call as the built-in plan's entry
                 continue
             ent["cpu_baseline"] = cpu_baseline(name, M, secs, n_rows=rows)
-        if twin_entry is not None:
-            twin_entry["cpu_baseline"] = cpu_twin_baseline(2.0)
+        if prep_entries is not None:
+            prep_entries[0]["cpu_baseline"] = cpu_twin_baseline(2.0)
+            prep_entries[1]["cpu_baseline"] = cpu_dequant_baseline(1.0)
 
     head = entries[hl_index]
     name, M = headline[1], headline[2]
@@ -675,8 +731,8 @@ def run(args):
     }
     if "cpu_baseline" in head:
         line["cpu_baseline"] = head["cpu_baseline"]
-    if len(entries) > 1 or twin_entry is not None:
-        line["configs"] = entries + ([twin_entry] if twin_entry is not None else [])
+    if len(entries) > 1 or prep_entries is not None:
+        line["configs"] = entries + (prep_entries or [])
         line["floors"] = floor_summary
     line["timing"] = {"gpu_setup_and_rounds_s": round(gpu_s, 1), "total_s": round(time.perf_counter() - t_start, 1)}
     return line

@@ -282,7 +282,7 @@ int bsfp8_pad_k_input(const uint16_t* x, int64_t ldx, int64_t M, int64_t G, int6
 
 int bsfp8_dequant(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
                   uint16_t* w_out, void* stream) {
-  if (G < 0 || N < 0 || K < 0 || N % 32 || K % 32) return BSFP8_ESHAPE;
+  if (G < 0 || N < 0 || K < 0 || N % 32 || K % 32 || K > (1 << 24)) return BSFP8_ESHAPE;
   if (G * N * K == 0) return BSFP8_OK;
   if (!q || !e || !w_out) return BSFP8_EINVAL;
   if (!aligned16(q) || !aligned16(w_out)) return BSFP8_ESTRIDE;

@@ -123,7 +123,11 @@ BSFP8_API int bsfp8_pad_k_weight(const uint8_t* q, const uint8_t* e, int64_t G, 
 
 /* Standalone dequantisation of a twin to bf16 (page "wo_a_w8.py", _dequant_kernel and
  * dequant_into_scratch): w_out[g][n][k] = bf16(e4m3(q) * 2^(b-127)), exact.
- *   q: [G][N][K], e: [G][N/32][K/32], w_out: uint16_t [G][N][K] (all device, caller-owned). */
+ *   q: [G][N][K], e: [G][N/32][K/32], w_out: uint16_t [G][N][K] (all device, caller-owned);
+ *   N and K multiples of 32, K <= 2^24; q and w_out 16-byte aligned. Asynchronous.
+ * Returns BSFP8_ESHAPE (N or K not a multiple of 32, negative sizes, K > 2^24), BSFP8_EINVAL
+ * (a missing pointer, w_out overlapping q or e), BSFP8_ESTRIDE (misaligned q or w_out), BSFP8_EHIP
+ * on a launch failure; nothing to do (a zero size) is BSFP8_OK. */
 BSFP8_API int bsfp8_dequant(const uint8_t* q, const uint8_t* e, int64_t G, int64_t N, int64_t K,
                   uint16_t* w_out, void* stream);
 

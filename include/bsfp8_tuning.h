@@ -95,7 +95,8 @@ BSFP8_API int bsfp8_gemm_mx_config(const uint8_t* xq, const uint8_t* xs, int64_t
  * group b * slab_groups / nwg; LDS-mode loads of one kilobyte per wave): the floor of a GEMM
  * whose workgroups also each read the activation rows of their group, as the decode GEMMs do.
  * With out_bytes > 0 each workgroup then also writes its contiguous share of `out` (16 bytes per
- * lane): the floor of a GEMM that reads those bytes and stores that many output bytes.
+ * lane; non-temporal stores for shares of 16 KB and more): the floor of a kernel that reads those
+ * bytes and stores that many output bytes.
  *   p    : device memory, 16-byte aligned, at least `bytes` long (may be NULL when bytes = 0);
  *          bytes < 2^31.
  *   slab : device memory, 16-byte aligned, slab_groups x slab_bytes long (NULL when slab_bytes

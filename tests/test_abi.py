@@ -178,6 +178,7 @@ def test_argument_checks_return_before_gpu_work(lib):
     assert lib.bsfp8_pad_k_weight(null, null, 1, 32, 64, 48, null, null, null) == B.ESHAPE
     assert lib.bsfp8_pad_k_input(null, 10, 1, 1, 32, 64, null, null) == B.ESTRIDE
     assert lib.bsfp8_dequant(null, null, 1, 32, 40, null, null) == B.ESHAPE
+    assert lib.bsfp8_dequant(null, null, 1, 32, (1 << 24) + 32, null, null) == B.ESHAPE
     assert lib.bsfp8_scales_from_f32(null, -1, 2, null, ctypes.byref(bad), null) == B.ESHAPE
 
 

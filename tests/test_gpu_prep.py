@@ -145,6 +145,26 @@ def test_dequant_all_codes_all_exponents_bitwise():
     assert np.array_equal(got, oracle.dequant_bf16(q, e))
 
 
+def test_dequant_over_several_launches_bitwise():
+    """More than 2^30 codes: the library dequantises in row ranges of under 2^30 codes (its indices
+    are 32-bit); rows on both sides of each range boundary, and the last rows, equal the oracle."""
+    K = 1 << 14
+    N = (1 << 16) + 96                      # 65632 rows: the first range holds 65536 of them
+    g = torch.Generator(device="cuda").manual_seed(3300)
+    q = torch.randint(0, 256, (1, N, K), dtype=torch.uint8, device="cuda", generator=g)
+    q[q == 0x7F] = 0
+    q[q == 0xFF] = 0
+    e = torch.randint(110, 140, (1, N // 32, K // 32), dtype=torch.uint8, device="cuda", generator=g)
+    w = B.bsfp8_dequant(q, e)
+    torch.cuda.synchronize()
+    for r0 in (0, 65504, 65536, N - 32):
+        qs = q[:, r0:r0 + 32].cpu().numpy()
+        es = e[:, r0 // 32:r0 // 32 + 1].cpu().numpy()
+        got = bf16_bits(w[:, r0:r0 + 32])
+        assert np.array_equal(got, oracle.dequant_bf16(qs, es)), r0
+    del w, q
+
+
 def test_dequant_round_trip_of_twin():
     src = S.twin_source(3200, G=4, R=128, D=256)
     w = oracle.dequant_bf16(src["q"], src["e"])

@@ -29,7 +29,7 @@ def wo_a_weight():
     return d, W, to_gpu_u8(d["q"]), to_gpu_u8(d["e"])
 
 
-@pytest.mark.parametrize("M", [2, 4, 6, 8, 16, 32, 64, 128, 192])
+@pytest.mark.parametrize("M", [2, 4, 6, 8, 16, 24, 32, 64, 128, 192])
 def test_wo_a_full_size(wo_a_weight, M):
     d, W, qt, et = wo_a_weight
     x = S.bf16_normal(S.rng(2100 + M), (M, 2 * 4096))
