@@ -142,10 +142,13 @@ BSFP8_API int bsfp8_pad_k_input(const uint16_t* x, int64_t ldx, int64_t M, int64
                       int64_t K_pad, uint16_t* x_pad, void* stream);
 
 /* Workspace bytes the GEMM entry points need for this shape (0 when no split of K across
- * workgroups is used). split_k as in the GEMM calls (0 = built-in table). The workspace holds
- * fp32 split-K partials and one arrival counter per output tile. It must be ZERO-FILLED once
- * after allocation; every call leaves the counters at zero again. One workspace must not be used
- * by two calls that can run at the same time (e.g. on two streams). */
+ * workgroups is used). split_k as in the GEMM calls (0 = built-in table). The workspace holds,
+ * for the one-pass kernels, one 64-bit exchange slot per output (rows rounded up to 16) and node
+ * of the pairwise-combine tree over the splits, and for the tile kernel the fp32 partials
+ * [splits][M][G][N] its reduce kernel sums. It must be ZERO-FILLED once after allocation; every
+ * call leaves the exchange slots at zero again (the second partner of each node clears its slot).
+ * One workspace must not be used by two calls that can run at the same time (e.g. on two
+ * streams). */
 BSFP8_API size_t bsfp8_workspace_bytes(int64_t M, int64_t G, int64_t N, int64_t K, int split_k);
 
 /* The GEMM. Page "wo_a_w8.py": _wo_a_partial_w8 (2..8 rows) and _wo_a_mid_kernel (9..192 rows).
