@@ -39,7 +39,7 @@ _SIGS = {
     "bsfp8_gemm": (_I, _GEMM_ARGS),
     "bsfp8_gemm_no_alloc": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I, _P, _I, _P]),
     "bsfp8_num_configs": (_I, []),
-    "bsfp8_read_floor": (_I, [_P, _SZ, _I, _P, _SZ, _I, _P, _P, _SZ, _P]),
+    "bsfp8_read_floor": (_I, [_P, _SZ, _I, _P, _SZ, _I, _I, _P, _P, _SZ, _P]),
     "bsfp8_config_info": (_I, [_I, ctypes.POINTER(_I)]),
     "bsfp8_plan_info": (_I, [_I64, _I64, _I64, _I64, _I, _I, ctypes.POINTER(_I)]),
     "bsfp8_workspace_bytes_config": (_SZ, [_I64, _I64, _I64, _I64, _I, _I]),
@@ -337,12 +337,13 @@ def bsfp8_num_configs():
     return int(lib().bsfp8_num_configs())
 
 
-def bsfp8_read_floor(t, nbytes=None, nwg=256, sink=None, out=None, slab=None, slab_groups=1):
+def bsfp8_read_floor(t, nbytes=None, nwg=256, sink=None, out=None, slab=None, slab_groups=1, interleave=False):
     """Plain-read floor: one kernel that reads the first nbytes (default: all) of the GPU tensor t
     once with the GEMM's load shape and computes nothing else (a measurement aid; nbytes = 0 is a
     bare launch). sink: uint32 [nwg] on t's device (allocated when None). slab: a contiguous GPU
-    tensor of slab_groups equal parts; every workgroup first reads the part of its group whole
-    (the activation rows every decode workgroup reads), or None. out: a contiguous GPU tensor of a
+    tensor of slab_groups equal parts; every workgroup also reads the part of its group whole
+    (the activation rows every workgroup of a GEMM reads), before its share of t, or spread over
+    the steps of that share with interleave=True; or None. out: a contiguous GPU tensor of a
     multiple of 16 bytes that the kernel also writes whole (the read + write floor of a GEMM
     storing that many output bytes), or None. Returns the sink."""
     nb = t.numel() * t.element_size() if nbytes is None else int(nbytes)
@@ -366,8 +367,8 @@ def bsfp8_read_floor(t, nbytes=None, nwg=256, sink=None, out=None, slab=None, sl
         if slab_groups < 1 or total % slab_groups:
             raise ValueError(f"slab of {total} bytes does not split into {slab_groups} groups")
         sb = total // slab_groups
-    _check(lib().bsfp8_read_floor(_ptr(t), nb, nwg, _ptr(slab), sb, int(slab_groups), _ptr(sink), _ptr(out), ob,
-                                  _stream(t)), "bsfp8_read_floor")
+    _check(lib().bsfp8_read_floor(_ptr(t), nb, nwg, _ptr(slab), sb, int(slab_groups), 1 if interleave else 0,
+                                  _ptr(sink), _ptr(out), ob, _stream(t)), "bsfp8_read_floor")
     return sink
 
 

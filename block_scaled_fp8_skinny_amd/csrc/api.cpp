@@ -387,8 +387,9 @@ int bsfp8_gemm_row32_config(const uint16_t* x, int64_t ldx, int64_t M, int64_t G
 }
 
 int bsfp8_read_floor(const void* p, size_t bytes, int nwg, const void* slab, size_t slab_bytes, int slab_groups,
-                     uint32_t* sink, void* out, size_t out_bytes, void* stream) {
+                     int flags, uint32_t* sink, void* out, size_t out_bytes, void* stream) {
   if (nwg < 1 || nwg > 65536 || !sink || (out_bytes && !out)) return BSFP8_EINVAL;
+  if (flags & ~BSFP8_FLOOR_SLAB_INTERLEAVED) return BSFP8_EINVAL;
   if (slab_bytes && (!slab || slab_groups < 1 || slab_groups > nwg)) return BSFP8_EINVAL;
   if (bytes && (!p || !aligned16(p))) return BSFP8_ESTRIDE;
   if (out_bytes && (!aligned16(out) || out_bytes % 16)) return BSFP8_ESTRIDE;
@@ -398,8 +399,8 @@ int bsfp8_read_floor(const void* p, size_t bytes, int nwg, const void* slab, siz
   const size_t slab_span = slab_bytes ? slab_bytes * (size_t)slab_groups : 0;
   if (outputs_alias({{out, out_bytes}, {sink, (size_t)nwg * 4}}, {{p, bytes}, {slab, slab_span}}))
     return BSFP8_EINVAL;
-  return launch_read_floor(p, bytes, nwg, slab, slab_bytes, slab_bytes ? slab_groups : 1, sink, out, out_bytes,
-                           as_stream(stream));
+  return launch_read_floor(p, bytes, nwg, slab, slab_bytes, slab_bytes ? slab_groups : 1,
+                           (flags & BSFP8_FLOOR_SLAB_INTERLEAVED) != 0, sink, out, out_bytes, as_stream(stream));
 }
 
 int bsfp8_num_configs(void) { return num_gemm_configs(); }

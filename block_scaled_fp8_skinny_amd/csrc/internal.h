@@ -95,7 +95,7 @@ int mx_pick(int M, int G, int N);
 // Plain-read floor of a weight stream (measure.hip): reads `bytes` once with the GEMM's load shape,
 // then, with out_bytes > 0, writes that many bytes to out.
 int launch_read_floor(const void* p, size_t bytes, int nwg, const void* slab, size_t slab_bytes, int slab_groups,
-                      uint32_t* sink, void* out, size_t out_bytes, hipStream_t stream);
+                      int interleave, uint32_t* sink, void* out, size_t out_bytes, hipStream_t stream);
 
 // Static scratch of bsfp8_gemm_no_alloc (scratch.hip): the array's address on the device of
 // `stream` (the current device for a null stream), looked up once per device.

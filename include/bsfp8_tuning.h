@@ -91,9 +91,12 @@ BSFP8_API int bsfp8_gemm_mx_config(const uint8_t* xq, const uint8_t* xs, int64_t
  * page "recipes/docker-images/mia-tp4/adapter/shared_pad_k.py", MEASUREMENT: distinct weight
  * copies so that the cache is cold, captured graphs, interleaved rounds), it gives the floor a
  * GEMM that streams those bytes can reach on this machine; bytes = 0 times a bare launch.
- * With slab_bytes > 0 every workgroup first reads the whole slab of its group (workgroup b takes
+ * With slab_bytes > 0 every workgroup also reads the whole slab of its group (workgroup b takes
  * group b * slab_groups / nwg; LDS-mode loads of one kilobyte per wave): the floor of a GEMM
- * whose workgroups also each read the activation rows of their group, as the decode GEMMs do.
+ * whose workgroups also each read the activation rows of their group, as the GEMMs do. The slab
+ * is read before the share, or, with flags = BSFP8_FLOOR_SLAB_INTERLEAVED, spread evenly over
+ * the steps of the share (each step's slab loads issued just before its share loads, as a GEMM
+ * issues each chunk's activations before its weights); flags = 0 otherwise.
  * With out_bytes > 0 each workgroup then also writes its contiguous share of `out` (16 bytes per
  * lane; non-temporal stores for shares of 16 KB and more): the floor of a kernel that reads those
  * bytes and stores that many output bytes.
@@ -106,11 +109,13 @@ BSFP8_API int bsfp8_gemm_mx_config(const uint8_t* xq, const uint8_t* xs, int64_t
  *   out  : device memory, 16-byte aligned, out_bytes long (NULL when out_bytes = 0); out_bytes a
  *          multiple of 16 below 2^31; receives the workgroups' folds (meaningless contents).
  * Returns BSFP8_EINVAL (nwg outside 1..65536, no sink, out or slab missing, slab_groups out of
- * range, out or sink overlapping p, the slab or each other), BSFP8_ESTRIDE (misaligned p, slab or
+ * range, an unknown flag, out or sink overlapping p, the slab or each other), BSFP8_ESTRIDE (misaligned p, slab or
  * out, slab_bytes or out_bytes not a multiple of 16), BSFP8_ESHAPE (bytes, the slab or out_bytes
  * too large), BSFP8_EHIP on a launch failure. */
+#define BSFP8_FLOOR_SLAB_INTERLEAVED 1
 BSFP8_API int bsfp8_read_floor(const void* p, size_t bytes, int nwg, const void* slab, size_t slab_bytes,
-                               int slab_groups, uint32_t* sink, void* out, size_t out_bytes, void* stream);
+                               int slab_groups, int flags, uint32_t* sink, void* out, size_t out_bytes,
+                               void* stream);
 
 #ifdef __cplusplus
 }

@@ -153,26 +153,27 @@ def test_argument_checks_return_before_gpu_work(lib):
     # the floor kernel's checks: a sink, an output buffer when output bytes are asked for, 16-byte
     # alignment and a multiple of 16 bytes, and no overlap with what it reads
     F = lib.bsfp8_read_floor
-    # F(p, bytes, nwg, slab, slab_bytes, slab_groups, sink, out, out_bytes, stream)
-    assert F(xa, 1024, 0, null, 0, 1, ya, null, 0, null) == B.EINVAL
-    assert F(xa, 1024, 4, null, 0, 1, null, null, 0, null) == B.EINVAL
-    assert F(xa, 1024, 4, null, 0, 1, ya, null, 64, null) == B.EINVAL
-    assert F(ctypes.c_void_p((1 << 32) + 8), 1024, 4, null, 0, 1, ya, null, 0, null) == B.ESTRIDE
-    assert F(xa, 1024, 4, null, 0, 1, ya, ctypes.c_void_p((4 << 32) + 4096 + 8), 64, null) == B.ESTRIDE
-    assert F(xa, 1024, 4, null, 0, 1, ya, ctypes.c_void_p((4 << 32) + 4096), 40, null) == B.ESTRIDE
-    assert F(xa, 1 << 31, 4, null, 0, 1, ya, null, 0, null) == B.ESHAPE
-    assert F(xa, 1024, 4, null, 0, 1, ya, ctypes.c_void_p((1 << 32) + 512), 64, null) == B.EINVAL
+    # F(p, bytes, nwg, slab, slab_bytes, slab_groups, flags, sink, out, out_bytes, stream)
+    assert F(xa, 1024, 0, null, 0, 1, 0, ya, null, 0, null) == B.EINVAL
+    assert F(xa, 1024, 4, null, 0, 1, 0, null, null, 0, null) == B.EINVAL
+    assert F(xa, 1024, 4, null, 0, 1, 0, ya, null, 64, null) == B.EINVAL
+    assert F(xa, 1024, 4, null, 0, 1, 2, ya, null, 0, null) == B.EINVAL     # unknown flag
+    assert F(ctypes.c_void_p((1 << 32) + 8), 1024, 4, null, 0, 1, 0, ya, null, 0, null) == B.ESTRIDE
+    assert F(xa, 1024, 4, null, 0, 1, 0, ya, ctypes.c_void_p((4 << 32) + 4096 + 8), 64, null) == B.ESTRIDE
+    assert F(xa, 1024, 4, null, 0, 1, 0, ya, ctypes.c_void_p((4 << 32) + 4096), 40, null) == B.ESTRIDE
+    assert F(xa, 1 << 31, 4, null, 0, 1, 0, ya, null, 0, null) == B.ESHAPE
+    assert F(xa, 1024, 4, null, 0, 1, 0, ya, ctypes.c_void_p((1 << 32) + 512), 64, null) == B.EINVAL
     # the slab: present when it has bytes, 1..nwg groups, aligned, a multiple of 16 bytes, under
     # 2^31 bytes in all, and no output over it
     sl = ctypes.c_void_p(5 << 32)
-    assert F(xa, 1024, 4, null, 64, 1, ya, null, 0, null) == B.EINVAL
-    assert F(xa, 1024, 4, sl, 64, 0, ya, null, 0, null) == B.EINVAL
-    assert F(xa, 1024, 4, sl, 64, 5, ya, null, 0, null) == B.EINVAL
-    assert F(xa, 1024, 4, ctypes.c_void_p((5 << 32) + 8), 64, 1, ya, null, 0, null) == B.ESTRIDE
-    assert F(xa, 1024, 4, sl, 40, 1, ya, null, 0, null) == B.ESTRIDE
-    assert F(xa, 1024, 4, sl, 1 << 30, 2, ya, null, 0, null) == B.ESHAPE
-    assert F(xa, 1024, 4, sl, 4096, 2, ya, ctypes.c_void_p((5 << 32) + 4096), 64, null) == B.EINVAL
-    assert F(xa, 1024, 4, sl, 4096, 2, ctypes.c_void_p((5 << 32) + 64), null, 0, null) == B.EINVAL
+    assert F(xa, 1024, 4, null, 64, 1, 0, ya, null, 0, null) == B.EINVAL
+    assert F(xa, 1024, 4, sl, 64, 0, 0, ya, null, 0, null) == B.EINVAL
+    assert F(xa, 1024, 4, sl, 64, 5, 0, ya, null, 0, null) == B.EINVAL
+    assert F(xa, 1024, 4, ctypes.c_void_p((5 << 32) + 8), 64, 1, 0, ya, null, 0, null) == B.ESTRIDE
+    assert F(xa, 1024, 4, sl, 40, 1, 0, ya, null, 0, null) == B.ESTRIDE
+    assert F(xa, 1024, 4, sl, 1 << 30, 2, 0, ya, null, 0, null) == B.ESHAPE
+    assert F(xa, 1024, 4, sl, 4096, 2, 0, ya, ctypes.c_void_p((5 << 32) + 4096), 64, null) == B.EINVAL
+    assert F(xa, 1024, 4, sl, 4096, 2, 0, ctypes.c_void_p((5 << 32) + 64), null, 0, null) == B.EINVAL
     bad = ctypes.c_int64(0)
     assert lib.bsfp8_make_twin(null, 1, 33, 32, null, null, null, ctypes.byref(bad), null) == B.ESHAPE
     assert lib.bsfp8_pad_k_weight(null, null, 1, 32, 64, 48, null, null, null) == B.ESHAPE

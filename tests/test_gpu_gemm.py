@@ -387,8 +387,18 @@ def test_read_floor_reads_and_writes_in_bounds():
     B.bsfp8_read_floor(t, nwg=256, sink=sink, out=out)
     B.bsfp8_read_floor(t, nwg=256, sink=sink, slab=slab, slab_groups=2)        # 48 KB per group
     B.bsfp8_read_floor(t, nbytes=0, nwg=256, sink=sink, slab=slab[:6912], slab_groups=1)
+    # the slab spread over the steps of the share: one step (256 workgroups), six steps of twelve
+    # loads per wave (16 workgroups), no share at all
+    B.bsfp8_read_floor(t, nwg=256, sink=sink, slab=slab, slab_groups=2, interleave=True)
+    B.bsfp8_read_floor(t, nwg=16, sink=sink[:16], slab=slab, slab_groups=2, interleave=True)
+    B.bsfp8_read_floor(t, nbytes=0, nwg=256, sink=sink, slab=slab[:6912], slab_groups=1, interleave=True)
     guard[:24576].fill_(0xAB)
     B.bsfp8_read_floor(t, nwg=256, sink=sink, out=out, slab=slab, slab_groups=2)
+    torch.cuda.synchronize()
+    assert bool((sink == 7).all())
+    assert bool((out == 0).all())
+    guard[:24576].fill_(0xAB)
+    B.bsfp8_read_floor(t, nwg=16, sink=sink[:16], out=out, slab=slab, slab_groups=2, interleave=True)
     torch.cuda.synchronize()
     assert bool((sink == 7).all())
     assert bool((out == 0).all())
