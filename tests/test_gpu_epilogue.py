@@ -40,7 +40,8 @@ def _partials(seed, S_, M, L):
         blocks[0, 4, 0], blocks[0, 4, 1] = 1.0, np.float32(1.0625 / 256)
         blocks[:, 5] = 0.0                                          # saturation: 1.9 * 2^8 > 448
         blocks[0, 5, 0], blocks[0, 5, 1] = np.float32(1.9), np.float32(-1.9)
-        blocks[:, 6] *= np.float32(2.0 ** 100)                      # near the top of fp32
+        with np.errstate(over="ignore"):                            # near and past the top of
+            blocks[:, 6] *= np.float32(2.0 ** 100)                  # fp32 (some become inf)
         blocks[:, 7] = np.ldexp(np.float32(1), -149) * r.integers(-3, 4, size=(S_, 32))   # subnormals
     return blocks.reshape(S_, M, L)
 
