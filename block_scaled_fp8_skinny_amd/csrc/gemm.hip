@@ -9,20 +9,25 @@
 // Design (gfx950, wave64):
 //  * MFMA v_mfma_f32_16x16x32_bf16 with the WEIGHT as the A operand (16 rows of W) and X^T as
 //    the B operand (16 rows of X): D[n][m] holds four consecutive n per lane.
-//  * K is walked in 128-wide chunks. In a chunk each lane loads two 16-byte pieces of one weight
-//    row (k offsets 16*q and 64 + 16*q for lane group q = lane/16), i.e. a wave reads whole
-//    128-byte lines of 16 rows, straight from HBM into VGPRs.
+//  * K is walked in 128-wide chunks. In a chunk, lane (q, r) of the MFMA takes the k values
+//    16*q .. 16*q + 15 and 64 + 16*q .. 64 + 16*q + 15 of its row r (q = lane/16) in every kernel,
+//    so a chunk's four MFMAs sum the same products in the same order whichever kernel runs it.
+//  * How they arrive: the first kernels (gemm_kernel, gemm_direct_kernel) load the weight pieces
+//    in that lane order straight from HBM into VGPRs (64 contiguous bytes per row and load); the
+//    decode, paired, LDS-staged register and tile kernels read eight lanes per row (128
+//    contiguous bytes per row and load, which HBM streams about 30% faster) straight into LDS
+//    with the buffer loads' LDS mode, each lane fetching the granule that belongs in its slot of
+//    a swizzled row-major tile, and take the MFMA fragments from there.
 //  * Every global load is a raw buffer load: out-of-range offsets return zero, so masked
-//    pieces (ragged K tail, rows beyond M) need no branches, and the compiler can wait for each
-//    load individually. Dequant and MFMA of the first chunks therefore overlap the arrival of
-//    the later ones, and a multi-pass workgroup prefetches the next pass (X, exponents and
-//    weights) into registers before computing the current one.
+//    pieces (ragged K tail, rows beyond M) need no branches, and each wave waits for exactly the
+//    loads a chunk needs (the compiler's counts for VGPR loads, explicit s_waitcnt for LDS-mode
+//    loads, which complete in order). Dequant and MFMA of the first chunks therefore overlap the
+//    arrival of the later ones.
 //  * Dequant is v_cvt_scalef32_pk_bf16_fp8: 2 codes -> 2 bf16 scaled by the block factor in one
 //    instruction, exact for every code and exponent byte 0..254 (checked on the hardware).
-//  * X and the exponent bytes of a pass are staged in LDS; X is stored in MFMA fragment order
-//    and each thread writes the slot of its own lane, so every ds_write_b128 and ds_read_b128
-//    of a wave touches 1 KB of consecutive LDS (no bank conflicts). Rows at or beyond M are not
-//    written at all: they feed only MFMA output columns that are never stored.
+//  * X rows and the exponent bytes are staged in LDS in layouts whose fragment reads are free of
+//    bank conflicts. Rows at or beyond M are not loaded: they feed only MFMA output columns that
+//    are never stored.
 //  * Waves of a workgroup split the n rows (NWN) and the chunks (NWK); the NWK partial tiles are
 //    summed through LDS in ascending wave order. Workgroups may further split K (splits > 1).
 //    Their partials meet in a binary tree of pairwise combines: at each node the two partners
@@ -34,9 +39,10 @@
 //    no waiting for stores to drain.
 //  * The map chunk -> (split, pass, wave, step) depends only on the chunk index and the plan,
 //    not on K, so zero-padding K inside the same chunk count leaves every fp32 sum unchanged.
-//  * Workgroup ids are remapped so that consecutive logical tiles run on the same XCD
-//    (workgroups are dealt round-robin over the 8 XCDs): splits sharing an X slab and m-blocks
-//    sharing a weight tile hit the same L2.
+//  * Workgroup ids of the flat-grid kernels are remapped so that consecutive logical tiles run on
+//    the same XCD (workgroups are dealt round-robin over the 8 XCDs): splits sharing an X slab
+//    and m-blocks sharing a weight tile hit the same L2. The decode kernels take their tile from
+//    a three-dimensional grid instead (no index arithmetic before the first loads).
 
 #include <type_traits>
 
