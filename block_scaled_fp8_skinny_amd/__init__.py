@@ -30,6 +30,7 @@ _SIGS = {
     "bsfp8_abi_version": (_I, []),
     "bsfp8_scales_from_f32": (_I, [_P, _I64, _I64, _P, ctypes.POINTER(_I64), _P]),
     "bsfp8_make_twin": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, ctypes.POINTER(_I64), _P]),
+    "bsfp8_make_twin_async": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "bsfp8_pad_k_weight": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P]),
     "bsfp8_pad_k_input": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]),
     "bsfp8_dequant": (_I, [_P, _P, _I64, _I64, _I64, _P, _P]),
@@ -213,6 +214,33 @@ def bsfp8_make_twin(w):
     st = _check(lib().bsfp8_make_twin(_ptr(w), G, R, D, _ptr(q), _ptr(e), _ptr(ok), ctypes.byref(bad),
                                       _stream(w)), "bsfp8_make_twin")
     return Twin(st == OK, q, e, ok, bad.value)
+
+
+def bsfp8_make_twin_async(w, n_bad, q=None, e=None, ok=None):
+    """Enqueue the encoder of bf16 w [G, R, D] without waiting: returns (q, e, ok) and adds the
+    number of inexact blocks to n_bad, an int64 GPU tensor of one element that the caller zeroes
+    (the twin is exact iff the count it received is 0). q, e, ok: optional outputs of the shapes
+    bsfp8_make_twin returns (ok may be skipped with ok=False)."""
+    _need(w, torch.bfloat16, "w")
+    if w.dim() != 3:
+        raise ValueError("w must be [G, R, D]")
+    G, R, D = w.shape
+    _need(n_bad, torch.int64, "n_bad", numel=1, device=w.device)
+    if q is None:
+        q = torch.empty((G, R, D), dtype=torch.uint8, device=w.device)
+    _need(q, torch.uint8, "q", numel=G * R * D, device=w.device)
+    if e is None:
+        e = torch.empty((G, R // 32, D // 32), dtype=torch.uint8, device=w.device)
+    _need(e, torch.uint8, "e", numel=G * (R // 32) * (D // 32), device=w.device)
+    if ok is None:
+        ok = torch.empty((G, R // 32, D // 32), dtype=torch.uint8, device=w.device)
+    elif ok is False:
+        ok = None
+    else:
+        _need(ok, torch.uint8, "ok", numel=G * (R // 32) * (D // 32), device=w.device)
+    _check(lib().bsfp8_make_twin_async(_ptr(w), G, R, D, _ptr(q), _ptr(e), _ptr(ok), _ptr(n_bad), _stream(w)),
+           "bsfp8_make_twin_async")
+    return q, e, ok
 
 
 def make_twin(w):

@@ -233,6 +233,21 @@ int bsfp8_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t*
   return bad ? BSFP8_NOT_EXACT : BSFP8_OK;
 }
 
+int bsfp8_make_twin_async(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t* q_out,
+                          uint8_t* e_out, uint8_t* block_ok, int64_t* n_bad_dev, void* stream) {
+  if (G < 0 || R < 0 || D < 0 || R % 32 || D % 32) return BSFP8_ESHAPE;
+  if (!n_bad_dev || reinterpret_cast<uintptr_t>(n_bad_dev) % 8) return BSFP8_EINVAL;
+  if (G * R * D == 0) return BSFP8_OK;
+  if (!w || !q_out || !e_out) return BSFP8_EINVAL;
+  if (!aligned16(w) || !aligned16(q_out)) return BSFP8_ESTRIDE;
+  {
+    const size_t n = (size_t)G * R * D, nb = n / 1024;
+    if (outputs_alias({{q_out, n}, {e_out, nb}, {block_ok, nb}, {n_bad_dev, 8}}, {{w, n * 2}})) return BSFP8_EINVAL;
+  }
+  return launch_make_twin(w, G, R, D, q_out, e_out, block_ok, reinterpret_cast<unsigned long long*>(n_bad_dev),
+                          as_stream(stream));
+}
+
 int bsfp8_make_twin_row32(const uint16_t* w, int64_t G, int64_t N, int64_t K, uint8_t* q_out, uint8_t* e_out,
                           uint8_t* block_ok, int64_t* n_bad_out, void* stream) {
   if (G < 0 || N < 0 || K < 0 || K % 32) return BSFP8_ESHAPE;

@@ -98,6 +98,19 @@ BSFP8_API int bsfp8_scales_from_f32(const float* scales, int64_t rows, int64_t c
 BSFP8_API int bsfp8_make_twin(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t* q_out,
                     uint8_t* e_out, uint8_t* block_ok, int64_t* n_bad_out, void* stream);
 
+/* bsfp8_make_twin without the synchronisation, for loading many layers: the encoder is enqueued
+ * on `stream` and the call returns at once; the verdict stays on the device. Same rule, outputs
+ * and page as bsfp8_make_twin.
+ *   n_bad_dev: device int64_t, 8-byte aligned: the number of blocks that are not exact is ADDED to
+ *              it (the caller zeroes it first; one counter may gather several layers). The twin
+ *              is exact iff the count it received is 0.
+ * Allocates nothing and does not wait, so it may be captured in a graph (zero the counter with a
+ * kernel, not a memset node, before each replay that should count from zero). Returns BSFP8_OK once
+ * enqueued, BSFP8_ESHAPE / ESTRIDE / EINVAL as bsfp8_make_twin (EINVAL also for a missing or
+ * misaligned n_bad_dev, or one that overlaps w or an output), BSFP8_EHIP on a launch failure. */
+BSFP8_API int bsfp8_make_twin_async(const uint16_t* w, int64_t G, int64_t R, int64_t D, uint8_t* q_out,
+                                    uint8_t* e_out, uint8_t* block_ok, int64_t* n_bad_dev, void* stream);
+
 /* bf16 weight -> e4m3 twin with one exponent per row and 32 columns, accepted only when it rebuilds
  * the weight bit for bit. Page "recipes/docker-images/mia-tp4/docs/tp4-adapters.md", row
  * draft_main_proj: each rank keeps its output columns as e4m3 with per-(row, 32-column)

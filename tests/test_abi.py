@@ -176,6 +176,17 @@ def test_argument_checks_return_before_gpu_work(lib):
     assert F(xa, 1024, 4, sl, 4096, 2, 0, ctypes.c_void_p((5 << 32) + 64), null, 0, null) == B.EINVAL
     bad = ctypes.c_int64(0)
     assert lib.bsfp8_make_twin(null, 1, 33, 32, null, null, null, ctypes.byref(bad), null) == B.ESHAPE
+    # the asynchronous encoder: a device counter, 8-byte aligned, outside w and the outputs
+    TA = lib.bsfp8_make_twin_async
+    wa, qa, ea = ctypes.c_void_p(6 << 32), ctypes.c_void_p(7 << 32), ctypes.c_void_p(8 << 32)
+    cnt = ctypes.c_void_p(9 << 32)
+    assert TA(wa, 1, 33, 32, qa, ea, null, cnt, null) == B.ESHAPE
+    assert TA(wa, 1, 32, 32, qa, ea, null, null, null) == B.EINVAL
+    assert TA(wa, 1, 32, 32, qa, ea, null, ctypes.c_void_p((9 << 32) + 4), null) == B.EINVAL
+    assert TA(wa, 1, 32, 32, qa, ea, null, ctypes.c_void_p((6 << 32) + 64), null) == B.EINVAL   # inside w
+    assert TA(wa, 1, 32, 32, qa, ea, null, ctypes.c_void_p((7 << 32) + 8), null) == B.EINVAL    # inside q
+    assert TA(ctypes.c_void_p((6 << 32) + 8), 1, 32, 32, qa, ea, null, cnt, null) == B.ESTRIDE
+    assert TA(wa, 0, 32, 32, qa, ea, null, cnt, null) == B.OK                                   # nothing to do
     assert lib.bsfp8_pad_k_weight(null, null, 1, 32, 64, 48, null, null, null) == B.ESHAPE
     assert lib.bsfp8_pad_k_input(null, 10, 1, 1, 32, 64, null, null) == B.ESTRIDE
     assert lib.bsfp8_dequant(null, null, 1, 32, 40, null, null) == B.ESHAPE

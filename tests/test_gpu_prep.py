@@ -66,6 +66,55 @@ def test_make_twin_perturbed_and_random_weights_bitwise():
     assert np.array_equal(_twin_gpu(wp)[3].astype(bool), ~mask)
 
 
+def test_make_twin_async_equals_the_synchronous_call_and_replays_in_a_graph():
+    """The asynchronous encoder writes the twin bytes, exponents and block mask of the
+    synchronous call, adds its inexact-block count to the caller's device counter (so one counter
+    gathers several layers), and replays in a graph with the counter cleared by a kernel."""
+    src = S.twin_source(3010, G=2, R=256, D=512)
+    w = oracle.dequant_bf16(src["q"], src["e"])
+    wp, mask = S.perturb_one_element(w, S.rng(3011), 0.1)
+    ref, refp = oracle.make_twin(w), oracle.make_twin(wp)
+    wt, wpt = to_gpu_bf16(w), to_gpu_bf16(wp)
+    n_bad = torch.zeros(1, dtype=torch.int64, device="cuda")
+    q, e, ok = B.bsfp8_make_twin_async(wt, n_bad)
+    torch.cuda.synchronize()
+    assert int(n_bad.item()) == 0
+    assert np.array_equal(q.cpu().numpy(), ref.q) and np.array_equal(e.cpu().numpy(), ref.e)
+    assert np.array_equal(ok.cpu().numpy(), ref.ok)
+    qp, ep, okp = B.bsfp8_make_twin_async(wpt, n_bad)
+    q2, e2, _ = B.bsfp8_make_twin_async(wpt, n_bad, ok=False)        # no mask; the count adds up
+    torch.cuda.synchronize()
+    nb = int((refp.ok == 0).sum())
+    assert nb == int(mask.sum()) > 0 and int(n_bad.item()) == 2 * nb
+    assert np.array_equal(qp.cpu().numpy(), refp.q) and np.array_equal(ep.cpu().numpy(), refp.e)
+    assert np.array_equal(okp.cpu().numpy(), refp.ok)
+    assert torch.equal(q2, qp) and torch.equal(e2, ep)
+    # in a graph: two layers, one counter each, cleared inside the graph by a kernel
+    cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+    outs = [(torch.empty_like(q), torch.empty_like(e), torch.empty_like(ok)) for _ in range(2)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            cnt.zero_()
+            for i, ww in enumerate((wt, wpt)):
+                B.bsfp8_make_twin_async(ww, cnt[i:i + 1], *outs[i])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            for t in o:
+                t.fill_(0xAB)
+        cnt.fill_(12345)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert cnt.tolist() == [0, nb], rep
+        assert torch.equal(outs[0][0], q) and torch.equal(outs[0][1], e) and torch.equal(outs[0][2], ok)
+        assert torch.equal(outs[1][0], qp) and torch.equal(outs[1][1], ep) and torch.equal(outs[1][2], okp)
+
+
 def test_make_twin_edge_blocks():
     w = np.zeros((1, 64, 96), dtype=np.uint16)
     w[0, 0, 40] = 0x8000                  # block (0,1): only a negative zero
