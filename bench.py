@@ -10,6 +10,8 @@ weight copies so that the cache is cold, captured graphs, interleaved rounds):
     together hold at least 512 MiB (twice the 256 MiB Infinity Cache), whatever --steps says;
   * a step is one GEMM call on each of the C copies, in order (the pages' ms/step over their 43
     layers), captured once in a HIP graph;
+  * activations are cold too: call i of a step reads activation copy i (the same values), as a
+    layer reads the previous kernel's output rather than a buffer left in L2 by the call before;
   * rounds: every configuration's step graph, and the plain-read floor graphs, replayed in turn
     between HIP events on the replay stream (the headline: exactly --steps steps per round, each
     timed region bracketed by synchronisation); at least 5 rounds; each figure is the median over
@@ -190,7 +192,8 @@ def padded_weight_set(torch, B, src, name):
 def twin_weight_set(torch, B, seed, n_layers=TWIN_LAYERS, reps=5):
     """The padded-TP3 twin workload: n_layers exact bf16 layers [4, 1024, 4096] (each 32x32 block
     e4m3 * 2^e, e - 127 in [115, 123] - 127, rebuilt from seeded codes by bsfp8_dequant), encoded by
-    bsfp8_make_twin (timed per layer, `reps` rounds), whose twins are the GEMM's weight copies."""
+    bsfp8_make_twin (each call timed, `reps` rounds), whose twins are the GEMM's weight copies, and by
+    bsfp8_make_twin_async in one graph over all layers (`reps` timed replays: the encoder's rate)."""
     name = "wo_a_tp3"
     src = random_weight_set(torch, name, seed, n=n_layers)
     layers = [B.bsfp8_dequant(q, e) for q, e in zip(src.q, src.e)]
@@ -222,7 +225,28 @@ def twin_weight_set(torch, B, seed, n_layers=TWIN_LAYERS, reps=5):
         bufs.append(b)
     same = all(torch.equal(t.q, q0) and torch.equal(t.e, e0) for t, q0, e0 in zip(twins, src.q, src.e))
     nbytes = G * N * K * 2 + G * N * K + 2 * G * (N // 32) * (K // 32)   # read bf16; write codes, exps, ok
-    us = statistics.median(round_means)
+    sync_us = statistics.median(round_means)
+    # the encoder itself: bsfp8_make_twin_async (no allocation, no synchronisation) on every layer
+    # in one graph, each into its own twin buffers and inexact-block counter, `reps` timed replays
+    aq = [torch.empty_like(t.q) for t in twins]
+    ae = [torch.empty_like(t.e) for t in twins]
+    aok = [torch.empty_like(t.ok) for t in twins]
+    cnt = torch.zeros(n_layers, dtype=torch.int64, device="cuda")
+    ga = capture(torch, lambda i: B.bsfp8_make_twin_async(layers[i], cnt[i:i + 1], aq[i], ae[i], aok[i]), n_layers)
+    ga.replay()
+    torch.cuda.synchronize()
+    async_same = (int(cnt.count_nonzero().item()) == n_layers - accepted and
+                  all(torch.equal(a, t.q) and torch.equal(b, t.e) for a, b, t in zip(aq, ae, twins)))
+    tw_rounds = []
+    for rd in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        ga.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        tw_rounds.append(1e3 * a.elapsed_time(b) / n_layers)
+    us = statistics.median(tw_rounds)
+    del ga, aq, ae, aok
     # the standalone dequantisation (the twin back to bf16, into the layers' own buffers, so every
     # call reads and writes its own cold copy): one graph of n_layers calls, `reps` timed replays
     g = capture(torch, lambda i: B.bsfp8_dequant(twins[i].q, twins[i].e, out=layers[i]), n_layers)
@@ -266,10 +290,14 @@ def twin_weight_set(torch, B, seed, n_layers=TWIN_LAYERS, reps=5):
     del g, gf
     twin_entry = {
         "label": "d4 make_twin", "workload": "wo_a_tp3", "path": "make_twin",
-        "desc": f"make_twin of {n_layers} exact bf16 layers [{G},{N},{K}] (synchronous prepare call: "
-                f"counter clear, encoder kernel, verdict read back), GPU span per layer",
+        "desc": f"twin encoder on {n_layers} exact bf16 layers [{G},{N},{K}]: bsfp8_make_twin_async, one graph "
+                f"of {n_layers} calls, each into its own buffers and counter; sync_call_us_per_layer = the "
+                f"synchronous bsfp8_make_twin (counter allocated and cleared, encoder, verdict read back), "
+                f"GPU span per call",
         "layers": n_layers, "accepted": accepted, "twins_equal_source": bool(same),
-        "us_per_layer": us, "us_per_layer_rounds": round_means, "bytes_per_layer": nbytes,
+        "async_equals_sync": bool(async_same),
+        "us_per_layer": us, "us_per_layer_rounds": [round(v, 3) for v in tw_rounds], "bytes_per_layer": nbytes,
+        "sync_call_us_per_layer": round(sync_us, 3), "sync_call_us_per_layer_rounds": round_means,
         "algorithmic_gbs": nbytes / (us * 1e3),
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e3), 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(nbytes / (us * 1e3) / HBM_PEAK_GBS, 4)},
@@ -352,29 +380,31 @@ def algorithmic_bytes(name, M, path="bf16"):
     return w, e, x, y
 
 
-def make_call(torch, B, ws_set, name, M, split_k, path, x, out):
-    """The per-call function over the copies of ws_set, its plan report and its buffers."""
+def make_call(torch, B, ws_set, name, M, split_k, path, xs, out):
+    """The per-call function over the copies of ws_set (call i reads weight copy i and activation
+    copy i of xs), its plan report and its buffers."""
     G, N, K, _ = shape_of(name)
     od = WORKLOADS[name][5]
-    C = len(ws_set)
+    C, X = len(ws_set), len(xs)
     if path == "mx":
-        xq, xs = B.bsfp8_quantize_mx(x)
+        xm = [B.bsfp8_quantize_mx(x) for x in xs]
         plan = {"mx_cfg": B.bsfp8_mx_plan(M, G, N), **B.bsfp8_mx_config_info(B.bsfp8_mx_plan(M, G, N))}
-        return (lambda i: B.bsfp8_gemm_mx(xq, xs, ws_set.q[i % C], ws_set.e[i % C], out=out, out_dtype=od)), plan
+        return (lambda i: B.bsfp8_gemm_mx(xm[i % X][0], xm[i % X][1], ws_set.q[i % C], ws_set.e[i % C], out=out,
+                                          out_dtype=od)), plan
     if name in ROW_SCALE_WORKLOADS:
         ws = B.workspace_row32(M, G, N, K, split_k)
-        return (lambda i: B.bsfp8_gemm_row32(x, ws_set.q[i % C], ws_set.e[i % C], split_k=split_k, ws=ws, out=out,
-                                             out_dtype=od)), {"row_scale_twin": True}
+        return (lambda i: B.bsfp8_gemm_row32(xs[i % X], ws_set.q[i % C], ws_set.e[i % C], split_k=split_k, ws=ws,
+                                             out=out, out_dtype=od)), {"row_scale_twin": True}
     if path == "mxfp8":
         plan = B.bsfp8_plan_info(M, G, N, K, split_k, path=3)
         ws = B.workspace_mxfp8(M, G, N, K, split_k)
         yq = torch.empty((M, G * N), dtype=torch.uint8, device="cuda")
         ys = torch.empty((M, G * N // 32), dtype=torch.uint8, device="cuda")
-        return (lambda i: B.bsfp8_gemm_mxfp8(x, ws_set.q[i % C], ws_set.e[i % C], split_k=split_k, ws=ws, yq=yq,
-                                             ys=ys)), plan
+        return (lambda i: B.bsfp8_gemm_mxfp8(xs[i % X], ws_set.q[i % C], ws_set.e[i % C], split_k=split_k, ws=ws,
+                                             yq=yq, ys=ys)), plan
     plan = B.bsfp8_plan_info(M, G, N, K, split_k)
     ws = B.workspace(M, G, N, K, split_k)
-    return (lambda i: B.bsfp8_gemm(x, ws_set.q[i % C], ws_set.e[i % C], split_k=split_k, ws=ws, out=out,
+    return (lambda i: B.bsfp8_gemm(xs[i % X], ws_set.q[i % C], ws_set.e[i % C], split_k=split_k, ws=ws, out=out,
                                    out_dtype=od)), plan
 
 
@@ -591,11 +621,15 @@ def run(args):
     for (label, name, M, split_k) in configs:
         G, N, K, _ = shape_of(name)
         ws_set = sets[WEIGHT_SET[name]]
-        x = activations(torch, M, G, K, 7100 + M)
+        # one activation copy per weight copy: a layer's input is the previous kernel's output, not
+        # a buffer left in L2 by the call before (with one shared copy, 96 KB of activations stayed
+        # in L2 across calls or not depending on where the allocator put them: 4.09 or 4.22 us)
+        C = len(ws_set)
+        x0 = activations(torch, M, G, K, 7100 + M)
+        xs = [x0] + [x0.clone() for _ in range(C - 1)]
         od = torch.float32 if WORKLOADS[name][5] == "f32" else torch.bfloat16
         out = torch.empty((M, G, N), dtype=od, device="cuda")
-        fn, plan = make_call(torch, B, ws_set, name, M, split_k, path, x, out)
-        C = len(ws_set)
+        fn, plan = make_call(torch, B, ws_set, name, M, split_k, path, xs, out)
         for i in range(C):                          # eager warm-up over every copy
             fn(i)
         torch.cuda.synchronize()
@@ -603,7 +637,7 @@ def run(args):
         reps = args.steps if (label, name, M, split_k) == headline else args.reps
         timed.append(Timed((label, name, M, split_k), g, C, reps))
         meta.append((label, name, M, split_k, plan, ws_set))
-        keep.append((x, out, fn))                   # fn holds the workspace the graph writes
+        keep.append((xs, out, fn))                  # fn holds the workspace the graph writes
     # plain-read floors and a bare launch over each weight set's copies
     floors = {}
     sink = torch.empty(FLOOR_WGS, dtype=torch.int32, device="cuda")
@@ -631,7 +665,8 @@ def run(args):
     # floor workgroup also reading a slab of the bytes a workgroup of the plan reads beyond its
     # share of the weights (the activation rows of its m-block, K wide, and the weight rows that
     # the plan's other m-blocks read again), spread over the 256 floor workgroups; those bytes are
-    # cache-resident after their first reads, as the activations and re-read weights are. The
+    # cache-resident after their first reads in a call, as the activations and re-read weights
+    # are, and every call reads its own slab copy, as every GEMM call its own activations. The
     # slab loads are spread over the steps of the weight share (each step's before its weight
     # loads, as the GEMMs issue each chunk's activations before its weights): with one step (every
     # shape below the LM head) that is the slab first, and on the LM head's 640 KB shares it was
@@ -653,10 +688,10 @@ def run(args):
         if key in xrw_floors:
             continue
         yb = torch.empty(ob, dtype=torch.uint8, device="cuda")
-        slab = torch.zeros(groups * sb, dtype=torch.uint8, device="cuda")
-        keep.extend([yb, slab])
-        g = capture(torch, lambda i, s=ws_set, yb=yb, slab=slab, gr=groups: B.bsfp8_read_floor(
-            s.bufs[i], nwg=FLOOR_WGS, sink=sink, out=yb, slab=slab, slab_groups=gr, interleave=True), len(ws_set))
+        slabs = [torch.zeros(groups * sb, dtype=torch.uint8, device="cuda") for _ in range(len(ws_set))]
+        keep.extend([yb, slabs])
+        g = capture(torch, lambda i, s=ws_set, yb=yb, sl=slabs, gr=groups: B.bsfp8_read_floor(
+            s.bufs[i], nwg=FLOOR_WGS, sink=sink, out=yb, slab=sl[i], slab_groups=gr, interleave=True), len(ws_set))
         xrw_floors[key] = Timed(("floor_xrw",) + key, g, len(ws_set), args.reps)
     every = (timed + [t for pair in floors.values() for t in pair] + list(rw_floors.values()) +
              list(xrw_floors.values()))
