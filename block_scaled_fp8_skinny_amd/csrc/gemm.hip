@@ -1700,9 +1700,11 @@ gemm_slab_kernel(KParams p) {
 // (K = 128 * NWK * CW): every chunk is then in range and no load, factor or output needs a range
 // test, which shortens the path from the arguments to the first loads (each instruction there
 // delays the whole stream) and the epilogue. Their sums are those of the general instance.
-template <int NWK, int CP, bool RG, bool FULL = false>
+// WF weight chunks (at most two, the first pair's) are issued before the X rows, the rest after.
+template <int NWK, int CP, bool RG, bool FULL = false, int WF = 0>
 __global__ void __launch_bounds__(WAVE * NWK)
 gemm_pair_kernel(KParams p) {
+  static_assert(WF >= 0 && WF <= 2, "only the first pair's weight chunks go before the X rows");
   constexpr int CW = 2 * CP;                        // chunks per wave
   constexpr int XR = 8;                             // rows of X per workgroup
   constexpr int XS = CW * 16;                       // granules of one X row slice
@@ -1748,6 +1750,19 @@ gemm_pair_kernel(KParams p) {
     const int c = cw0 + lane;
     lds_load4(re, lds_addr(ew), lane < CW && (FULL || c < c_end) ? (uint32_t)(erow * KB + c * 4) : OOB);
   }
+  // (3) weight chunks, one load each: lane l fills row R = l / 8, slot l % 8 with granule
+  //     (l % 8) ^ (R / 2); the first WF of them before the X rows
+  const int wR = lane >> 3;
+  const int wgsrc = (lane & 7) ^ (wR >> 1);
+  const uint32_t qrow = (uint32_t)(g * N + n0 + wR) * (uint32_t)K;
+  auto wload = [&](int cl) {
+    const int c = cw0 + cl;
+    const uint32_t off = qrow + (uint32_t)(c * KCH + wgsrc * 16);
+    const bool ok = (FULL || c < c_end) && (!RG || c * KCH + wgsrc * 16 < K);
+    lds_load16_stream(rq, lds_addr(ww + cl * WT), ok ? off : OOB);
+  };
+#pragma unroll
+  for (int cl = 0; cl < WF; ++cl) wload(cl);
   // (2) X rows m0 .. m0 + 7 over the wave's chunks: load i fills slots 64i .. 64i + 63 of the rows'
   //     slices (row-major); the lane fetches the granule that belongs in its slot. Loads whose rows
   //     all lie at or beyond M are skipped (those rows feed only discarded columns).
@@ -1763,20 +1778,8 @@ gemm_pair_kernel(KParams p) {
     const bool ok = m < M && (FULL || cw0 + cl < c_end) && (!RG || k < K);
     if (m0 + (i * 64) / XS < M) lds_load16(rx, lds_addr(xw + i * 64), ok ? off : OOB);
   }
-  // (3) weight chunks, one load each: lane l fills row R = l / 8, slot l % 8 with granule
-  //     (l % 8) ^ (R / 2)
-  {
-    const int R = lane >> 3;
-    const int gsrc = (lane & 7) ^ (R >> 1);
-    const uint32_t qrow = (uint32_t)(g * N + n0 + R) * (uint32_t)K;
 #pragma unroll
-    for (int cl = 0; cl < CW; ++cl) {
-      const int c = cw0 + cl;
-      const uint32_t off = qrow + (uint32_t)(c * KCH + gsrc * 16);
-      const bool ok = (FULL || c < c_end) && (!RG || c * KCH + gsrc * 16 < K);
-      lds_load16_stream(rq, lds_addr(ww + cl * WT), ok ? off : OOB);
-    }
-  }
+  for (int cl = WF; cl < CW; ++cl) wload(cl);
 
   // (4) pairs, each once its own loads (and everything issued before them) have landed
   pin_epilogue_args(p);                             // every load is issued
@@ -1918,6 +1921,7 @@ struct Config {
 #define SCFG(MT, NT, NWM, NWN, NWK, S) {MT, NT, NWM, NWN, NWK, S, gemm_slab_kernel<MT, NT, NWM, NWN, NWK, S>, SLAB}
 #define PCFG(NWK, CP, RG) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, RG>, PAIR, 0, 8, RG}
 #define PFCFG(NWK, CP) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, false, true>, PAIR_FULL, 0, 8, 0}
+#define PFWCFG(NWK, CP, WF) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, false, true, WF>, PAIR_FULL, 0, 8, 0}
 #define RDCFG(MT, NT, NWK, CW, D) {MT, NT, 1, 1, NWK, CW, gemm_rows_dma_kernel<MT, NT, NWK, CW, D>, ROWS_DMA}
 
 const Config kConfigs[] = {
@@ -2036,6 +2040,7 @@ const Config kConfigs[] = {
     RDCFG(1, 1, 8, 4, 2),     // 106 rows, LDS-mode: 16 x 16 tile, 8 waves along K x 4 chunks
     RDCFG(1, 1, 4, 8, 2),     // 107 rows, LDS-mode: 16 x 16 tile, 4 waves along K x 8 chunks
     RDCFG(2, 1, 4, 8, 2),     // 108 rows, LDS-mode: 32 x 16 tile, 4 waves along K x 8 chunks
+    PFWCFG(8, 2, 2),          // 109 pair, whole range (93) with the first pair's weights issued before X
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2131,7 +2136,8 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
 //    output's fp32 sum is then the same ascending chain of chunks and MFMAs whatever the tile, so
 //    a row's result does not depend on how many rows share the call.
 //  * Decode rows (at most 8) over exactly 32 chunks on at most 256 eight-row tiles (wo_a at G = 2):
-//    the paired decode kernel on the whole range, one workgroup per CU.
+//    the paired decode kernel on the whole range, one workgroup per CU (up to 3 rows with the
+//    first weight chunks issued before the X rows).
 //  * Other decode rows (at most 8, or 16 with a long K): the decode kernel (everything streamed
 //    into LDS, 8 rows of X per workgroup); when K is not whole 128-wide chunks its ragged
 //    instances, which read zeros past K, so K zero-padded to whole chunks (576 -> 640) gives
@@ -2155,8 +2161,10 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool al
     else cfg = n64 ? 10 : 16;
   } else if (allow_pair && s.M <= 8 && s.K == 32 * KCH && split_k <= 1 && (long long)s.G * s.N / 8 <= 256) {
     // decode rows on at most 256 eight-row tiles over exactly 32 chunks: the paired kernel on the
-    // whole range (one workgroup per CU, every MFMA computing two chunks)
-    cfg = 93;
+    // whole range (one workgroup per CU, every MFMA computing two chunks). Up to 3 rows the first
+    // pair's weight chunks go out before the X rows (3.77 against 3.87 us at 2 rows); from 4 rows
+    // on the X rows go first (4.25 against 4.41 us at 6 rows). The sums are the same either way.
+    cfg = s.M <= 3 ? 109 : 93;
     cps = kchunks;
   } else if (s.M <= 8 || (s.M <= 16 && kchunks > 8)) {
     // decode kernel (8 rows of X per workgroup); for K that is not whole chunks its ragged
