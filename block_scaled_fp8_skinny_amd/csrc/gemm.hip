@@ -1701,10 +1701,14 @@ gemm_slab_kernel(KParams p) {
 // test, which shortens the path from the arguments to the first loads (each instruction there
 // delays the whole stream) and the epilogue. Their sums are those of the general instance.
 // WF weight chunks (at most two, the first pair's) are issued before the X rows, the rest after.
-template <int NWK, int CP, bool RG, bool FULL = false, int WF = 0>
+// XG (two groups, one m-block, one split): the workgroups of group 0 run on XCDs 0..3 and those of
+// group 1 on XCDs 4..7 (the hardware deals workgroups to the 8 XCDs by linear index mod 8), so each
+// XCD's L2 fetches the activation rows of one group instead of both.
+template <int NWK, int CP, bool RG, bool FULL = false, int WF = 0, bool XG = false>
 __global__ void __launch_bounds__(WAVE * NWK)
 gemm_pair_kernel(KParams p) {
   static_assert(WF >= 0 && WF <= 2, "only the first pair's weight chunks go before the X rows");
+  static_assert(!XG || FULL, "XCD grouping: the whole-range instances (one split)");
   constexpr int CW = 2 * CP;                        // chunks per wave
   constexpr int XR = 8;                             // rows of X per workgroup
   constexpr int XS = CW * 16;                       // granules of one X row slice
@@ -1722,7 +1726,13 @@ gemm_pair_kernel(KParams p) {
   const int lane = threadIdx.x & 63, wk = threadIdx.x >> 6;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  const Tile tl = tile_of_grid(p);
+  Tile tl = tile_of_grid(p);
+  if constexpr (XG) {
+    // linear index L = x + y * nblocks over nblocks x 2 workgroups: XCD L % 8, slot L / 8
+    const int L = (int)blockIdx.x + (int)blockIdx.y * (int)gridDim.x;
+    tl.g = (L & 7) >> 2;
+    tl.nb = (L & 3) + ((L >> 3) << 2);
+  }
   const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
 
   const int K = p.K, M = p.M, N = p.N, G = p.G;
@@ -1910,6 +1920,7 @@ struct Config {
   int row_scales = 0;                    // 1: exponents per weight row and 32 columns
   int TR = 16;                           // DECODE: real weight rows per 16-row MFMA tile (8 or 16)
   int ragged = 0;                        // DECODE: takes K that is not a multiple of 128
+  int xg = 0;                            // PAIR_FULL: one group per half of the XCDs (G = 2 only)
 };
 
 #define CFG(MT, NT, NWN, NWK, CW) {MT, NT, 1, NWN, NWK, CW, gemm_kernel<MT, NT, NWN, NWK, CW>, STAGED}
@@ -1922,6 +1933,7 @@ struct Config {
 #define PCFG(NWK, CP, RG) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, RG>, PAIR, 0, 8, RG}
 #define PFCFG(NWK, CP) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, false, true>, PAIR_FULL, 0, 8, 0}
 #define PFWCFG(NWK, CP, WF) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, false, true, WF>, PAIR_FULL, 0, 8, 0}
+#define PFXCFG(NWK, CP, WF) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, false, true, WF, true>, PAIR_FULL, 0, 8, 0, 1}
 #define RDCFG(MT, NT, NWK, CW, D) {MT, NT, 1, 1, NWK, CW, gemm_rows_dma_kernel<MT, NT, NWK, CW, D>, ROWS_DMA}
 
 const Config kConfigs[] = {
@@ -2041,6 +2053,8 @@ const Config kConfigs[] = {
     RDCFG(1, 1, 4, 8, 2),     // 107 rows, LDS-mode: 16 x 16 tile, 4 waves along K x 8 chunks
     RDCFG(2, 1, 4, 8, 2),     // 108 rows, LDS-mode: 32 x 16 tile, 4 waves along K x 8 chunks
     PFWCFG(8, 2, 2),          // 109 pair, whole range (93) with the first pair's weights issued before X
+    PFXCFG(8, 2, 0),          // 110 pair, whole range (93), one group per XCD half (G = 2 only)
+    PFXCFG(8, 2, 2),          // 111 pair, whole range (109), one group per XCD half (G = 2 only)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2111,6 +2125,7 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   if (p.splits > 64) return BSFP8_EINVAL;
   p.mblocks = (s.M + p.BM - 1) / p.BM;
   p.nblocks = s.N / p.NB;
+  if (c.xg && (s.G != 2 || p.nblocks % 4 != 0)) return BSFP8_EINVAL;   // its tile map needs both
   if (c.kind == TILE) {
     // fp32 partials [splits][M][G][N], summed by the reduce kernel
     if (p.splits > 1) p.ws_bytes = (size_t)p.splits * s.M * s.G * s.N * 4;
@@ -2137,7 +2152,8 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
 //    a row's result does not depend on how many rows share the call.
 //  * Decode rows (at most 8) over exactly 32 chunks on at most 256 eight-row tiles (wo_a at G = 2):
 //    the paired decode kernel on the whole range, one workgroup per CU (up to 3 rows with the
-//    first weight chunks issued before the X rows).
+//    first weight chunks issued before the X rows; with two groups from 3 rows on, each group on
+//    its own half of the XCDs).
 //  * Other decode rows (at most 8, or 16 with a long K): the decode kernel (everything streamed
 //    into LDS, 8 rows of X per workgroup); when K is not whole 128-wide chunks its ragged
 //    instances, which read zeros past K, so K zero-padded to whole chunks (576 -> 640) gives
@@ -2163,8 +2179,12 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool al
     // decode rows on at most 256 eight-row tiles over exactly 32 chunks: the paired kernel on the
     // whole range (one workgroup per CU, every MFMA computing two chunks). Up to 3 rows the first
     // pair's weight chunks go out before the X rows (3.77 against 3.87 us at 2 rows); from 4 rows
-    // on the X rows go first (4.25 against 4.41 us at 6 rows). The sums are the same either way.
-    cfg = s.M <= 3 ? 109 : 93;
+    // on the X rows go first (4.25 against 4.41 us at 6 rows). With two groups from 3 rows on,
+    // each group's workgroups run on their own four XCDs (4.16 against 4.26 us at 6 rows, 4.06
+    // against 4.16 at 4; at 2 rows 3.82 against 3.76, so not there). The sums are the same in
+    // every variant.
+    const bool xg = s.G == 2 && (s.N / 8) % 4 == 0;
+    cfg = s.M <= 2 ? 109 : s.M <= 3 ? (xg ? 111 : 109) : (xg ? 110 : 93);
     cps = kchunks;
   } else if (s.M <= 8 || (s.M <= 16 && kchunks > 8)) {
     // decode kernel (8 rows of X per workgroup); for K that is not whole chunks its ragged
