@@ -404,7 +404,7 @@ def bsfp8_config_info(cfg):
     out = (_I * 8)()
     _check(lib().bsfp8_config_info(cfg, out), "bsfp8_config_info")
     return dict(BM=out[0], NB=out[1], threads=out[2], CW=out[3], NWN=out[4], NWK=out[5], direct=out[6] in (1, 2, 4),
-                kind=out[6], row_scales=out[7])
+                kind=out[6], row_scales=out[7] & 1, xcds_per_group=out[7] >> 8)
 
 
 def bsfp8_plan_info(M, G, N, K, split_k=0, path=2):

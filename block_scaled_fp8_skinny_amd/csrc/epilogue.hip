@@ -317,7 +317,7 @@ int launch_decode_mxfp8(const GemmShape& s, const GemmPlan& p, const uint16_t* x
   int info[8];
   if (gemm_config_info(p.cfg, info) != BSFP8_OK) return BSFP8_EINVAL;
   const int BM = info[0], NB = info[1], CW = info[3], NWN = info[4], NWK = info[5], kind = info[6];
-  if (kind != 4 || info[7] != 0 || BM != 8 || NB != 16 || NWN != 1 || p.splits != 1) return BSFP8_EINVAL;
+  if (kind != 4 || (info[7] & 1) != 0 || BM != 8 || NB != 16 || NWN != 1 || p.splits != 1) return BSFP8_EINVAL;
   if (s.K % KCH != 0 || s.N % 32 != 0 || p.kchunks > NWK * CW) return BSFP8_EINVAL;
   void (*fn)(DecodeMxParams);
   if (NWK == 8 && CW == 4) fn = decode_mxfp8_kernel<8, 4>;

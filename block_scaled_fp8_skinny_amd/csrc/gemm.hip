@@ -1184,9 +1184,13 @@ gemm_tile_kernel(KParams p) {
 // TR = real weight rows per 16-row MFMA tile: with TR = 8 a workgroup holds half as many weight
 // rows, so a long K range still fits its LDS in one pass; the MFMA's rows 8..15 then repeat rows
 // 0..7 and their outputs are not stored.
-template <int NT, int NWN, int NWK, int CW, int XR, int RS, int TR, bool RG = false>
+// XGP > 0 (G = 8 / XGP groups): the workgroups of group g run on XCDs XGP*g .. XGP*g + XGP - 1 (the
+// hardware deals workgroups to the 8 XCDs by linear index mod 8), so each XCD's L2 fetches the
+// activation rows of one group instead of all of them.
+template <int NT, int NWN, int NWK, int CW, int XR, int RS, int TR, bool RG = false, int XGP = 0>
 __global__ void __launch_bounds__(WAVE * NWN * NWK)
 gemm_decode_kernel(KParams p) {
+  static_assert(XGP == 0 || XGP == 2 || XGP == 4, "XCDs per group");
   constexpr int NWAVE = NWN * NWK;
   constexpr int NB = TR * NT * NWN;
   constexpr int TG = TR * 8;                        // granules of one tile's chunk in LDS
@@ -1213,7 +1217,13 @@ gemm_decode_kernel(KParams p) {
   const int wn = wave % NWN, wk = wave / NWN;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  const Tile tl = tile_of_grid(p);
+  Tile tl = tile_of_grid(p);
+  if constexpr (XGP > 0) {
+    // linear index L = x + y * nblocks over nblocks x G workgroups: XCD L % 8, slot L / 8
+    const int L = (int)blockIdx.x + (int)blockIdx.y * (int)gridDim.x;
+    tl.g = (L & 7) / XGP;
+    tl.nb = (L & (XGP - 1)) + (L >> 3) * XGP;
+  }
   const int mb = tl.mb, nb = tl.nb, g = tl.g, s = tl.s;
 
   const int K = p.K, M = p.M, N = p.N, G = p.G;
@@ -1920,7 +1930,7 @@ struct Config {
   int row_scales = 0;                    // 1: exponents per weight row and 32 columns
   int TR = 16;                           // DECODE: real weight rows per 16-row MFMA tile (8 or 16)
   int ragged = 0;                        // DECODE: takes K that is not a multiple of 128
-  int xg = 0;                            // PAIR_FULL: one group per half of the XCDs (G = 2 only)
+  int xg = 0;                            // XCDs per group of the XCD-grouped tile maps (G = 8 / xg)
 };
 
 #define CFG(MT, NT, NWN, NWK, CW) {MT, NT, 1, NWN, NWK, CW, gemm_kernel<MT, NT, NWN, NWK, CW>, STAGED}
@@ -1933,7 +1943,7 @@ struct Config {
 #define PCFG(NWK, CP, RG) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, RG>, PAIR, 0, 8, RG}
 #define PFCFG(NWK, CP) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, false, true>, PAIR_FULL, 0, 8, 0}
 #define PFWCFG(NWK, CP, WF) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, false, true, WF>, PAIR_FULL, 0, 8, 0}
-#define PFXCFG(NWK, CP, WF) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, false, true, WF, true>, PAIR_FULL, 0, 8, 0, 1}
+#define PFXCFG(NWK, CP, WF) {8, 1, 1, 1, NWK, 2 * CP, gemm_pair_kernel<NWK, CP, false, true, WF, true>, PAIR_FULL, 0, 8, 0, 4}
 #define RDCFG(MT, NT, NWK, CW, D) {MT, NT, 1, 1, NWK, CW, gemm_rows_dma_kernel<MT, NT, NWK, CW, D>, ROWS_DMA}
 
 const Config kConfigs[] = {
@@ -2055,6 +2065,9 @@ const Config kConfigs[] = {
     PFWCFG(8, 2, 2),          // 109 pair, whole range (93) with the first pair's weights issued before X
     PFXCFG(8, 2, 0),          // 110 pair, whole range (93), one group per XCD half (G = 2 only)
     PFXCFG(8, 2, 2),          // 111 pair, whole range (109), one group per XCD half (G = 2 only)
+    // the decode shape of 54 with a group per XCD half (G = 2) or quarter (G = 4)
+    {8, 1, 1, 1, 8, 4, gemm_decode_kernel<1, 1, 8, 4, 8, 0, 16, false, 4>, DECODE, 0, 16, 0, 4},   // 112
+    {8, 1, 1, 1, 8, 4, gemm_decode_kernel<1, 1, 8, 4, 8, 0, 16, false, 2>, DECODE, 0, 16, 0, 2},   // 113
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2078,7 +2091,7 @@ int gemm_config_info(int cfg, int* out) {
   out[4] = c.NWN;
   out[5] = c.NWK;
   out[6] = c.kind;
-  out[7] = c.row_scales;
+  out[7] = c.row_scales | (c.xg << 8);
   return BSFP8_OK;
 }
 
@@ -2125,7 +2138,7 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
   if (p.splits > 64) return BSFP8_EINVAL;
   p.mblocks = (s.M + p.BM - 1) / p.BM;
   p.nblocks = s.N / p.NB;
-  if (c.xg && (s.G != 2 || p.nblocks % 4 != 0)) return BSFP8_EINVAL;   // its tile map needs both
+  if (c.xg && (s.G * c.xg != 8 || p.nblocks % c.xg != 0)) return BSFP8_EINVAL;   // its tile map needs both
   if (c.kind == TILE) {
     // fp32 partials [splits][M][G][N], summed by the reduce kernel
     if (p.splits > 1) p.ws_bytes = (size_t)p.splits * s.M * s.G * s.N * 4;
@@ -2155,7 +2168,8 @@ int plan_with(const GemmShape& s, int cfg, int cps, GemmPlan* plan) {
 //    first weight chunks issued before the X rows; with two groups from 3 rows on, each group on
 //    its own half of the XCDs).
 //  * Other decode rows (at most 8, or 16 with a long K): the decode kernel (everything streamed
-//    into LDS, 8 rows of X per workgroup); when K is not whole 128-wide chunks its ragged
+//    into LDS, 8 rows of X per workgroup; with four groups, each on its own two XCDs); when K is
+//    not whole 128-wide chunks its ragged
 //    instances, which read zeros past K, so K zero-padded to whole chunks (576 -> 640) gives
 //    bitwise the same Y.
 //  * Few rows (at most 32): the one-pass register kernel with X rows in LDS, one 16-row block of X
@@ -2197,6 +2211,10 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool al
     } else {
       cfg = whole ? 54 : 81;         // 16 weight rows, 8 waves along K x 4 chunks
       cps = kchunks < 32 ? kchunks : 32;
+      // four groups (wo_a at padded TP3): each group's workgroups on their own two XCDs, whose
+      // L2s then fetch one group's activation rows instead of all four (5.15 against 5.60 us at
+      // 2 rows, 5.29 against 5.53 at 6; no change with two groups at 16 rows)
+      if (whole && s.G == 4 && (s.N / 16) % 2 == 0) cfg = 113;
     }
   } else if (path == PATH_SMALL || s.M <= 32) {
     if (s.M <= 16 && kchunks <= 8) {
@@ -2234,7 +2252,7 @@ int plan_gemm(const GemmShape& s, int path, int split_k, GemmPlan* plan, bool al
     // An explicit split leaves each workgroup a few chunks: a workgroup sized for them (fewer
     // waves and chunk buffers, so several fit on a CU) instead of one sized for the whole range,
     // most of whose waves would sit idle while its LDS keeps the CU to one workgroup at a time.
-    if (cfg == 54 || cfg == 59) cfg = cps <= 4 ? 104 : cps <= 8 ? 59 : cps <= 16 ? 60 : cfg;
+    if (cfg == 54 || cfg == 59 || cfg == 113) cfg = cps <= 4 ? 104 : cps <= 8 ? 59 : cps <= 16 ? 60 : cfg;
     else if (cfg == 20 || cfg == 106) cfg = cps <= 8 ? 21 : cps <= 16 ? 19 : cfg;
   }
   const int st = plan_with(s, cfg, cps, plan);

@@ -34,8 +34,10 @@ BSFP8_API int bsfp8_num_configs(void);
  * and 5 take K in whole 128-wide chunks (K % 128 == 0), and so do the kind-4 configurations
  * except those built for a ragged last chunk (a call with K % 128 != 0 is refused with
  * BSFP8_EINVAL by the others).
- * out[7] = 1 when the configuration reads one exponent per weight row and 32 columns (it then
- * runs only through bsfp8_gemm_row32_config). Returns BSFP8_EINVAL for an unknown cfg. `out` is
+ * out[7] bit 0 = 1 when the configuration reads one exponent per weight row and 32 columns (it
+ * then runs only through bsfp8_gemm_row32_config); out[7] >> 8 = the XCDs per group of an
+ * XCD-grouped tile map (0: none; such a configuration takes only G = 8 / that value and a number
+ * of n-blocks it divides, else BSFP8_EINVAL). Returns BSFP8_EINVAL for an unknown cfg. `out` is
  * host memory of 8 ints. */
 BSFP8_API int bsfp8_config_info(int cfg, int* out);
 

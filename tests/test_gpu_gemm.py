@@ -123,11 +123,13 @@ def test_every_kernel_configuration():
     """Each compiled configuration, with a few chunks-per-split values, on a shape with several
     m-blocks (where the tile is smaller than M), a ragged K tail (the tile, slab, LDS-staged
     register and aligned decode kernels take K in whole 128-wide chunks) and every N tile width."""
-    G, N = 2, 256
+    N = 256
     for cfg in range(B.bsfp8_num_configs()):
         info = B.bsfp8_config_info(cfg)
         if info["row_scales"]:              # these read [G][N][K/32] exponents: test_gpu_row32.py
             continue
+        # the XCD-grouped tile maps take G = 8 / (XCDs per group), every other configuration G = 2
+        G = 8 // info["xcds_per_group"] if info["xcds_per_group"] else 2
         K = 768 if info["kind"] in (3, 4, 5, 6, 8) else 800
         if info["kind"] in (4, 6) and _takes_ragged_k(cfg):
             K = 800                         # a decode instance built for a ragged last chunk
