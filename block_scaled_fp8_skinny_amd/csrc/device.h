@@ -145,8 +145,9 @@ __device__ __forceinline__ Tile tile_of(const KParams& p) {
 }
 // The same for a three-dimensional grid (x = n-block, y = group, z = split * mblocks + m-block),
 // which the decode kernels use: the hardware hands each workgroup its indices, so nothing stands
-// between the arguments and the first loads (a decode workgroup reads its own weight rows and the
-// shared activations, which every L2 holds after its first miss, so the XCD order buys nothing).
+// between the arguments and the first loads. A decode workgroup reads its own weight rows and its
+// group's activations, which each XCD's L2 fetches on its first miss; with several groups the
+// kernels' XCD-grouped instances remap (x, y) so that each XCD serves one group.
 __device__ __forceinline__ Tile tile_of_grid(const KParams& p) {
   Tile r;
   r.nb = blockIdx.x;
