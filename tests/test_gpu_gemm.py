@@ -153,6 +153,31 @@ def test_every_kernel_configuration():
             check_bf16(bf16_bits(y), x, G, N, K, q, e, exact=exact)
 
 
+def test_xcd_grouped_instances_bitwise_equal_to_the_plain_map():
+    """The XCD-grouped tile maps only change which workgroup computes which tile: every output
+    equals the plain map's bit for bit (paired kernel at two groups, decode kernel at two and
+    four groups), and a group count the map was not built for is refused."""
+    pairs = [(110, 93, 2), (111, 109, 2), (112, 54, 2), (113, 54, 4)]
+    K = 4096
+    for new, base, G in pairs:
+        ni = B.bsfp8_config_info(new)
+        assert ni["xcds_per_group"] * G == 8
+        N = 512
+        for M in (1, 3, 6, 8):
+            x, q, e = _inputs(900 + new + M, M, G, N, K, elo=118, ehi=122)
+            xg, qg, eg = to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e)
+            for od in ("bf16", "f32"):
+                print(f"cfg {new} vs {base} G {G} M {M} {od}", flush=True)
+                a = B.bsfp8_gemm_config(xg, qg, eg, new, 32, out_dtype=od)
+                b = B.bsfp8_gemm_config(xg, qg, eg, base, 32, out_dtype=od)
+                torch.cuda.synchronize()
+                it = torch.int32 if od == "f32" else torch.int16
+                assert torch.equal(a.view(it), b.view(it)), (new, M, od)
+        x, q, e = _inputs(990, 2, 1, N, K)             # one group: not the count the map serves
+        with pytest.raises(B.BsfpError):
+            B.bsfp8_gemm_config(to_gpu_bf16(x), to_gpu_u8(q), to_gpu_u8(e), new, 32)
+
+
 def test_fp32_output():
     M, G, N, K = 12, 1, 256, 1536
     x, q, e = _inputs(500, M, G, N, K, elo=118, ehi=122)
